@@ -1,0 +1,176 @@
+/*
+ * oracle.c -- plain CPU reference of the W4A16 weight-only GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this file's library. It shares no code, header,
+ * table or helper with the GPU library; the two meet only through the arrays
+ * of the seeded input generator.
+ *
+ * What it computes. The W4A16 scheme keeps weights in 4-bit storage and the
+ * activations in 16-bit floating point (kongchang.com page, section "What
+ * Exactly Is This Stack"). A decode step reads each weight matrix once and
+ * multiplies it by the activation rows of every stream in the batch
+ * (ai.satyajit.si page, section "One weight read, shared by every stream").
+ * The 4-bit checkpoint is group-wise integer, one scale per group of weights
+ * (same page, section "What one more stream costs on this model"):
+ *
+ *   w[n][k] = q[n][k] * s[n][floor(k/g)]                         (dequantize)
+ *   y[m][n] = sum_{k=0}^{K-1} x[m][k] * w[n][k]                   (accumulate)
+ *
+ * with q in {-8..7}, s fp16, x bf16, g the group size. Both steps are done in
+ * IEEE double: w is exact (at most 4 + 11 significant bits), each product
+ * x*w is exact (8 + 15 <= 53 bits), and the sum runs in increasing k, so
+ * the only rounding is that of the double additions. Output stays in double.
+ *
+ * The packed format (a reading of the pages, which say nothing about it):
+ *   qweight[n][j] (uint32, j = 0..K/8-1) holds q[n][8j+i] in bits 4i..4i+3 as a
+ *   4-bit two's-complement code; scales are stored group-major: sp[j][n] =
+ *   s[n][j]. Unpacking a code c gives ((c ^ 8) - 8).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- number decoding (bf16 and fp16 bit patterns to double) ---- */
+
+/* bf16 is the top half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_fp16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1F;
+  int frac = h & 0x3FF;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)frac, -24);                 /* zero or subnormal */
+  } else if (expo == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + frac), expo - 25);  /* 1.frac * 2^(expo-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* ---- the GEMM ---- */
+
+typedef struct {
+  const uint16_t* x;
+  const int8_t* q;
+  const uint16_t* s;
+  double* y;
+  int M, N, K, group;
+  int n0, n1;
+} oracle_job;
+
+/* Returns 0, or 1 if the column buffer could not be allocated. */
+static int oracle_columns(const oracle_job* j) {
+  const int K = j->K, G = K / j->group;
+  double* w = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  if (!w) return 1;
+  for (int n = j->n0; n < j->n1; ++n) {
+    /* dequantize column n: w[k] = q[n][k] * s[n][floor(k / g)] */
+    const int8_t* qn = j->q + (size_t)n * K;
+    const uint16_t* sn = j->s + (size_t)n * G;
+    for (int k = 0; k < K; ++k) w[k] = (double)qn[k] * oracle_fp16_to_f64(sn[k / j->group]);
+    /* accumulate: y[m][n] = sum_k x[m][k] * w[k], increasing k */
+    for (int m = 0; m < j->M; ++m) {
+      const uint16_t* xm = j->x + (size_t)m * K;
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += oracle_bf16_to_f64(xm[k]) * w[k];
+      j->y[(size_t)m * j->N + n] = acc;
+    }
+  }
+  free(w);
+  return 0;
+}
+
+static void* oracle_thread(void* p) {
+  return (void*)(intptr_t)oracle_columns((const oracle_job*)p);
+}
+
+/*
+ * y[M][N] (double) = x[M][K] (bf16 bits) times dequant(q[N][K] int8, s[N][K/group] fp16 bits).
+ * Threads split the output columns; each dot product is summed by one thread
+ * in increasing k, so the result does not depend on the thread count.
+ * Returns 0; 1 on invalid arguments (nothing written); 2 if memory ran out.
+ */
+int oracle_gemm_f64(const uint16_t* x, const int8_t* q, const uint16_t* s, double* y,
+                    int M, int N, int K, int group, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || group <= 0 || K % group != 0) return 1;
+  if ((M > 0 && N > 0) && (!y || (K > 0 && (!x || !q || !s)))) return 1;
+  if (M == 0 || N == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > N) nthreads = N;
+  oracle_job jobs[256];
+  pthread_t th[256];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (oracle_job){x, q, s, y, M, N, K, group,
+                           (int)((long long)N * t / nthreads),
+                           (int)((long long)N * (t + 1) / nthreads)};
+  }
+  int started = 0, rc = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, oracle_thread, &jobs[t]) != 0) break;
+    started = t;
+  }
+  rc |= oracle_columns(&jobs[0]);
+  for (int t = 1; t <= started; ++t) {
+    void* r = NULL;
+    pthread_join(th[t], &r);
+    rc |= (int)(intptr_t)r;
+  }
+  for (int t = started + 1; t < nthreads; ++t) rc |= oracle_columns(&jobs[t]);
+  return rc ? 2 : 0;
+}
+
+/* ---- the packed format ---- */
+
+/*
+ * Pack q[N][K] (int8, each in -8..7) into qweight[N][K/8] and copy the scales
+ * s[N][K/group] into group-major sp[K/group][N]. Returns 0; 1 if a shape is
+ * invalid (K % 8, K % group, group % 8) or any code is out of range, in which
+ * case nothing is written.
+ */
+int oracle_pack(const int8_t* q, const uint16_t* s, uint32_t* qweight, uint16_t* sp,
+                int N, int K, int group) {
+  if (N < 0 || K < 0 || group <= 0 || K % 8 != 0 || group % 8 != 0 || K % group != 0) return 1;
+  for (size_t i = 0; i < (size_t)N * K; ++i)
+    if (q[i] < -8 || q[i] > 7) return 1;
+  const int W = K / 8, G = K / group;
+  for (int n = 0; n < N; ++n) {
+    for (int j = 0; j < W; ++j) {
+      uint32_t word = 0;
+      for (int i = 0; i < 8; ++i) {
+        uint32_t code = (uint32_t)(q[(size_t)n * K + 8 * j + i] & 0xF);
+        word |= code << (4 * i);
+      }
+      qweight[(size_t)n * W + j] = word;
+    }
+    for (int g = 0; g < G; ++g) sp[(size_t)g * N + n] = s[(size_t)n * G + g];
+  }
+  return 0;
+}
+
+/* Inverse of the weight half of oracle_pack: qweight[N][K/8] -> q[N][K]. */
+int oracle_unpack(const uint32_t* qweight, int8_t* q, int N, int K) {
+  if (N < 0 || K < 0 || K % 8 != 0) return 1;
+  const int W = K / 8;
+  for (int n = 0; n < N; ++n)
+    for (int j = 0; j < W; ++j) {
+      uint32_t word = qweight[(size_t)n * W + j];
+      for (int i = 0; i < 8; ++i) {
+        int code = (int)((word >> (4 * i)) & 0xF);
+        q[(size_t)n * K + 8 * j + i] = (int8_t)((code ^ 8) - 8);
+      }
+    }
+  return 0;
+}
