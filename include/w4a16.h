@@ -1,0 +1,118 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 weight-only GEMM library.
+ *
+ * The operation. W4A16 keeps the weights of a linear layer in 4-bit integer
+ * storage and the activations in 16-bit floating point (kongchang.com page,
+ * section "What Exactly Is This Stack"). One decode step reads every weight
+ * matrix once and multiplies it by the activation rows of all streams of the
+ * batch, so extra rows add arithmetic but almost no bytes (ai.satyajit.si page,
+ * section "One weight read, shared by every stream", the t_step equation and
+ * the paragraph before it); with speculation each stream adds its verified
+ * positions as further rows (same page, section "Speculation spends the same
+ * arithmetic"). The 4-bit checkpoint is group-wise integer, one scale per group
+ * of weights (same page, section "What one more stream costs on this model").
+ * This library computes, for M activation rows,
+ *
+ *     y[m][n] = sum_k x[m][k] * q[n][k] * s[n][k / group]      (0 <= m < M, 0 <= n < N)
+ *
+ * with x bf16, q a signed 4-bit code in -8..7, s an fp16 scale, fp32
+ * accumulation and a bf16 result rounded to nearest even.
+ *
+ * Packed format (the pages leave it open; this is the library's definition):
+ *   qweight : uint32 [N][K/8]. Word j of output column n holds the codes of
+ *             k = 8j .. 8j+7; the code of k = 8j+i sits in bits 4i..4i+3 as
+ *             4-bit two's complement (q & 0xF).
+ *   scales  : fp16 [K/group][N], group-major (all columns of group 0 first).
+ *   x       : bf16 [M][K] row-major, contiguous.   y : bf16 [M][N] row-major.
+ *
+ * Ownership and threading. The caller owns every buffer. The library keeps no
+ * per-call state, allocates no memory, never synchronizes, and may be called
+ * from several host threads at once. GEMM calls are asynchronous on `stream`
+ * (NULL = the device's default stream); the pointers must stay valid until the
+ * work on `stream` completes. `y` must not overlap any input.
+ *
+ * Errors. Every check happens on the host before any launch; a failed call
+ * launches nothing and leaves no state behind, so the next call is unaffected.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*` */
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1, /* null pointer, negative size, size mismatch, code out of -8..7 */
+  W4A16_ERR_UNSUPPORTED = 2, /* shape outside the supported set (see w4a16_gemm) */
+  W4A16_ERR_MISALIGNED = 3,  /* a device pointer is not 16-byte aligned */
+  W4A16_ERR_LAUNCH = 4       /* the HIP runtime refused the kernel launch */
+} w4a16_status;
+
+/* Kernel paths; W4A16_PATH_AUTO lets the M-dispatch heuristic choose. */
+typedef enum {
+  W4A16_PATH_AUTO = 0,
+  W4A16_PATH_SKINNY = 1, /* small M: per-wave weight streaming, 16-row MFMA tiles, split-K */
+  W4A16_PATH_LARGE = 2   /* large M: LDS-staged activation tiles, bf16 MFMA, per-group fp32 scaling */
+} w4a16_path;
+
+/* Bytes of the packed weights, N*K/2, and of the packed scales, N*(K/group)*2.
+ * Return 0 for negative sizes, K not a multiple of 8, or group not dividing K. */
+size_t w4a16_qweight_bytes(int N, int K);
+size_t w4a16_scales_bytes(int N, int K, int group);
+
+/*
+ * Host-side packing into the packed format above. Pure and deterministic; no
+ * device involvement.
+ *   q          : host int8 [N][K], each code in -8..7 (read only)
+ *   scales_in  : host fp16 bit patterns [N][K/group], row n = output column n
+ *   qweight_out: host uint32 [N][K/8]             (w4a16_qweight_bytes bytes)
+ *   scales_out : host fp16 bit patterns [K/group][N] (w4a16_scales_bytes bytes)
+ * Requires N >= 0, K >= 0, K % 8 == 0, group > 0, group % 8 == 0, K % group == 0.
+ * Returns W4A16_OK, or W4A16_ERR_INVALID_ARG (nothing written) for a null
+ * pointer with a non-empty shape, a bad shape, or any code outside -8..7.
+ * Scale values are copied bit for bit; they are not inspected.
+ */
+int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out,
+               uint16_t* scales_out, int N, int K, int group);
+
+/*
+ * y = x . dequant(qweight, scales) on the GPU, overwriting y (no bias, no beta).
+ *   x       : device bf16 [M][K]
+ *   qweight : device uint32 [N][K/8], scales: device fp16 [K/group][N] (as w4a16_pack writes)
+ *   y       : device bf16 [M][N]
+ * All four pointers must be 16-byte aligned device addresses of the current
+ * device. Supported shapes: M >= 0, N >= 1, K >= 1, group in {32, 64, 128, 256},
+ * K % group == 0; N needs no rounding (ragged column tiles are masked).
+ * M == 0 returns W4A16_OK and launches nothing.
+ * Returns W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED,
+ * W4A16_ERR_MISALIGNED or W4A16_ERR_LAUNCH.
+ */
+int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
+               int K, int group, struct ihipStream_t* stream);
+
+/* As w4a16_gemm, with the kernel path forced (W4A16_PATH_*); every path gives
+ * a result within the same tolerance of the exact product. */
+int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* y, int M,
+                  int N, int K, int group, int path, struct ihipStream_t* stream);
+
+/* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
+ * host integers), or -1 for an unsupported shape. */
+int w4a16_select_path(int M, int N, int K, int group);
+
+/* Static text for a status code; never NULL. */
+const char* w4a16_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

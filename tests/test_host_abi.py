@@ -1,0 +1,135 @@
+"""Host-only tests of the C-ABI library: it loads without a GPU, exports every
+function include/w4a16.h declares, packs bit for bit like the oracle, and
+rejects bad arguments before any launch (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+import synth
+import w4a16_weight_only_gemm_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "w4a16.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 8, names
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in w4.SIGNATURES, f"{name} has no binding"
+
+
+def test_version_and_status_strings():
+    assert w4.w4a16_version() >= 100
+    for st in range(5):
+        assert w4.w4a16_status_string(st).startswith("W4A16_")
+    assert "unknown" in w4.w4a16_status_string(99)
+
+
+def test_sizes():
+    assert w4.w4a16_qweight_bytes(7168, 5120) == 7168 * 5120 // 2
+    assert w4.w4a16_scales_bytes(7168, 5120, 128) == 7168 * 40 * 2
+    assert w4.w4a16_qweight_bytes(4, 12) == 0          # K % 8
+    assert w4.w4a16_scales_bytes(4, 96, 64) == 0       # K % group
+    assert w4.w4a16_qweight_bytes(-1, 8) == 0
+
+
+def _lib_pack(q, s, g):
+    try:
+        return w4.w4a16_pack(q, s, g)
+    except w4.W4A16Error as e:  # the pins expect ValueError for rejected input
+        raise ValueError(str(e)) from e
+
+
+def test_library_pack_golden_words():
+    pins.pin_golden_words(_lib_pack)
+    pins.pin_scale_layout(_lib_pack)
+    pins.pin_pack_rejects(_lib_pack)
+
+
+@pytest.mark.parametrize("shape", [(512, 256, 64), (96, 1024, 128), (40, 768, 256), (24, 64, 32)])
+def test_library_pack_matches_oracle(shape):
+    N, K, g = shape
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 9, 0), N, K)
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 9, 0), N, K // g)
+    qw_lib, sp_lib = w4.w4a16_pack(q, s, g)
+    qw_ref, sp_ref = oracle.pack(q, s, g)
+    assert np.array_equal(qw_lib, qw_ref)
+    assert np.array_equal(sp_lib, sp_ref)
+
+
+def test_library_pack_matches_oracle_full_projection():
+    # the largest projection of the layer set (gate+up, 5120 x 34816), bit for bit
+    p = synth.LAYER_PROJECTIONS[2]
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, 2), p.N, p.K)
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, 2), p.N, p.K // synth.GROUP)
+    qw_lib, sp_lib = w4.w4a16_pack(q, s, synth.GROUP)
+    qw_ref, sp_ref = oracle.pack(q, s, synth.GROUP)
+    assert np.array_equal(qw_lib, qw_ref) and np.array_equal(sp_lib, sp_ref)
+
+
+def test_pack_rejects_and_writes_nothing():
+    N, K, g = 4, 64, 32
+    q = np.zeros((N, K), np.int8)
+    q[3, 63] = -9
+    s = np.ones((N, K // g), np.uint16)
+    qw = np.full((N, K // 8), 0xDEADBEEF, np.uint32)
+    sp = np.full((K // g, N), 0xABCD, np.uint16)
+    rc = w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, g)
+    assert rc == w4.W4A16_ERR_INVALID_ARG
+    assert (qw == 0xDEADBEEF).all() and (sp == 0xABCD).all()
+    # bad shapes
+    for (K2, g2) in [(60, 30), (64, 12), (64, 48), (12, 4)]:
+        assert w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data,
+                              N, K2, g2) == w4.W4A16_ERR_INVALID_ARG
+    # null pointers with a non-empty shape, and the empty shape
+    assert w4.pack_status(None, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, g) == 1
+    assert w4.pack_status(None, None, None, None, 0, K, g) == w4.W4A16_OK
+    # a valid call right after the failures succeeds
+    q[3, 63] = 7
+    assert w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, g) == 0
+    assert qw[3, 7] == 0x70000000
+
+
+# Fake, never-dereferenced addresses: every call below fails its host checks
+# before any HIP call, so no device is needed.
+A = 0x10000  # 16-byte aligned
+
+
+def test_gemm_argument_checks_without_launch():
+    st = w4.gemm_status
+    assert st(A, A, A, A, 0, 512, 256, 64) == w4.W4A16_OK                     # M == 0: no-op
+    assert st(None, None, None, None, 0, 512, 256, 64) == w4.W4A16_OK
+    assert st(None, A, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG     # null x
+    assert st(A, A, A, None, 1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG     # null y
+    assert st(A, A, A, A, -1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert st(A, A, A, A, 1, -5, 256, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert st(A, A, A, A, 1, 512, 256, 48) == w4.W4A16_ERR_UNSUPPORTED       # group
+    assert st(A, A, A, A, 1, 512, 250, 64) == w4.W4A16_ERR_UNSUPPORTED       # K % group
+    assert st(A, A, A, A, 1, 0, 256, 64) == w4.W4A16_ERR_UNSUPPORTED
+    assert st(A, A, A, A, 1, 512, 0, 64) == w4.W4A16_ERR_UNSUPPORTED
+    assert st(A + 2, A, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
+    assert st(A, A + 8, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
+    assert st(A, A, A + 4, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
+    assert st(A, A, A, A + 2, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
+    assert st(A, A, A, A, 1, 512, 256, 64, path=7) == w4.W4A16_ERR_INVALID_ARG
+
+
+def test_select_path():
+    assert w4.w4a16_select_path(1, 7168, 5120, 128) == w4.W4A16_PATH_SKINNY
+    assert w4.w4a16_select_path(16, 5120, 17408, 128) == w4.W4A16_PATH_SKINNY
+    assert w4.w4a16_select_path(1024, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
+    assert w4.w4a16_select_path(1, 512, 256, 48) == -1
+    assert w4.w4a16_select_path(-1, 512, 256, 64) == -1

@@ -1,0 +1,176 @@
+"""Python binding of the MI355X W4A16 weight-only GEMM library (``libw4a16.so``).
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels, and packing runs in its host code. The names match the C ABI in
+``include/w4a16.h``. PyTorch, when used, only provides device memory and the
+current HIP stream. There is no fallback: if the library has not been built
+(``python w4a16_weight_only_gemm_amd/_build.py`` or ``__graft_entry__.build()``),
+importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+try:  # load torch's HIP runtime first so the library binds to the same one
+    import torch as _torch
+except ImportError:  # pragma: no cover - torch is optional for host-only use
+    _torch = None
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a16.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python w4a16_weight_only_gemm_amd/_build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+W4A16_OK = 0
+W4A16_ERR_INVALID_ARG = 1
+W4A16_ERR_UNSUPPORTED = 2
+W4A16_ERR_MISALIGNED = 3
+W4A16_ERR_LAUNCH = 4
+
+W4A16_PATH_AUTO = 0
+W4A16_PATH_SKINNY = 1
+W4A16_PATH_LARGE = 2
+
+# Every symbol include/w4a16.h declares, with its ctypes signature.
+_vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "w4a16_qweight_bytes": (_sz, [_int, _int]),
+    "w4a16_scales_bytes": (_sz, [_int, _int, _int]),
+    "w4a16_pack": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int]),
+    "w4a16_gemm": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "w4a16_gemm_ex": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
+    "w4a16_select_path": (_int, [_int, _int, _int, _int]),
+    "w4a16_status_string": (ctypes.c_char_p, [_int]),
+    "w4a16_version": (_int, []),
+}
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {w4a16_status_string(status)}")
+
+
+def w4a16_status_string(status: int) -> str:
+    return _lib.w4a16_status_string(int(status)).decode()
+
+
+def w4a16_version() -> int:
+    return int(_lib.w4a16_version())
+
+
+def w4a16_qweight_bytes(N: int, K: int) -> int:
+    return int(_lib.w4a16_qweight_bytes(N, K))
+
+
+def w4a16_scales_bytes(N: int, K: int, group: int) -> int:
+    return int(_lib.w4a16_scales_bytes(N, K, group))
+
+
+def w4a16_select_path(M: int, N: int, K: int, group: int) -> int:
+    return int(_lib.w4a16_select_path(M, N, K, group))
+
+
+def w4a16_pack(q: np.ndarray, scales: np.ndarray, group: int):
+    """Host packing: q int8 [N, K] in -8..7 and fp16 scales [N, K/group] (float16 or
+    uint16 bit patterns) -> (qweight uint32 [N, K/8], scales uint16 [K/group, N])."""
+    q = np.ascontiguousarray(q)
+    if q.dtype != np.int8 or q.ndim != 2:
+        raise TypeError("q must be a 2-D int8 array")
+    s = np.ascontiguousarray(scales)
+    if s.dtype == np.float16:
+        s = s.view(np.uint16)
+    if s.dtype != np.uint16 or s.ndim != 2:
+        raise TypeError("scales must be a 2-D float16 or uint16 array")
+    N, K = q.shape
+    if group <= 0 or K % group != 0 or s.shape != (N, K // group):
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_pack")
+    qw = np.empty((N, K // 8), dtype=np.uint32)
+    sp = np.empty((K // group, N), dtype=np.uint16)
+    rc = _lib.w4a16_pack(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, group)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_pack")
+    return qw, sp
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if _torch is not None and isinstance(t, _torch.Tensor):
+        if not t.is_cuda:
+            raise ValueError("device tensor expected")
+        if not t.is_contiguous():
+            raise ValueError("contiguous tensor expected")
+        return t.data_ptr()
+    raise TypeError(f"unsupported buffer type {type(t)}")
+
+
+def _stream(stream):
+    if stream is None:
+        if _torch is not None and _torch.cuda.is_available():
+            return _torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream
+
+
+def _check_tensors(x, qweight, scales, y, M, N, K, group):
+    """Size and dtype checks for torch tensors (raw addresses are the caller's business)."""
+    if _torch is None:
+        return
+    need = {"x": (x, 2 * M * K, True), "y": (y, 2 * M * N, True),
+            "qweight": (qweight, N * K // 2, False), "scales": (scales, 2 * N * (K // group), False)}
+    for name, (t, nbytes, bf16) in need.items():
+        if isinstance(t, _torch.Tensor):
+            if bf16 and t.dtype != _torch.bfloat16:
+                raise TypeError(f"{name} must be torch.bfloat16")
+            have = t.numel() * t.element_size()
+            if have < nbytes:
+                raise ValueError(f"{name} holds {have} bytes, needs {nbytes}")
+
+
+def w4a16_gemm_ex(x, qweight, scales, y, M: int, N: int, K: int, group: int, path: int,
+                  stream=None) -> None:
+    """y[M, N] = x[M, K] . dequant(qweight, scales) on the GPU, asynchronously on `stream`
+    (default: torch's current stream). Buffers are torch device tensors or raw device
+    addresses. Raises W4A16Error on a non-OK status."""
+    if group > 0 and K % group == 0:
+        _check_tensors(x, qweight, scales, y, M, N, K, group)
+    rc = _lib.w4a16_gemm_ex(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group, path,
+                            _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm_ex")
+
+
+def w4a16_gemm(x, qweight, scales, y, M: int, N: int, K: int, group: int, stream=None) -> None:
+    if group > 0 and K % group == 0:
+        _check_tensors(x, qweight, scales, y, M, N, K, group)
+    rc = _lib.w4a16_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
+                         _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm")
+
+
+def gemm_status(x, qweight, scales, y, M, N, K, group, path=W4A16_PATH_AUTO, stream=None) -> int:
+    """Raw status of w4a16_gemm_ex, without raising (for tests of the error paths)."""
+    return int(_lib.w4a16_gemm_ex(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
+                                  path, _stream(stream)))
+
+
+def pack_status(q_ptr, s_ptr, qw_ptr, sp_ptr, N, K, group) -> int:
+    """Raw status of w4a16_pack on raw host addresses (for tests of the error paths)."""
+    return int(_lib.w4a16_pack(q_ptr, s_ptr, qw_ptr, sp_ptr, N, K, group))

@@ -1,0 +1,71 @@
+// w4a16_device.h -- device helpers shared by the gfx950 kernels: operand types,
+// in-register dequantization of packed int4 words, the matching permutation of
+// bf16 activation fragments, and number conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace w4a16_internal {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern of -136.0: sign 1, exponent 134 (2^7), fraction 8/128.
+constexpr uint32_t kBiasPair = 0xC308C308u;
+
+// Biased dequantization of one packed word (eight 4-bit two's-complement codes,
+// code i of k = 8j+i in bits 4i..4i+3). Output register v holds, as a bf16
+// pair, code v in its low half and code v+4 in its high half, each as the
+// exact value 136 + q: (c & 0xF) ^ 8 is the offset code q + 8 in 0..15, and
+// OR-ing it into the fraction of 0x4300 (128.0, whose unit in the last place
+// is 1) gives 128 + q + 8. One shift and one and-xor per register.
+//
+// MFMA consumes the eight bf16 of a register quad as k-slots 0..7, so the
+// k-slot order of this operand is (0, 4, 1, 5, 2, 6, 3, 7) within the word;
+// the activation fragment must use the same order (act_frag below).
+__device__ __forceinline__ bf16x8 dequant_biased(uint32_t w) {
+  u32x4 r;
+  r[0] = (w & 0x000F000Fu) ^ 0x43084308u;
+  r[1] = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
+  r[2] = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
+  r[3] = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Eight consecutive bf16 activations x0..x7 (as four dwords, x0 in the low half
+// of d[0]) reordered into the k-slot order of dequant_biased:
+// (x0, x4), (x1, x5), (x2, x6), (x3, x7). v_perm_b32 selects bytes of
+// {src0 = bytes 4..7, src1 = bytes 0..3}.
+__device__ __forceinline__ bf16x8 act_frag(u32x4 d) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ bf16x8 bias_operand() {
+  u32x4 r = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace w4a16_internal
