@@ -1,0 +1,374 @@
+"""Benchmark of the W4A16 weight-only GEMM hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the four projections of one
+27B-class layer (qkv 5120x7168, o 6144x5120, gate+up 5120x34816, down
+17408x5120, group 128) at M activation rows, each a w4a16_gemm call through the
+C ABI. Weights are packed once per layer and kept in HBM; successive steps cycle
+through --layers distinct layer sets (1.39 GB at the default 8) so that no step
+finds its weights in the 256 MB last-level cache. Inputs are resident on the
+device before the timed region starts.
+
+The headline line reports the decode layer set (M = 1) in HBM TB/s over
+algorithmic bytes (packed weights + scales + activations + outputs, counted once
+per call). Extra entries report the verify block (M = 16, TB/s) and the batched
+step (M = 1024, TFLOP/s).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, vendor figure
+GROUP = 128
+
+
+def algorithmic_bytes(M: int, N: int, K: int, group: int) -> int:
+    """Bytes a W4A16 GEMM must move at least once: packed int4 weights, fp16
+    scales, bf16 activations in and bf16 outputs out."""
+    return K * N // 2 + 2 * N * (K // group) + 2 * M * K + 2 * M * N
+
+
+def flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def ceiling_tokens_per_s(bandwidth_gbs: float, bytes_per_token_gb: float) -> float:
+    """Memory-bound decode ceiling: bandwidth over bytes read per token (the
+    bandwidth-ceiling equation of the throughput page's "One weight read" section)."""
+    return bandwidth_gbs / bytes_per_token_gb
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a16_weight_only_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from committed rocprofv3 PMC results, or None when
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(f"{kernel}|{workload}")
+    if not entry or entry.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+class LayerStore:
+    """Packed weights and scales of L layer sets, resident on the device."""
+
+    def __init__(self, layers: int):
+        import numpy as np
+        import torch
+
+        import synth
+        import w4a16_weight_only_gemm_amd as w4
+        self.projs = synth.LAYER_PROJECTIONS
+        self.layers = []
+        for layer in range(layers):
+            entry = []
+            for pi, p in enumerate(self.projs):
+                q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K)
+                s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N,
+                                     p.K // GROUP)
+                qw, sp = w4.w4a16_pack(q, s, GROUP)
+                entry.append((torch.from_numpy(qw.view(np.int32)).to("cuda"),
+                              torch.from_numpy(sp.view(np.int16)).to("cuda")))
+                del q, s, qw, sp
+            self.layers.append(entry)
+        torch.cuda.synchronize()
+
+    @property
+    def weight_bytes(self) -> int:
+        return sum(t.numel() * t.element_size() for e in self.layers for pair in e for t in pair)
+
+
+class Workload:
+    """Activations, outputs and launch arguments at M rows for every layer set."""
+
+    def __init__(self, store: LayerStore, M: int, grouped: bool):
+        import ctypes
+
+        import numpy as np
+        import torch
+
+        import synth
+        import w4a16_weight_only_gemm_amd as w4
+        self.M = M
+        self.store = store
+        self.grouped = grouped and M <= 16
+        self.x, self.y = [], []
+        for layer in range(len(store.layers)):
+            xs, ys = [], []
+            for pi, p in enumerate(store.projs):
+                xb = synth.gen_x(synth.tensor_id(synth.KIND_X, layer, pi, M), M, p.K)
+                xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16))
+                ys.append(torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda"))
+            self.x.append(xs)
+            self.y.append(ys)
+        cols = sum(p.N for p in store.projs)
+        self.ws_bytes = w4.w4a16_workspace_bytes(M, cols)
+        self.ws = torch.zeros(max(1, self.ws_bytes // 4), dtype=torch.int32, device="cuda")
+        # raw launch arguments, so the timed loop does no Python-side checking
+        self.args, self.problems = [], []
+        for layer in range(len(store.layers)):
+            la, entries = [], []
+            for pi, p in enumerate(store.projs):
+                qw, sp = store.layers[layer][pi]
+                la.append((self.x[layer][pi].data_ptr(), qw.data_ptr(), sp.data_ptr(),
+                           self.y[layer][pi].data_ptr(), M, p.N, p.K, GROUP))
+                entries.append((self.x[layer][pi], qw, sp, self.y[layer][pi], p.N, p.K))
+            self.args.append(la)
+            arr = w4.make_problems(entries)
+            self.problems.append((arr, ctypes.cast(arr, ctypes.c_void_p).value))
+
+    def step_bytes(self) -> int:
+        return sum(algorithmic_bytes(self.M, p.N, p.K, GROUP) for p in self.store.projs)
+
+    def step_flops(self) -> int:
+        return sum(flops(self.M, p.N, p.K) for p in self.store.projs)
+
+
+def run_steps(wl: Workload, lib, stream: int, first: int, count: int, events=None, dom=2):
+    """Launch `count` steps starting at step index `first`. Grouped steps are one
+    launch (all four projections); otherwise four. With `events`, an event pair
+    is recorded around the dominant launch of every step (the grouped launch,
+    or projection `dom`)."""
+    L = len(wl.args)
+    for s in range(first, first + count):
+        if wl.grouped:
+            if events is not None:
+                events[s - first][0].record()
+            rc = lib.w4a16_gemm_grouped(wl.problems[s % L][1], 4, wl.M, GROUP,
+                                        wl.ws.data_ptr(), wl.ws_bytes, stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
+            if events is not None:
+                events[s - first][1].record()
+            continue
+        la = wl.args[s % L]
+        for pi, a in enumerate(la):
+            if events is not None and pi == dom:
+                events[s - first][0].record()
+            rc = lib.w4a16_gemm(*a, stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+            if events is not None and pi == dom:
+                events[s - first][1].record()
+
+
+def time_workload(wl: Workload, steps: int, warmup: int, use_graph: bool):
+    """(ms per step, mean dominant-launch duration in ms, steps timed)."""
+    import torch
+
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    L = len(wl.args)
+
+    # dominant-launch durations, from events around each of its launches
+    run_steps(wl, lib, stream, 0, warmup)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    run_steps(wl, lib, stream, 0, steps, events=ev)
+    torch.cuda.synchronize()
+    dom_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    # whole steps, back to back
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run_steps(wl, lib, s.cuda_stream, 0, L)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            run_steps(wl, lib, torch.cuda.current_stream().cuda_stream, 0, L)
+        for _ in range(max(1, warmup // L)):
+            graph.replay()
+        reps = max(1, steps // L)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (reps * L), dom_ms, reps * L
+    run_steps(wl, lib, stream, 0, warmup)
+    torch.cuda.synchronize()
+    t0.record()
+    run_steps(wl, lib, stream, 0, steps)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, dom_ms, steps
+
+
+def check_parity(wl: Workload, layer: int, cols: int = 64):
+    """Sampled parity of the last outputs of one layer against the oracle:
+    max over sampled elements of |y - y_ref| / (1e-2 (1 + |y_ref|))."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    worst = 0.0
+    for pi, p in enumerate(wl.store.projs):
+        rng = np.random.default_rng(pi)
+        c = np.sort(rng.choice(p.N, cols, replace=False))
+        rows = min(wl.M, 64)
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K)[c]
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N, p.K // GROUP)[c]
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, layer, pi, wl.M), wl.M, p.K, rows=(0, rows))
+        ref = oracle.gemm(x, q, s, GROUP, threads=synth.default_threads())
+        y = wl.y[layer][pi][:rows].view(torch.int16).cpu().numpy().view(np.uint16)[:, c]
+        yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(yv - ref) / (1e-2 * (1 + np.abs(ref))))))
+    return worst
+
+
+def cpu_baseline(seconds_target: float = 15.0):
+    """The oracle, as it stands, on the host cores: the decode layer set (M = 1)
+    one projection after another until about `seconds_target` of CPU work."""
+    import synth
+    import oracle
+    threads = synth.default_threads()
+    done_bytes, t_total, parts = 0, 0.0, []
+    for pi, p in enumerate(synth.LAYER_PROJECTIONS):
+        x, q, s = synth.layer_inputs(0, pi, 1)
+        t0 = time.perf_counter()
+        oracle.gemm(x, q, s, GROUP, threads=threads)
+        dt = time.perf_counter() - t0
+        done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
+        t_total += dt
+        parts.append(p.name)
+        if t_total >= seconds_target:
+            break
+    return {"value": done_bytes / t_total / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"M=1 projections {'+'.join(parts)} of layer 0, group 128, fp64 oracle, "
+                      f"{t_total:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the steps from a captured HIP graph (no host launch cost)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--m-list", default="1,16,1024")
+    ap.add_argument("--separate", action="store_true",
+                    help="four launches per step at every M (no grouped streaming launch)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMM is not sharded across GPUs in this build)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    import w4a16_weight_only_gemm_amd  # noqa: F401  (fails loudly without the library)
+
+    t0 = time.time()
+    store = LayerStore(args.layers)
+    print(f"# packed {args.layers} layer sets, {store.weight_bytes / 1e9:.3f} GB resident, "
+          f"{time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    results = {}
+    for M in [int(v) for v in args.m_list.split(",")]:
+        wl = Workload(store, M, grouped=not args.separate)
+        ms, dom_ms, nsteps = time_workload(wl, args.steps, args.warmup, args.graph)
+        parity = check_parity(wl, 0)
+        results[M] = (wl, ms, dom_ms, parity, nsteps)
+        print(f"# M={M}: {ms * 1e3:.2f} us/step, dominant launch {dom_ms * 1e3:.2f} us, "
+              f"parity ratio {parity:.3f}", file=sys.stderr, flush=True)
+        del wl
+
+    M0 = int(args.m_list.split(",")[0])
+    wl, ms, dom_ms, parity, nsteps = results[M0]
+    step_bytes = wl.step_bytes()
+    value = step_bytes / (ms * 1e-3) / 1e12
+    gu = store.projs[2]
+    if wl.grouped:
+        dom_name = "grouped stream-K launch (qkv+o+gate_up+down) at M=%d" % M0
+        dom_key = "streamk_grouped"
+        dom_bytes = step_bytes
+    else:
+        dom_name = "gate_up projection (5120x34816) at M=%d" % M0
+        dom_key = "gate_up"
+        dom_bytes = algorithmic_bytes(M0, gu.N, gu.K, GROUP)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    workload = (f"decode layer set M={M0}: qkv 5120x7168, o 6144x5120, gate_up 5120x34816, "
+                f"down 17408x5120; int4 weights, group {GROUP}, fp16 scales, bf16 activations")
+    traffic = load_traffic(dom_key, f"M={M0}")
+    extra = []
+    for M, (wl2, ms2, dom2, par2, _) in results.items():
+        if M == M0:
+            continue
+        b, f = wl2.step_bytes(), wl2.step_flops()
+        e = {"M": M, "ms_per_step": ms2, "tbps": b / (ms2 * 1e-3) / 1e12,
+             "tflops": f / (ms2 * 1e-3) / 1e12, "positions_per_s": M / (ms2 * 1e-3),
+             "parity_ratio": par2}
+        if M >= 256:
+            e["roofline"] = {"bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": e["tflops"] / BF16_PEAK_TFLOPS}
+        else:
+            e["roofline"] = {"bound": "hbm", "achieved": e["tbps"] * 1e3, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": e["tbps"] * 1e3 / HBM_PEAK_GBS}
+        extra.append(e)
+
+    line = {
+        "metric": "W4A16 GEMM achieved HBM TB/s (M=1,16) and TFLOP/s (M>=256) vs MI355X peak",
+        "value": value,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "M": M0, "group": GROUP, "layers_rotated": args.layers,
+                   "graph": bool(args.graph), "positions_per_s": M0 / (ms * 1e-3),
+                   "parity_ratio": parity},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": dom_name},
+        "extra": extra,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

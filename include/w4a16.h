@@ -18,11 +18,17 @@
  * with x bf16, q a signed 4-bit code in -8..7, s an fp16 scale, fp32
  * accumulation and a bf16 result rounded to nearest even.
  *
- * Packed format (the pages leave it open; this is the library's definition):
- *   qweight : uint32 [N][K/8]. Word j of output column n holds the codes of
- *             k = 8j .. 8j+7; the code of k = 8j+i sits in bits 4i..4i+3 as
- *             4-bit two's complement (q & 0xF).
- *   scales  : fp16 [K/group][N], group-major (all columns of group 0 first).
+ * Packed format (the pages leave it open; this is the library's definition).
+ *   Logical words: word j of output column n holds the codes of k = 8j..8j+7;
+ *   the code of k = 8j+i sits in bits 4i..4i+3 as 4-bit two's complement
+ *   (q & 0xF). Device arrangement (what w4a16_pack writes and the kernels
+ *   read): columns in blocks of 16, the last block padded with zero codes and
+ *   zero scales; blocks = ceil(N/16), G = K/group, wpl = group/32.
+ *   qweight : uint32 [blocks][G][64][wpl]. Tile (b, t) covers 16 columns x one
+ *             group; its entry (l, w) is logical word t*(group/8) + (l/16)*wpl + w
+ *             of column 16b + (l%16). A tile is exactly the MFMA B operands of
+ *             its group for one wavefront, and a block's K range is contiguous.
+ *   scales  : fp16 [blocks][G][16]; entry (b, t, c) = s[16b + c][t].
  *   x       : bf16 [M][K] row-major, contiguous.   y : bf16 [M][N] row-major.
  *
  * Ownership and threading. The caller owns every buffer. The library keeps no
@@ -61,8 +67,9 @@ typedef enum {
   W4A16_PATH_LARGE = 2   /* large M: LDS-staged activation tiles, bf16 MFMA, per-group fp32 scaling */
 } w4a16_path;
 
-/* Bytes of the packed weights, N*K/2, and of the packed scales, N*(K/group)*2.
- * Return 0 for negative sizes, K not a multiple of 8, or group not dividing K. */
+/* Bytes of the packed weights, ceil(N/16)*16*K/2, and of the packed scales,
+ * ceil(N/16)*16*(K/group)*2. Return 0 for negative sizes, K not a multiple of
+ * 32, or a group that is not a multiple of 32 or does not divide K. */
 size_t w4a16_qweight_bytes(int N, int K);
 size_t w4a16_scales_bytes(int N, int K, int group);
 
@@ -71,9 +78,9 @@ size_t w4a16_scales_bytes(int N, int K, int group);
  * device involvement.
  *   q          : host int8 [N][K], each code in -8..7 (read only)
  *   scales_in  : host fp16 bit patterns [N][K/group], row n = output column n
- *   qweight_out: host uint32 [N][K/8]             (w4a16_qweight_bytes bytes)
- *   scales_out : host fp16 bit patterns [K/group][N] (w4a16_scales_bytes bytes)
- * Requires N >= 0, K >= 0, K % 8 == 0, group > 0, group % 8 == 0, K % group == 0.
+ *   qweight_out: host, w4a16_qweight_bytes(N, K) bytes, device arrangement above
+ *   scales_out : host, w4a16_scales_bytes(N, K, group) bytes, device arrangement above
+ * Requires N >= 0, K >= 0, group > 0, group % 32 == 0, K % group == 0.
  * Returns W4A16_OK, or W4A16_ERR_INVALID_ARG (nothing written) for a null
  * pointer with a non-empty shape, a bad shape, or any code outside -8..7.
  * Scale values are copied bit for bit; they are not inspected.
@@ -84,7 +91,7 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
 /*
  * y = x . dequant(qweight, scales) on the GPU, overwriting y (no bias, no beta).
  *   x       : device bf16 [M][K]
- *   qweight : device uint32 [N][K/8], scales: device fp16 [K/group][N] (as w4a16_pack writes)
+ *   qweight, scales : device copies of what w4a16_pack wrote for (N, K, group)
  *   y       : device bf16 [M][N]
  * All four pointers must be 16-byte aligned device addresses of the current
  * device. Supported shapes: M >= 0, N >= 1, K >= 1, group in {32, 64, 128, 256},
@@ -100,6 +107,53 @@ int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, 
  * a result within the same tolerance of the exact product. */
 int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* y, int M,
                   int N, int K, int group, int path, struct ihipStream_t* stream);
+
+/*
+ * Workspace of the streaming entry points below, for M activation rows and
+ * `total_columns` output columns (the sum of N over the problems of a call):
+ * per-block counters followed by fp32 partial sums. Device memory owned by the
+ * caller, 256-byte aligned, zero-filled once before its first use; every call
+ * leaves the counters at zero again, so it is reused without clearing. One
+ * workspace must not serve two calls that can run at the same time. Returns 0
+ * for M < 0 or total_columns < 0.
+ */
+size_t w4a16_workspace_bytes(int M, long long total_columns);
+
+/*
+ * As w4a16_gemm, using a workspace (see w4a16_workspace_bytes(M, N)). For
+ * M <= 16 this runs the streaming kernel: a persistent grid whose waves split
+ * the packed weights into equal contiguous runs, combining the column blocks
+ * cut between waves through the workspace (deterministically: parts are summed
+ * in a fixed order). Larger M runs the kernels of w4a16_gemm. Extra errors:
+ * W4A16_ERR_INVALID_ARG for a null or too small workspace (checked only when
+ * the streaming kernel runs), W4A16_ERR_MISALIGNED for a workspace that is not
+ * 256-byte aligned.
+ */
+int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
+                  int K, int group, void* workspace, size_t workspace_bytes,
+                  struct ihipStream_t* stream);
+
+/* One GEMM of a grouped call: y[M][N] = x[M][K] . dequant(qweight, scales). */
+typedef struct w4a16_problem {
+  const void* x;
+  const void* qweight;
+  const void* scales;
+  void* y;
+  int N;
+  int K;
+} w4a16_problem;
+
+/*
+ * Several GEMMs that share M and the group size, in one launch when M <= 16
+ * (for example the four projections of one layer at a decode step: one weight
+ * stream and one launch instead of four). `problems` is host memory read
+ * during the call; count is 1..W4A16_MAX_PROBLEMS. The workspace is sized by
+ * w4a16_workspace_bytes(M, sum of N). Each problem is validated as in
+ * w4a16_gemm; for M > 16 the problems run one after another on `stream`.
+ */
+#define W4A16_MAX_PROBLEMS 8
+int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int group,
+                       void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
 
 /* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
  * host integers), or -1 for an unsupported shape. */

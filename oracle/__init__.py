@@ -49,7 +49,7 @@ def _load():
         lib.oracle_pack.restype = c_int
         lib.oracle_pack.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int]
         lib.oracle_unpack.restype = c_int
-        lib.oracle_unpack.argtypes = [vp, vp, c_int, c_int]
+        lib.oracle_unpack.argtypes = [vp, vp, c_int, c_int, c_int]
         _lib = lib
     return _lib
 
@@ -87,13 +87,21 @@ def gemm(x_bf16: np.ndarray, q: np.ndarray, s_fp16: np.ndarray, group: int,
     return y
 
 
+def blocks(N: int) -> int:
+    return (N + 15) // 16
+
+
 def pack(q: np.ndarray, s_fp16: np.ndarray, group: int):
-    """(qweight uint32 [N][K/8], scales fp16 bits [K/group][N]) in the packed format."""
+    """(qweight uint32 [blocks*16*K/8], scales fp16 bits [blocks*(K/group)*16]) in the
+    device arrangement described in oracle.c."""
     q = _c(q, np.int8)
     s = _c(s_fp16, np.uint16)
     N, K = q.shape
-    qw = np.empty((N, K // 8), dtype=np.uint32)
-    sp = np.empty((K // group if group else 0, N), dtype=np.uint16)
+    if group <= 0 or group % 32 or K % group or s.shape != (N, K // group):
+        raise ValueError("oracle_pack: bad shape")
+    B = blocks(N)
+    qw = np.empty(B * 16 * K // 8, dtype=np.uint32)
+    sp = np.empty(B * (K // group) * 16, dtype=np.uint16)
     rc = _load().oracle_pack(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data,
                              N, K, group)
     if rc != 0:
@@ -101,11 +109,12 @@ def pack(q: np.ndarray, s_fp16: np.ndarray, group: int):
     return qw, sp
 
 
-def unpack(qweight: np.ndarray, K: int) -> np.ndarray:
+def unpack(qweight: np.ndarray, N: int, K: int, group: int) -> np.ndarray:
     qw = _c(qweight, np.uint32)
-    N = qw.shape[0]
+    if qw.size != blocks(N) * 16 * K // 8:
+        raise ValueError("oracle_unpack: bad size")
     q = np.empty((N, K), dtype=np.int8)
-    rc = _load().oracle_unpack(qw.ctypes.data, q.ctypes.data, N, K)
+    rc = _load().oracle_unpack(qw.ctypes.data, q.ctypes.data, N, K, group)
     if rc != 0:
         raise ValueError("oracle_unpack rejected the input")
     return q

@@ -22,11 +22,17 @@
  * x*w is exact (8 + 15 <= 53 bits), and the sum runs in increasing k, so
  * the only rounding is that of the double additions. Output stays in double.
  *
- * The packed format (a reading of the pages, which say nothing about it):
- *   qweight[n][j] (uint32, j = 0..K/8-1) holds q[n][8j+i] in bits 4i..4i+3 as a
- *   4-bit two's-complement code; scales are stored group-major: sp[j][n] =
- *   s[n][j]. Unpacking a code c gives ((c ^ 8) - 8).
- */
+ * The packed format (a reading of the pages, which say nothing about it).
+ * Logical words: word j of output column n holds the codes of k = 8j..8j+7,
+ * code of k = 8j+i in bits 4i..4i+3 as 4-bit two's complement (q & 0xF);
+ * unpacking a code c gives ((c ^ 8) - 8). Device arrangement: columns are
+ * taken in blocks of 16 (the last block padded with zero codes and zero
+ * scales), and each (column block b, group t) tile of 16 columns x g weights
+ * is stored contiguously as 64 lanes of g/32 consecutive words: lane l holds,
+ * for column 16b + (l mod 16), the g/32 logical words that start at word
+ * t*(g/8) + (l div 16)*(g/32). Tiles are ordered block-major, then by group.
+ * Scales are stored as [block][group][16]: entry (b, t, c) = s[16b + c][t].
+  */
 #include <math.h>
 #include <pthread.h>
 #include <stdint.h>
@@ -134,43 +140,68 @@ int oracle_gemm_f64(const uint16_t* x, const int8_t* q, const uint16_t* s, doubl
 
 /* ---- the packed format ---- */
 
+/* Logical word j of column n (n < N), from the codes q[n][8j .. 8j+7]. */
+static uint32_t oracle_logical_word(const int8_t* q, int K, int n, int j) {
+  uint32_t word = 0;
+  for (int i = 0; i < 8; ++i) {
+    uint32_t code = (uint32_t)(q[(size_t)n * K + 8 * j + i] & 0xF);
+    word |= code << (4 * i);
+  }
+  return word;
+}
+
+static int oracle_pack_shape_ok(int N, int K, int group) {
+  return N >= 0 && K >= 0 && group > 0 && group % 32 == 0 && K % group == 0;
+}
+
+/* Number of 16-column blocks. */
+static int oracle_blocks(int N) { return (N + 15) / 16; }
+
 /*
- * Pack q[N][K] (int8, each in -8..7) into qweight[N][K/8] and copy the scales
- * s[N][K/group] into group-major sp[K/group][N]. Returns 0; 1 if a shape is
- * invalid (K % 8, K % group, group % 8) or any code is out of range, in which
- * case nothing is written.
+ * Pack q[N][K] (int8, each in -8..7) and s[N][K/group] (fp16 bits) into the
+ * device arrangement: qweight holds blocks*16*K/8 words, sp holds
+ * blocks*(K/group)*16 fp16 values. Returns 0; 1 (nothing written) if the shape
+ * is invalid (group % 32, K % group) or a code is out of range.
  */
 int oracle_pack(const int8_t* q, const uint16_t* s, uint32_t* qweight, uint16_t* sp,
                 int N, int K, int group) {
-  if (N < 0 || K < 0 || group <= 0 || K % 8 != 0 || group % 8 != 0 || K % group != 0) return 1;
+  if (!oracle_pack_shape_ok(N, K, group)) return 1;
   for (size_t i = 0; i < (size_t)N * K; ++i)
     if (q[i] < -8 || q[i] > 7) return 1;
-  const int W = K / 8, G = K / group;
-  for (int n = 0; n < N; ++n) {
-    for (int j = 0; j < W; ++j) {
-      uint32_t word = 0;
-      for (int i = 0; i < 8; ++i) {
-        uint32_t code = (uint32_t)(q[(size_t)n * K + 8 * j + i] & 0xF);
-        word |= code << (4 * i);
+  const int B = oracle_blocks(N), G = K / group, wpl = group / 32;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < G; ++t) {
+      for (int l = 0; l < 64; ++l) {
+        const int n = 16 * b + l % 16;
+        for (int w = 0; w < wpl; ++w) {
+          const int j = t * (group / 8) + (l / 16) * wpl + w;
+          const size_t dst = (((size_t)b * G + t) * 64 + l) * wpl + w;
+          qweight[dst] = n < N ? oracle_logical_word(q, K, n, j) : 0u;
+        }
       }
-      qweight[(size_t)n * W + j] = word;
+      for (int c = 0; c < 16; ++c) {
+        const int n = 16 * b + c;
+        sp[((size_t)b * G + t) * 16 + c] = n < N ? s[(size_t)n * G + t] : (uint16_t)0;
+      }
     }
-    for (int g = 0; g < G; ++g) sp[(size_t)g * N + n] = s[(size_t)n * G + g];
-  }
   return 0;
 }
 
-/* Inverse of the weight half of oracle_pack: qweight[N][K/8] -> q[N][K]. */
-int oracle_unpack(const uint32_t* qweight, int8_t* q, int N, int K) {
-  if (N < 0 || K < 0 || K % 8 != 0) return 1;
-  const int W = K / 8;
-  for (int n = 0; n < N; ++n)
-    for (int j = 0; j < W; ++j) {
-      uint32_t word = qweight[(size_t)n * W + j];
+/* Inverse of the weight half of oracle_pack: device words -> q[N][K]. */
+int oracle_unpack(const uint32_t* qweight, int8_t* q, int N, int K, int group) {
+  if (!oracle_pack_shape_ok(N, K, group)) return 1;
+  const int G = K / group, wpl = group / 32;
+  for (int n = 0; n < N; ++n) {
+    const int b = n / 16, c = n % 16;
+    for (int j = 0; j < K / 8; ++j) {
+      const int t = j / (group / 8), r = j % (group / 8);
+      const int l = (r / wpl) * 16 + c, w = r % wpl;
+      const uint32_t word = qweight[(((size_t)b * G + t) * 64 + l) * wpl + w];
       for (int i = 0; i < 8; ++i) {
-        int code = (int)((word >> (4 * i)) & 0xF);
+        const int code = (int)((word >> (4 * i)) & 0xF);
         q[(size_t)n * K + 8 * j + i] = (int8_t)((code ^ 8) - 8);
       }
     }
+  }
   return 0;
 }

@@ -59,3 +59,23 @@ def tolerance_ratio(y_bits: np.ndarray, y_ref: np.ndarray) -> float:
     if not np.isfinite(y).all():
         return float("inf")
     return float(np.max(np.abs(y - y_ref) / (TOL * (1.0 + np.abs(y_ref)))))
+
+
+def workspace(M: int, total_columns: int):
+    """A zero-filled device workspace for the streaming entry points."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = torch_mod()
+    nbytes = w4.w4a16_workspace_bytes(M, total_columns)
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
+
+
+def run_ws(prob: "Problem", ws=None) -> np.ndarray:
+    """One call of w4a16_gemm_ws (streaming kernel for M <= 16)."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = torch_mod()
+    if ws is None:
+        ws = workspace(prob.M, prob.N)
+    y = torch.empty((prob.M, prob.N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm_ws(prob.x, prob.qw, prob.sp, y, prob.M, prob.N, prob.K, prob.group, ws)
+    torch.cuda.synchronize()
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)

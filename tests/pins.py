@@ -8,10 +8,8 @@ invariants (identity activation, one-hot activation, linearity) and a library
 matmul over weights dequantized by separate code. The same checks run against
 planted mistakes (``test_oracle_pins.py``) to show that each one bites.
 
-Conventions (packed format, a reading of pages that leave it open):
-  q int8 [N, K] in -8..7; x bf16 bits [M, K]; s fp16 bits [N, K/group];
-  qweight uint32 [N, K/8], code of q[n][8j+i] in bits 4i..4i+3 (two's complement);
-  packed scales fp16 bits [K/group, N] (group-major).
+Conventions: q int8 [N, K] in -8..7; x bf16 bits [M, K]; s fp16 bits
+[N, K/group]; the packed arrangement is described above pin_golden_words.
 """
 from __future__ import annotations
 
@@ -48,9 +46,15 @@ def fp16_to_f64(bits) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- packing
+#
+# Device arrangement (oracle.c states it in full): logical word j of column n
+# holds the codes of k = 8j..8j+7 (code of k = 8j+i in bits 4i..4i+3, two's
+# complement); tiles of 16 columns x one group are stored lane-major, lane l
+# holding g/32 consecutive logical words of column 16b + l%16 starting at
+# word t*g/8 + (l//16)*g/32; scales are [block][group][16].
 
-# (codes q[0..7] of one word, expected uint32), derived by hand: the code of
-# q[i] is q[i] & 0xF, placed at bits 4i..4i+3.
+# (codes q[0..7] of one logical word, expected uint32), derived by hand: the
+# code of q[i] is q[i] & 0xF, placed at bits 4i..4i+3.
 GOLDEN_WORDS = [
     ([0, 1, 2, 3, 4, 5, 6, 7], 0x76543210),
     ([-1] * 8, 0xFFFFFFFF),
@@ -64,60 +68,95 @@ GOLDEN_WORDS = [
 
 
 def pin_golden_words(pack):
-    q = np.array([c for c, _ in GOLDEN_WORDS], dtype=np.int8)           # N = 8 columns, K = 8
-    s = fp16_bits(np.ones((len(GOLDEN_WORDS), 1)))
-    qw, _ = pack(q, s, 8)
-    expect = np.array([[w] for _, w in GOLDEN_WORDS], dtype=np.uint32)
-    assert np.array_equal(qw, expect), [hex(v) for v in qw.ravel()]
-    # two words in one column: word j holds k = 8j..8j+7
-    q2 = np.array([[0, 1, 2, 3, 4, 5, 6, 7, -1, -1, -1, -1, -1, -1, -1, -1]], dtype=np.int8)
-    qw2, _ = pack(q2, fp16_bits([[1.0]]), 16)
-    assert qw2.tolist() == [[0x76543210, 0xFFFFFFFF]], [hex(v) for v in qw2.ravel()]
+    # N = 8 columns (one block, padded to 16), K = 32, group 32 (one word per
+    # lane, one group): lane l holds logical word l // 16 of column l % 16. The
+    # golden codes fill k = 0..7 of each column, so lanes 0..7 hold the golden
+    # words and every other lane (padding columns, or words 1..3) is zero.
+    q = np.zeros((8, 32), dtype=np.int8)
+    q[:, :8] = np.array([c for c, _ in GOLDEN_WORDS], dtype=np.int8)
+    qw, _ = pack(q, fp16_bits(np.ones((8, 1))), 32)
+    expect = np.zeros(64, dtype=np.uint32)
+    expect[:8] = [w for _, w in GOLDEN_WORDS]
+    assert np.array_equal(np.asarray(qw).ravel(), expect), [hex(v) for v in np.asarray(qw).ravel()]
+    # one column, codes 0..7 then eight -1: logical words 0x76543210, 0xFFFFFFFF,
+    # 0, 0 land in lanes 0, 16, 32, 48
+    q2 = np.zeros((1, 32), dtype=np.int8)
+    q2[0, :16] = [0, 1, 2, 3, 4, 5, 6, 7] + [-1] * 8
+    qw2 = np.asarray(pack(q2, fp16_bits([[1.0]]), 32)[0]).ravel()
+    expect2 = np.zeros(64, dtype=np.uint32)
+    expect2[0], expect2[16] = 0x76543210, 0xFFFFFFFF
+    assert np.array_equal(qw2, expect2), [hex(v) for v in qw2]
+
+
+def pin_tile_positions(pack):
+    """Three codes placed by hand in N = 20 (two blocks), K = 128, group 64
+    (two words per lane, eight words per column per group, two groups)."""
+    q = np.zeros((20, 128), dtype=np.int8)
+    q[17, 100] = -3   # block 1, column 1; word 12 = group 1, word 4 of it -> lane 2*16+1 = 33,
+    #                   word 0 of the lane; index ((1*2+1)*64+33)*2 = 450; code 0xD at nibble 4
+    q[2, 7] = 5       # block 0, column 2; word 0, nibble 7 -> lane 2, index 4; 5 << 28
+    q[19, 127] = -8   # block 1, column 3; word 15 = group 1, word 7 -> lane 3*16+3 = 51,
+    #                   word 1 of the lane; index ((1*2+1)*64+51)*2+1 = 487; 0x8 << 28
+    qw = np.asarray(pack(q, fp16_bits(np.ones((20, 2))), 64)[0]).ravel()
+    assert qw.size == 2 * 16 * 128 // 8
+    expect = np.zeros(512, dtype=np.uint32)
+    expect[450], expect[4], expect[487] = 0x000D0000, 0x50000000, 0x80000000
+    assert np.array_equal(qw, expect), [(i, hex(v)) for i, v in enumerate(qw) if v]
 
 
 def pin_scale_layout(pack):
-    N, K, g = 3, 32, 8
-    s = fp16_bits(np.arange(N * (K // g), dtype=np.float64).reshape(N, K // g) + 1.0)
-    _, sp = pack(np.zeros((N, K), dtype=np.int8), s, g)
-    # group-major: sp[j][n] == s[n][j]
-    assert sp.shape == (K // g, N)
-    for n in range(N):
-        for j in range(K // g):
-            assert sp[j, n] == s[n, j]
+    # N = 20 (two blocks), K = 64, group 32: s[n][t] = 2n + t + 1 (exact in fp16),
+    # stored as [block][group][16] with zero scales for the padding columns.
+    N, K, g = 20, 64, 32
+    s = fp16_bits(2.0 * np.arange(N)[:, None] + np.arange(K // g)[None, :] + 1.0)
+    sp = np.asarray(pack(np.zeros((N, K), dtype=np.int8), s, g)[1]).ravel()
+    v = fp16_to_f64(sp)
+    assert v.size == 2 * 2 * 16
+    assert v[0] == 1.0 and v[1] == 3.0 and v[15] == 31.0      # block 0, group 0: n = 0, 1, 15
+    assert v[16] == 2.0 and v[31] == 32.0                     # block 0, group 1: n = 0, 15
+    assert v[32] == 33.0 and v[35] == 39.0 and v[36] == 0.0   # block 1, group 0: n = 16, 19, pad
+    assert v[48] == 34.0 and v[51] == 40.0 and v[52:].sum() == 0.0  # block 1, group 1
+    assert np.count_nonzero(v) == N * (K // g)
 
 
 def pin_pack_roundtrip(pack, unpack):
     rng = np.random.default_rng(7)
-    # every combination of the four low codes of a word, high codes random, and vice versa
+    # every combination of four codes of a logical word (others random), both halves
     combos = np.array(np.meshgrid(*[np.arange(-8, 8)] * 4, indexing="ij")).reshape(4, -1).T
-    hi = rng.integers(-8, 8, size=(combos.shape[0], 4))
-    for q in (np.concatenate([combos, hi], axis=1), np.concatenate([hi, combos], axis=1)):
-        q = q.astype(np.int8)
-        qw, _ = pack(q, fp16_bits(np.ones((q.shape[0], 1))), 8)
-        assert np.array_equal(unpack(qw, 8), q)
-    # random matrices at the workload's group sizes
-    for (N, K, g) in [(5, 256, 64), (3, 1024, 128), (17, 128, 128)]:
+    for half in range(2):
+        N = combos.shape[0] // 64                   # 1024 columns, 64 combinations each
+        q = rng.integers(-8, 8, size=(N, 512)).astype(np.int8)
+        blk = combos.reshape(N, 64, 4)
+        for c in range(64):
+            q[:, 8 * c + 4 * half: 8 * c + 4 * half + 4] = blk[:, c, :]
+        qw, _ = pack(q, fp16_bits(np.ones((N, 4))), 128)
+        assert np.array_equal(unpack(qw, N, 512, 128), q)
+    # random matrices, ragged and whole column blocks, every group size
+    for (N, K, g) in [(5, 256, 64), (3, 1024, 128), (17, 128, 128), (40, 512, 256), (33, 96, 32)]:
         q = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
         qw, _ = pack(q, fp16_bits(np.ones((N, K // g))), g)
-        assert np.array_equal(unpack(qw, K), q)
-    # pack(unpack(w)) == w for arbitrary words (every 32-bit word is a valid packing)
-    words = rng.integers(0, 1 << 32, size=(64, 32), dtype=np.uint64).astype(np.uint32)
-    words[0, :8] = [0, 0xFFFFFFFF, 0x88888888, 0x77777777, 0x12345678, 0x87654321, 0xF0F0F0F0, 1]
-    q = unpack(words, 256)
-    qw, _ = pack(q, fp16_bits(np.ones((64, 2))), 128)
-    assert np.array_equal(qw, words)
+        assert np.array_equal(unpack(qw, N, K, g), q)
+    # pack(unpack(w)) == w for arbitrary words when N fills whole blocks
+    words = rng.integers(0, 1 << 32, size=64 * 32, dtype=np.uint64).astype(np.uint32)
+    words[:8] = [0, 0xFFFFFFFF, 0x88888888, 0x77777777, 0x12345678, 0x87654321, 0xF0F0F0F0, 1]
+    q = unpack(words, 32, 512, 128)
+    qw, _ = pack(q, fp16_bits(np.ones((32, 4))), 128)
+    assert np.array_equal(np.asarray(qw).ravel(), words)
 
 
 def pin_pack_rejects(pack):
-    bad = np.zeros((2, 16), dtype=np.int8)
+    bad = np.zeros((2, 64), dtype=np.int8)
     bad[1, 3] = 8
-    for q, g in [(bad, 8), (np.full((1, 8), -9, dtype=np.int8), 8)]:
+    cases = [(bad, 32), (np.full((1, 32), -9, dtype=np.int8), 32),
+             (np.zeros((1, 48), dtype=np.int8), 16),       # group not a multiple of 32
+             (np.zeros((1, 96), dtype=np.int8), 64)]       # K not a multiple of the group
+    for q, g in cases:
         try:
-            pack(q, fp16_bits(np.ones((q.shape[0], q.shape[1] // g))), g)
+            pack(q, fp16_bits(np.ones((q.shape[0], max(q.shape[1] // g, 1)))), g)
         except ValueError:
             pass
         else:
-            raise AssertionError("out-of-range code accepted")
+            raise AssertionError(f"accepted bad input (K={q.shape[1]}, group={g})")
 
 
 # ---------------------------------------------------------------- the GEMM

@@ -41,7 +41,9 @@ def test_version_and_status_strings():
 def test_sizes():
     assert w4.w4a16_qweight_bytes(7168, 5120) == 7168 * 5120 // 2
     assert w4.w4a16_scales_bytes(7168, 5120, 128) == 7168 * 40 * 2
-    assert w4.w4a16_qweight_bytes(4, 12) == 0          # K % 8
+    assert w4.w4a16_qweight_bytes(20, 64) == 32 * 64 // 2   # padded to 2 blocks of 16
+    assert w4.w4a16_scales_bytes(20, 64, 32) == 32 * 2 * 2
+    assert w4.w4a16_qweight_bytes(4, 48) == 0          # K % 32
     assert w4.w4a16_scales_bytes(4, 96, 64) == 0       # K % group
     assert w4.w4a16_qweight_bytes(-1, 8) == 0
 
@@ -85,13 +87,13 @@ def test_pack_rejects_and_writes_nothing():
     q = np.zeros((N, K), np.int8)
     q[3, 63] = -9
     s = np.ones((N, K // g), np.uint16)
-    qw = np.full((N, K // 8), 0xDEADBEEF, np.uint32)
-    sp = np.full((K // g, N), 0xABCD, np.uint16)
+    qw = np.full(w4.w4a16_qweight_bytes(N, K) // 4, 0xDEADBEEF, np.uint32)
+    sp = np.full(w4.w4a16_scales_bytes(N, K, g) // 2, 0xABCD, np.uint16)
     rc = w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, g)
     assert rc == w4.W4A16_ERR_INVALID_ARG
     assert (qw == 0xDEADBEEF).all() and (sp == 0xABCD).all()
     # bad shapes
-    for (K2, g2) in [(60, 30), (64, 12), (64, 48), (12, 4)]:
+    for (K2, g2) in [(60, 30), (64, 12), (64, 48), (12, 4), (96, 64)]:
         assert w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data,
                               N, K2, g2) == w4.W4A16_ERR_INVALID_ARG
     # null pointers with a non-empty shape, and the empty shape
@@ -100,7 +102,9 @@ def test_pack_rejects_and_writes_nothing():
     # a valid call right after the failures succeeds
     q[3, 63] = 7
     assert w4.pack_status(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, g) == 0
-    assert qw[3, 7] == 0x70000000
+    # column 3, k = 63: logical word 7 = group 1 (4 words per column per group of 32),
+    # its word 3 -> lane 3*16 + 3 = 51 of tile 1 -> word 64 + 51 = 115; code 7 at nibble 7
+    assert qw[115] == 0x70000000 and np.count_nonzero(qw) == 1
 
 
 # Fake, never-dereferenced addresses: every call below fails its host checks
@@ -133,3 +137,28 @@ def test_select_path():
     assert w4.w4a16_select_path(1024, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
     assert w4.w4a16_select_path(1, 512, 256, 48) == -1
     assert w4.w4a16_select_path(-1, 512, 256, 64) == -1
+
+
+def test_workspace_sizes():
+    assert w4.w4a16_workspace_bytes(-1, 10) == 0
+    a = w4.w4a16_workspace_bytes(1, 52224)
+    b = w4.w4a16_workspace_bytes(16, 52224)
+    assert 0 < a < b
+    assert w4.w4a16_workspace_bytes(16, 52224) == w4.w4a16_workspace_bytes(64, 52224)
+    assert w4.w4a16_workspace_bytes(0, 160) % 256 == 0
+
+
+def test_grouped_argument_checks_without_launch():
+    st = w4.grouped_status
+    ok = (A, A, A, A, 512, 256)
+    nb = w4.w4a16_workspace_bytes(4, 512)
+    assert st([ok], 0, 64, A * 16, nb) == w4.W4A16_OK                        # M == 0
+    assert st([ok] * 9, 4, 64, A * 16, nb) == w4.W4A16_ERR_INVALID_ARG        # too many
+    assert st([ok], -1, 64, A * 16, nb) == w4.W4A16_ERR_INVALID_ARG
+    assert st([ok], 4, 48, A * 16, nb) == w4.W4A16_ERR_UNSUPPORTED
+    assert st([(A, A, A, A, 512, 200)], 4, 64, A * 16, nb) == w4.W4A16_ERR_UNSUPPORTED
+    assert st([(A, None, A, A, 512, 256)], 4, 64, A * 16, nb) == w4.W4A16_ERR_INVALID_ARG
+    assert st([(A + 4, A, A, A, 512, 256)], 4, 64, A * 16, nb) == w4.W4A16_ERR_MISALIGNED
+    assert st([ok], 4, 64, None, nb) == w4.W4A16_ERR_INVALID_ARG              # no workspace
+    assert st([ok], 4, 64, A * 16, nb - 1) == w4.W4A16_ERR_INVALID_ARG        # too small
+    assert st([ok], 4, 64, A * 16 + 16, nb) == w4.W4A16_ERR_MISALIGNED        # not 256-aligned

@@ -33,6 +33,10 @@ def test_oracle_scale_layout():
     pins.pin_scale_layout(oracle.pack)
 
 
+def test_oracle_tile_positions():
+    pins.pin_tile_positions(oracle.pack)
+
+
 def test_oracle_pack_roundtrip():
     pins.pin_pack_roundtrip(oracle.pack, oracle.unpack)
 
@@ -47,7 +51,7 @@ def test_oracle_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.gemm(x, q, np.zeros((2, 1), np.uint16), 16)  # K % group != 0
     with pytest.raises(ValueError):
-        oracle.pack(np.zeros((2, 12), np.int8), np.zeros((2, 1), np.uint16), 12)  # K % 8, group % 8
+        oracle.pack(np.zeros((2, 48), np.int8), np.zeros((2, 1), np.uint16), 48)  # group % 32
 
 
 def test_oracle_thread_count_invariant():
@@ -139,8 +143,7 @@ def test_planted_gemm_mistake_is_caught(mutant):
 
 
 def _pack_nibbles_reversed(q, s, g):
-    qw, sp = oracle.pack(q[:, ::-1].reshape(q.shape[0], -1, 8)[:, ::-1, :].reshape(q.shape).copy(), s, g)
-    return qw, sp
+    return oracle.pack(q.reshape(q.shape[0], -1, 8)[:, :, ::-1].reshape(q.shape).copy(), s, g)
 
 
 def _pack_offset_binary(q, s, g):
@@ -149,18 +152,36 @@ def _pack_offset_binary(q, s, g):
 
 
 def _pack_scales_row_major(q, s, g):
-    qw, _ = oracle.pack(q, s, g)
-    return qw, s.copy()
+    qw, sp = oracle.pack(q, s, g)
+    flat = np.zeros_like(sp)
+    flat[:s.size] = s.ravel()
+    return qw, flat
 
 
-def _unpack_offset_binary(qw, K):
-    return oracle.unpack(qw ^ np.uint32(0x88888888), K)
+def _pack_untiled(q, s, g):
+    # logical words in plain [N][K/8] order (columns padded to 16), no lane tiling
+    qw, sp = oracle.pack(q, s, g)
+    N, K = q.shape
+    Np = oracle.blocks(N) * 16
+    qp = np.zeros((Np, K), np.int8)
+    qp[:N] = q
+    words = np.zeros((Np, K // 8), np.uint32)
+    codes = (qp.astype(np.int64) & 0xF).astype(np.uint32).reshape(Np, K // 8, 8)
+    for i in range(8):
+        words |= codes[:, :, i] << np.uint32(4 * i)
+    return words.ravel(), sp
+
+
+def _unpack_offset_binary(qw, N, K, g):
+    return oracle.unpack(qw ^ np.uint32(0x88888888), N, K, g)
 
 
 @pytest.mark.parametrize("mutant", [_pack_nibbles_reversed, _pack_offset_binary,
-                                    _pack_scales_row_major], ids=lambda f: f.__name__)
+                                    _pack_scales_row_major, _pack_untiled],
+                         ids=lambda f: f.__name__)
 def test_planted_pack_mistake_is_caught(mutant):
     caught = _fails_some_pin([lambda: pins.pin_golden_words(mutant),
+                              lambda: pins.pin_tile_positions(mutant),
                               lambda: pins.pin_scale_layout(mutant)])
     assert caught, f"{mutant.__name__} passed every pin"
 

@@ -38,6 +38,13 @@ W4A16_PATH_AUTO = 0
 W4A16_PATH_SKINNY = 1
 W4A16_PATH_LARGE = 2
 
+W4A16_MAX_PROBLEMS = 8
+
+
+class w4a16_problem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
+
 # Every symbol include/w4a16.h declares, with its ctypes signature.
 _vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
@@ -46,6 +53,9 @@ SIGNATURES = {
     "w4a16_pack": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int]),
     "w4a16_gemm": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "w4a16_gemm_ex": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
+    "w4a16_workspace_bytes": (_sz, [_int, ctypes.c_longlong]),
+    "w4a16_gemm_ws": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _sz, _vp]),
+    "w4a16_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_version": (_int, []),
@@ -84,7 +94,8 @@ def w4a16_select_path(M: int, N: int, K: int, group: int) -> int:
 
 def w4a16_pack(q: np.ndarray, scales: np.ndarray, group: int):
     """Host packing: q int8 [N, K] in -8..7 and fp16 scales [N, K/group] (float16 or
-    uint16 bit patterns) -> (qweight uint32 [N, K/8], scales uint16 [K/group, N])."""
+    uint16 bit patterns) -> (qweight uint32, scales uint16) as flat arrays in the
+    device arrangement (w4a16_qweight_bytes / w4a16_scales_bytes long)."""
     q = np.ascontiguousarray(q)
     if q.dtype != np.int8 or q.ndim != 2:
         raise TypeError("q must be a 2-D int8 array")
@@ -94,10 +105,10 @@ def w4a16_pack(q: np.ndarray, scales: np.ndarray, group: int):
     if s.dtype != np.uint16 or s.ndim != 2:
         raise TypeError("scales must be a 2-D float16 or uint16 array")
     N, K = q.shape
-    if group <= 0 or K % group != 0 or s.shape != (N, K // group):
+    if group <= 0 or group % 32 != 0 or K % group != 0 or s.shape != (N, K // group):
         raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_pack")
-    qw = np.empty((N, K // 8), dtype=np.uint32)
-    sp = np.empty((K // group, N), dtype=np.uint16)
+    qw = np.empty(w4a16_qweight_bytes(N, K) // 4, dtype=np.uint32)
+    sp = np.empty(w4a16_scales_bytes(N, K, group) // 2, dtype=np.uint16)
     rc = _lib.w4a16_pack(q.ctypes.data, s.ctypes.data, qw.ctypes.data, sp.ctypes.data, N, K, group)
     if rc != W4A16_OK:
         raise W4A16Error(rc, "w4a16_pack")
@@ -174,3 +185,48 @@ def gemm_status(x, qweight, scales, y, M, N, K, group, path=W4A16_PATH_AUTO, str
 def pack_status(q_ptr, s_ptr, qw_ptr, sp_ptr, N, K, group) -> int:
     """Raw status of w4a16_pack on raw host addresses (for tests of the error paths)."""
     return int(_lib.w4a16_pack(q_ptr, s_ptr, qw_ptr, sp_ptr, N, K, group))
+
+
+def w4a16_workspace_bytes(M: int, total_columns: int) -> int:
+    return int(_lib.w4a16_workspace_bytes(M, total_columns))
+
+
+def w4a16_gemm_ws(x, qweight, scales, y, M: int, N: int, K: int, group: int, workspace,
+                  workspace_bytes: int | None = None, stream=None) -> None:
+    """As w4a16_gemm, with a zero-initialised device workspace (torch tensor or address);
+    M <= 16 runs the streaming kernel."""
+    if group > 0 and K % group == 0:
+        _check_tensors(x, qweight, scales, y, M, N, K, group)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.w4a16_gemm_ws(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
+                            _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm_ws")
+
+
+def make_problems(entries):
+    """ctypes array of w4a16_problem from (x, qweight, scales, y, N, K) tuples."""
+    arr = (w4a16_problem * len(entries))()
+    for i, (x, qw, sp, y, N, K) in enumerate(entries):
+        arr[i] = w4a16_problem(_ptr(x), _ptr(qw), _ptr(sp), _ptr(y), N, K)
+    return arr
+
+
+def w4a16_gemm_grouped(problems, M: int, group: int, workspace, workspace_bytes: int | None = None,
+                       stream=None) -> None:
+    """Several GEMMs sharing M and the group size; `problems` is a list of
+    (x, qweight, scales, y, N, K) tuples or a make_problems() array."""
+    arr = problems if isinstance(problems, ctypes.Array) else make_problems(problems)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.w4a16_gemm_grouped(ctypes.cast(arr, ctypes.c_void_p), len(arr), M, group,
+                                 _ptr(workspace), workspace_bytes, _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm_grouped")
+
+
+def grouped_status(problems, M, group, workspace, workspace_bytes, stream=None) -> int:
+    arr = problems if isinstance(problems, ctypes.Array) else make_problems(problems)
+    return int(_lib.w4a16_gemm_grouped(ctypes.cast(arr, ctypes.c_void_p), len(arr), M, group,
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))

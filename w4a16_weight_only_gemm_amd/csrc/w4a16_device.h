@@ -15,6 +15,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Global (address space 1) views of pointers. Pointers read from a descriptor
+// in memory are generic to the compiler; through these, loads and stores are
+// global_* instructions (counted only by vmcnt) rather than flat_* (counted by
+// vmcnt and lgkmcnt, which would make every LDS wait also wait for them).
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return (gptr<T>)(p);  // address-space cast (generic to global)
+}
+
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt left at their maxima). Stores
+// and loads share the vector-memory counter but may retire out of order, so
+// while a store is outstanding the compiler must wait for every load in
+// flight before using any of them. Draining right after a rare store keeps a
+// hot loop's later waits exact.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A wave-uniform value moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // bf16 bit pattern of -136.0: sign 1, exponent 134 (2^7), fraction 8/128.
 constexpr uint32_t kBiasPair = 0xC308C308u;
 

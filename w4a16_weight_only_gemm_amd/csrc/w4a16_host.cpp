@@ -12,8 +12,10 @@
 namespace {
 
 bool pack_shape_ok(int N, int K, int group) {
-  return N >= 0 && K >= 0 && group > 0 && K % 8 == 0 && group % 8 == 0 && K % group == 0;
+  return N >= 0 && K >= 0 && group > 0 && group % 32 == 0 && K % group == 0;
 }
+
+size_t column_blocks(int N) { return (static_cast<size_t>(N) + 15) / 16; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -26,40 +28,54 @@ bool group_supported(int group) {
 extern "C" {
 
 size_t w4a16_qweight_bytes(int N, int K) {
-  if (N < 0 || K < 0 || K % 8 != 0) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(K) / 2;
+  if (N < 0 || K < 0 || K % 32 != 0) return 0;
+  return column_blocks(N) * 16 * static_cast<size_t>(K) / 2;
 }
 
 size_t w4a16_scales_bytes(int N, int K, int group) {
-  if (N < 0 || K < 0 || group <= 0 || K % group != 0) return 0;
-  return static_cast<size_t>(N) * static_cast<size_t>(K / group) * 2;
+  if (N < 0 || K < 0 || group <= 0 || group % 32 != 0 || K % group != 0) return 0;
+  return column_blocks(N) * 16 * static_cast<size_t>(K / group) * 2;
 }
 
 int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out,
                uint16_t* scales_out, int N, int K, int group) {
   if (!pack_shape_ok(N, K, group)) return W4A16_ERR_INVALID_ARG;
-  const size_t total = static_cast<size_t>(N) * static_cast<size_t>(K);
-  if (total == 0) return W4A16_OK;
+  if (N == 0 || K == 0) return W4A16_OK;
   if (!q || !scales_in || !qweight_out || !scales_out) return W4A16_ERR_INVALID_ARG;
+  const size_t total = static_cast<size_t>(N) * static_cast<size_t>(K);
   // Validate everything before writing anything.
   for (size_t i = 0; i < total; ++i) {
     if (q[i] < -8 || q[i] > 7) return W4A16_ERR_INVALID_ARG;
   }
-  const size_t words = static_cast<size_t>(K) / 8;
-  for (int n = 0; n < N; ++n) {
-    const int8_t* row = q + static_cast<size_t>(n) * K;
-    uint32_t* out = qweight_out + static_cast<size_t>(n) * words;
-    for (size_t j = 0; j < words; ++j) {
-      const int8_t* c = row + 8 * j;
-      uint32_t w = 0;
-      for (int i = 7; i >= 0; --i) w = (w << 4) | (static_cast<uint32_t>(c[i]) & 0xFu);
-      out[j] = w;
-    }
-  }
   const int G = K / group;
-  for (int n = 0; n < N; ++n) {
-    const uint16_t* src = scales_in + static_cast<size_t>(n) * G;
-    for (int g = 0; g < G; ++g) scales_out[static_cast<size_t>(g) * N + n] = src[g];
+  const int wpl = group / 32;           // words per lane per tile
+  const size_t blocks = column_blocks(N);
+  uint32_t* out = qweight_out;
+  uint16_t* sout = scales_out;
+  for (size_t b = 0; b < blocks; ++b) {
+    for (int t = 0; t < G; ++t) {
+      // tile (b, t): lane l = 16 * slice + column, holding wpl consecutive words
+      for (int slice = 0; slice < 4; ++slice) {
+        for (int col = 0; col < 16; ++col) {
+          const size_t n = b * 16 + col;
+          const int8_t* codes = q + n * K + static_cast<size_t>(t) * group + slice * wpl * 8;
+          for (int w = 0; w < wpl; ++w) {
+            uint32_t word = 0;
+            if (n < static_cast<size_t>(N)) {
+              for (int i = 7; i >= 0; --i)
+                word = (word << 4) | (static_cast<uint32_t>(codes[8 * w + i]) & 0xFu);
+            }
+            out[(slice * 16 + col) * wpl + w] = word;
+          }
+        }
+      }
+      out += 64 * wpl;
+      for (int col = 0; col < 16; ++col) {
+        const size_t n = b * 16 + col;
+        sout[col] = n < static_cast<size_t>(N) ? scales_in[n * G + t] : static_cast<uint16_t>(0);
+      }
+      sout += 16;
+    }
   }
   return W4A16_OK;
 }
@@ -99,6 +115,68 @@ int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, 
   return w4a16_gemm_ex(x, qweight, scales, y, M, N, K, group, W4A16_PATH_AUTO, stream);
 }
 
+size_t w4a16_workspace_bytes(int M, long long total_columns) {
+  if (M < 0 || total_columns < 0) return 0;
+  return w4a16_internal::streamk_counter_bytes(total_columns) +
+         w4a16_internal::streamk_part_bytes(M);
+}
+
+int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int group,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!problems || count < 1 || count > W4A16_MAX_PROBLEMS || M < 0)
+    return W4A16_ERR_INVALID_ARG;
+  if (M == 0) return W4A16_OK;
+  if (!group_supported(group)) return W4A16_ERR_UNSUPPORTED;
+  long long columns = 0;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem& p = problems[i];
+    if (p.N < 0 || p.K < 0) return W4A16_ERR_INVALID_ARG;
+    if (!p.x || !p.qweight || !p.scales || !p.y) return W4A16_ERR_INVALID_ARG;
+    if (p.N < 1 || p.K < 1 || p.K % group != 0) return W4A16_ERR_UNSUPPORTED;
+    if (!aligned16(p.x) || !aligned16(p.qweight) || !aligned16(p.scales) || !aligned16(p.y))
+      return W4A16_ERR_MISALIGNED;
+    columns += p.N;
+  }
+  if (M > 16) {
+    // Large M: the per-problem kernels, one launch each.
+    for (int i = 0; i < count; ++i) {
+      const w4a16_problem& p = problems[i];
+      const int rc = w4a16_gemm_ex(p.x, p.qweight, p.scales, p.y, M, p.N, p.K, group,
+                                   W4A16_PATH_AUTO, stream);
+      if (rc != W4A16_OK) return rc;
+    }
+    return W4A16_OK;
+  }
+  if (!workspace || workspace_bytes < w4a16_workspace_bytes(M, columns))
+    return W4A16_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return W4A16_ERR_MISALIGNED;
+  w4a16_internal::StreamKProblem probs[W4A16_MAX_PROBLEMS] = {};
+  for (int i = 0; i < count; ++i) {
+    probs[i].x = static_cast<const uint16_t*>(problems[i].x);
+    probs[i].qw = static_cast<const uint32_t*>(problems[i].qweight);
+    probs[i].sp = static_cast<const uint16_t*>(problems[i].scales);
+    probs[i].y = static_cast<uint16_t*>(problems[i].y);
+    probs[i].N = problems[i].N;
+    probs[i].K = problems[i].K;
+  }
+  char* ws = static_cast<char*>(workspace);
+  int* counters = reinterpret_cast<int*>(ws);
+  float* part = reinterpret_cast<float*>(ws + w4a16_internal::streamk_counter_bytes(columns));
+  const hipError_t err =
+      w4a16_internal::launch_streamk(probs, count, M, group, part, counters, stream);
+  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
+                  int K, int group, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
+  if (M > 16) return w4a16_gemm_ex(x, qweight, scales, y, M, N, K, group, W4A16_PATH_AUTO, stream);
+  w4a16_problem p = {x, qweight, scales, y, N, K};
+  if (M == 0) return W4A16_OK;
+  if (!x || !qweight || !scales || !y) return W4A16_ERR_INVALID_ARG;
+  return w4a16_gemm_grouped(&p, 1, M, group, workspace, workspace_bytes, stream);
+}
+
 const char* w4a16_status_string(int status) {
   switch (status) {
     case W4A16_OK: return "W4A16_OK: success";
@@ -113,3 +191,17 @@ const char* w4a16_status_string(int status) {
 int w4a16_version(void) { return 100; }
 
 }  // extern "C"
+
+namespace w4a16_internal {
+
+size_t streamk_counter_bytes(long long total_columns) {
+  const long long ints = kMaxProblems + (total_columns + 15) / 16;
+  return static_cast<size_t>((ints * 4 + 255) / 256 * 256);
+}
+
+size_t streamk_part_bytes(int M) {
+  const int rows = M < 16 ? M : 16;
+  return static_cast<size_t>(kStreamKMaxWaves) * 2 * rows * 16 * sizeof(float);
+}
+
+}  // namespace w4a16_internal

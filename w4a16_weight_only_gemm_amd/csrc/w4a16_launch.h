@@ -20,6 +20,41 @@ struct GemmArgs {
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream);
 
+// ---- stream-K (persistent, several problems per launch, M <= 16) ----
+constexpr int kMaxProblems = 8;
+constexpr int kStreamKMaxWaves = 8192;          // grid never exceeds this many waves
+constexpr size_t kStreamKLdsBudget = 64 * 1024;  // staged activations per workgroup
+
+struct StreamKProblem {
+  const uint16_t* x;        // bf16 [M][K]
+  const uint32_t* qw;       // packed weights (device arrangement)
+  const uint16_t* sp;       // packed scales
+  uint16_t* y;              // bf16 [M][N]
+  int N, K;
+  // filled in by launch_streamk
+  int G, NCB;               // groups per column, 16-column blocks
+  long long u_begin;        // first unit (column block, group) of this problem
+  int cb_begin;             // first column block (index of its counter)
+};
+
+struct StreamKArgs {
+  StreamKProblem prob[kMaxProblems];
+  int nprob;
+  int M;
+  long long units;          // total units over all problems
+  int nwaves;               // waves that own units (<= units)
+  float* part;              // [kStreamKMaxWaves][2][min(M,16)][16] fp32 parts
+  int* counters;            // one per column block, zero between calls
+};
+
+// Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints,
+// rounded up to 256 bytes), then the parts.
+size_t streamk_counter_bytes(long long total_columns);
+size_t streamk_part_bytes(int M);
+
+hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
+                          int* counters, hipStream_t stream);
+
 // M-dispatch: W4A16_PATH_SKINNY or W4A16_PATH_LARGE for a supported shape.
 int choose_path(int M, int N, int K, int group);
 

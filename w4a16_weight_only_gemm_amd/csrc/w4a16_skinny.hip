@@ -1,32 +1,35 @@
-// w4a16_skinny.hip -- the small-M path (decode and speculative-verify blocks).
+// w4a16_skinny.hip -- the small-M paths (decode and speculative-verify blocks).
 //
 // At small M the GEMM is bound by the weight stream: every packed weight is
 // read from HBM exactly once and shared by all M rows (ai.satyajit.si page,
-// section "One weight read, shared by every stream"). The kernel is built
-// around that stream:
+// section "One weight read, shared by every stream"). Both kernels here are
+// built around that stream and share one inner step:
 //
-//  * A workgroup owns a 16-column tile and the whole K range, split evenly
-//    over its WAVES waves (split-K inside the workgroup, reduced through LDS at
-//    the end, so there is no cross-workgroup traffic and no workspace).
-//  * Within a wave, lane l serves column (l % 16) and k-slice (l / 16) of
-//    every MFMA step. Per group of GS weights a lane issues one vector load of
-//    GS/32 consecutive packed words of its column (16 bytes at GS = 128);
-//    those words are exactly its B operands for the GS/32 MFMA steps of the
-//    group, so packed weights go HBM -> VGPR -> dequant -> MFMA without LDS.
+//  * A unit is one tile of the packed format: 16 output columns x one group
+//    (1 KB of packed weights at group 128), stored contiguously in the order
+//    lane l of a wavefront needs it: its words are exactly its B operands for
+//    the group's MFMA steps (lane l serves column l % 16 and k-slice l / 16 of
+//    every step). A wave therefore loads a unit with one contiguous vector load
+//    and feeds it HBM -> VGPR -> dequant -> MFMA without LDS.
 //  * Dequantization is to the exact biased value 136 + q in bf16 (two VALU
-//    ops per bf16 pair); after each step a second MFMA against a constant
-//    -136 operand removes the bias, so the MFMA sees exact codes, products are
-//    exact and the fp32 accumulator holds sum(x * q) for the group.
-//  * The group's fp32 partial is scaled by s[group][n] and added to the
-//    running fp32 result (one FMA per output element per group).
-//  * Rows are padded to 16 (RB row blocks of 16 per workgroup); padded rows
-//    repeat row M-1 and are never stored.
+//    ops per bf16 pair); a second MFMA against a constant -136 operand removes
+//    the bias, so the MFMA sees exact codes, products are exact and the fp32
+//    accumulator holds sum(x * q) over the group. The group's partial is then
+//    scaled by its fp16 scale and added to the running fp32 result.
+//  * Rows are padded to 16: padded rows repeat row M-1 and are never stored
+//    (an MFMA output row depends only on its own A row).
 //
-// Loads of weights and scales run P groups ahead of the math in a register
-// ring; activations (L2-resident) are loaded at the top of their group and
-// waited for after the dequantization. Weights use non-temporal loads since
-// each byte is read once. Every load is unconditional (indices are clamped),
-// which keeps the wait counters exact and the loop on scalar branches.
+// splitk_kernel: a workgroup owns one 16-column block and its whole K range,
+//   split over its waves and reduced through LDS. Needs no workspace.
+// streamk_kernel: a persistent grid of long-lived waves splits the linear
+//   sequence of units (problem, column block, group) -- contiguous in memory --
+//   evenly, so every wave streams one long contiguous run of weights. Column
+//   blocks cut between waves are combined through a caller-provided workspace:
+//   each wave writes its part, and the last to arrive (an atomic counter per
+//   block) sums the parts in wave order and stores the bf16 result, so the
+//   result does not depend on timing. The hand-off uses agent-scope atomics
+//   and explicit waits, not device-wide fences (see publish_part). Several problems (for example the four
+//   projections of a layer) can share one launch.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -42,6 +45,8 @@ struct Words {
   uint32_t w[WPL];
 };
 
+// One unit's packed words for this lane (WPL consecutive words), non-temporal:
+// every weight byte is read once.
 template <int WPL>
 __device__ __forceinline__ void load_words(Words<WPL>& out, const uint32_t* p) {
   if constexpr (WPL == 1) {
@@ -62,18 +67,54 @@ __device__ __forceinline__ void load_words(Words<WPL>& out, const uint32_t* p) {
   }
 }
 
+template <int WPL>
+__device__ __forceinline__ void load_words_g(Words<WPL>& out, gptr<const uint32_t> p) {
+  if constexpr (WPL == 1) {
+    out.w[0] = __builtin_nontemporal_load(p);
+  } else if constexpr (WPL == 2) {
+    u32x2 v = __builtin_nontemporal_load(reinterpret_cast<gptr<const u32x2>>(p));
+    out.w[0] = v[0];
+    out.w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < WPL / 4; ++h) {
+      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<gptr<const u32x4>>(p) + h);
+      out.w[4 * h + 0] = v[0];
+      out.w[4 * h + 1] = v[1];
+      out.w[4 * h + 2] = v[2];
+      out.w[4 * h + 3] = v[3];
+    }
+  }
+}
+
+// acc = sum over the group's WPL MFMA steps of a_t * q_t (exact codes).
+template <int WPL>
+__device__ __forceinline__ f32x4 group_product(const Words<WPL>& wq, const bf16x8 (&a)[WPL],
+                                               bf16x8 bias) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < WPL; ++t) {
+    const bf16x8 b = dequant_biased(wq.w[t]);
+    acc = mfma16(a[t], b, acc);
+    acc = mfma16(a[t], bias, acc);
+  }
+  return acc;
+}
+
+// ============================================================== split-K kernel
+
 template <int GS, int RB, int WAVES, int P>
-__global__ __launch_bounds__(64 * WAVES) void skinny_kernel(
+__global__ __launch_bounds__(64 * WAVES) void splitk_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ sp, uint16_t* __restrict__ y, int M, int N, int K) {
   constexpr int WPL = GS / 32;  // packed words per lane per group = MFMA steps per group
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c16 = lane & 15;  // B column / A row within the 16x16 tile
-  const int lg = lane >> 4;   // k-slice of each MFMA step
-  const int n0 = blockIdx.x * 16;
+  const int c16 = lane & 15;
+  const int lg = lane >> 4;
+  const int cb = blockIdx.x;
+  const int n0 = cb * 16;
   const int m0 = blockIdx.y * 16 * RB;
-  const int n = min(n0 + c16, N - 1);  // ragged column tile: clamp loads, mask stores
   const int G = K / GS;
   // This wave's groups [g0, g1); wave-uniform, so the loop runs on scalar branches.
   const int g0 = static_cast<int>(static_cast<long long>(G) * wave / WAVES);
@@ -86,24 +127,18 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(
 
   if (g1 > g0) {
     const int glast = g1 - 1;
-    const uint32_t* wp = qw + static_cast<size_t>(n) * (static_cast<size_t>(K) / 8) + lg * WPL;
-    const uint16_t* sn = sp + n;
-    // A rows of this lane. Rows past M read row M-1 instead: an MFMA output row
-    // depends only on its own A row, and padded rows are never stored.
+    const uint32_t* wp = qw + static_cast<size_t>(cb) * G * 64 * WPL + lane * WPL;
+    const uint16_t* sn = sp + static_cast<size_t>(cb) * G * 16 + c16;
     const uint16_t* xr[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int m = min(m0 + 16 * rb + c16, M - 1);
       xr[rb] = x + static_cast<size_t>(m) * K + lg * WPL * 8;
     }
-    // Loads past the wave's last group re-read that group (cache hits) so that
-    // every load is unconditional; their results are never used.
-    auto load_w = [&](Words<WPL>& o, uint16_t& s, int grp) {
-      grp = min(grp, glast);
-      load_words<WPL>(o, wp + static_cast<size_t>(grp) * (GS / 8));
-      s = sn[static_cast<size_t>(grp) * N];
-    };
-    auto load_x = [&](u32x4 (&xa)[RB][WPL], int grp) {
+    // Vector-memory loads retire in issue order, so a group's activations are
+    // issued together with its weights, P groups ahead. Loads past the wave's
+    // last group re-read it (cache hits), so every load is unconditional.
+    auto load_group = [&](Words<WPL>& o, uint16_t& s, u32x4 (&xa)[RB][WPL], int grp) {
       grp = min(grp, glast);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -111,40 +146,32 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(
         for (int t = 0; t < WPL; ++t)
           xa[rb][t] = *reinterpret_cast<const u32x4*>(xr[rb] + static_cast<size_t>(grp) * GS + 8 * t);
       }
+      load_words<WPL>(o, wp + static_cast<size_t>(grp) * 64 * WPL);
+      s = sn[static_cast<size_t>(grp) * 16];
     };
 
     Words<WPL> wq[P];
     uint16_t sq[P];
+    u32x4 xq[P][RB][WPL];
 #pragma unroll
-    for (int p = 0; p < P; ++p) load_w(wq[p], sq[p], g0 + p);
+    for (int p = 0; p < P; ++p) load_group(wq[p], sq[p], xq[p], g0 + p);
 
     for (int c = g0; c < g1; c += P) {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const int grp = c + p;
         if (grp < g1) {
-          u32x4 xa[RB][WPL];
-          load_x(xa, grp);
-          f32x4 acc[RB];
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < WPL; ++t) {
-            const bf16x8 b = dequant_biased(wq[p].w[t]);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              const bf16x8 a = act_frag(xa[rb][t]);
-              acc[rb] = mfma16(a, b, acc[rb]);
-              acc[rb] = mfma16(a, bias, acc[rb]);
-            }
-          }
           const float s = fp16_bits_to_f32(sq[p]);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
+            bf16x8 a[WPL];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[rb][r] = __builtin_fmaf(s, acc[rb][r], yacc[rb][r]);
+            for (int t = 0; t < WPL; ++t) a[t] = act_frag(xq[p][rb][t]);
+            const f32x4 acc = group_product<WPL>(wq[p], a, bias);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[rb][r] = __builtin_fmaf(s, acc[r], yacc[rb][r]);
           }
-          load_w(wq[p], sq[p], grp + P);
+          load_group(wq[p], sq[p], xq[p], grp + P);
         }
       }
     }
@@ -169,46 +196,417 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_kernel(
   }
 }
 
+// ============================================================= stream-K kernel
+
+// Wave w of NW owns units [U*w/NW, U*(w+1)/NW) of U.
+__device__ __forceinline__ long long wave_first_unit(int w, long long U, int NW) {
+  return U * w / NW;
+}
+
+// Owner of unit u: the largest w with floor(U*w/NW) <= u.
+__device__ __forceinline__ int unit_owner(long long u, long long U, int NW) {
+  return static_cast<int>(((u + 1) * NW - 1) / U);
+}
+
+// Cross-workgroup hand-off of a column block's parts, without device-wide
+// fences (on this chip a device-scope fence writes back and invalidates the
+// whole L2, which costs more than the GEMM itself). Instead every access that
+// crosses waves is an agent-scope atomic, coherent across the L2s of all
+// XCDs:
+//   writer: atomic stores of the part; wait until they complete (vmcnt 0);
+//           atomic increment of the block's counter.
+//   reader: the wave whose increment completes the count reads every part
+//           with atomic loads, issued only after the increment returned.
+// The writer's stores are complete, hence visible device-wide, before its
+// increment is issued; the reader's loads depend on its increment's result
+// and so happen after it. Compiler barriers keep the generated order.
+
+// Part of column block cb (of problem pr) that this wave (wg, whose run starts
+// at unit u0) computed: publish it and count it. Returns true when it was the
+// last part of the block to arrive; the caller then finalizes the block (after
+// its own stream, so the hot loop holds no inner loops). The parts of a block
+// come from the consecutive waves owning its first to last unit; a wave's slot
+// is 0 for the first block of its run and 1 for the last.
+__device__ __forceinline__ bool publish_part(const StreamKArgs& args, const StreamKProblem& pr,
+                                             int wg, long long u0, int cb, int lane, int lg,
+                                             int c16, int Mr, f32x4 yacc) {
+  const long long U = args.units;
+  const int NW = args.nwaves;
+  const long long ucb0 = pr.u_begin + static_cast<long long>(cb) * pr.G;
+  const int nseg = unit_owner(ucb0 + pr.G - 1, U, NW) - unit_owner(ucb0, U, NW) + 1;
+  const int slot = (u0 >= ucb0) ? 0 : 1;
+  float* mine = args.part + (static_cast<size_t>(wg) * 2 + slot) * Mr * 16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * lg + r;
+    if (m < Mr) __hip_atomic_store(mine + m * 16 + c16, yacc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_vmem_all();  // the part is complete before it is counted
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int old = 0;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(args.counters + pr.cb_begin + cb, 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = uniform(__shfl(old, 0)) == nseg - 1;
+  wait_vmem_all();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return last;
+}
+
+// Sum the parts of column block cb of problem pr in wave order, store the bf16
+// result and reset the block's counter for the next call.
+__device__ __forceinline__ void finalize_block(const StreamKArgs& args, const StreamKProblem& pr,
+                                               int cb, int lane, int lg, int c16, int M, int Mr) {
+  const long long U = args.units;
+  const int NW = args.nwaves;
+  const long long ucb0 = pr.u_begin + static_cast<long long>(cb) * pr.G;
+  const int wfirst = unit_owner(ucb0, U, NW);
+  const int wlast = unit_owner(ucb0 + pr.G - 1, U, NW);
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int w = wfirst; w <= wlast; ++w) {
+    const int ws = (wave_first_unit(w, U, NW) >= ucb0) ? 0 : 1;
+    float* part = args.part + (static_cast<size_t>(w) * 2 + ws) * Mr * 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (m < Mr) sum[r] += __hip_atomic_load(part + m * 16 + c16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const int n = cb * 16 + c16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * lg + r;
+    if (m < M && n < pr.N) to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(sum[r]);
+  }
+  if (lane == 0)
+    __hip_atomic_store(args.counters + pr.cb_begin + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int GS, int WAVES, int P, bool XLDS>
+__global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs args) {
+  constexpr int WPL = GS / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15;
+  const int lg = lane >> 4;
+  const int M = args.M;
+  const int Mr = min(M, 16);
+  const long long U = args.units;
+  const int NW = args.nwaves;
+  const int wg = blockIdx.x * WAVES + wave;  // waves wg >= NW of the last workgroup own nothing
+  const long long u0 = wg < NW ? wave_first_unit(wg, U, NW) : U;
+  const long long u1 = wg < NW ? wave_first_unit(wg + 1, U, NW) : U;
+
+  // Problem of a global unit (wave-uniform search over at most kMaxProblems).
+  auto problem_of = [&](long long u) {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i)
+      if (i < args.nprob && u >= args.prob[i].u_begin) p = i;
+    return p;
+  };
+
+  // Activations for the A operand. With XLDS the workgroup stages the x rows
+  // (M <= 16 rows, permuted into k-slot order) of every problem its units
+  // touch into LDS once; otherwise each lane reads them from global memory.
+  extern __shared__ uint32_t xlds[];
+  int lds_base[kMaxProblems];
+  int lds_stride[kMaxProblems];
+#pragma unroll
+  for (int i = 0; i < kMaxProblems; ++i) {
+    lds_base[i] = 0;
+    lds_stride[i] = 0;
+  }
+  if constexpr (XLDS) {
+    const long long wu0 = wave_first_unit(blockIdx.x * WAVES, U, NW);
+    const long long wu1 = wave_first_unit(min((blockIdx.x + 1) * WAVES, NW), U, NW);
+    int off = 0;  // in bf16 elements
+    if (wu1 > wu0) {
+      const int plo = problem_of(wu0), phi = problem_of(wu1 - 1);
+#pragma unroll
+      for (int i = 0; i < kMaxProblems; ++i) {
+        if (i >= plo && i <= phi) {
+          const StreamKProblem& pr = args.prob[i];
+          const int stride = pr.K + 8;  // 16 bytes of padding per row against bank conflicts
+          lds_base[i] = off;
+          lds_stride[i] = stride;
+          const int chunks = pr.K / 8;
+          for (int e = threadIdx.x; e < Mr * chunks; e += 64 * WAVES) {
+            const int row = e / chunks, c8 = e - row * chunks;
+            const u32x4 d = *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
+            *reinterpret_cast<bf16x8*>(xlds + (off + row * stride + 8 * c8) / 2) = act_frag(d);
+          }
+          off += Mr * stride;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (u1 <= u0) return;
+
+  const bf16x8 bias = bias_operand();
+  f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
+  // Blocks this wave must finalize (at most its first and last): problem, block.
+  int fin_p0 = -1, fin_cb0 = 0, fin_p1 = -1, fin_cb1 = 0;
+
+  // The wave's run, one problem at a time. Within a problem consecutive units
+  // are consecutive tiles, so the cursors are plain pointer increments.
+  for (long long u = u0; u < u1;) {
+    const int p = problem_of(u);
+    const StreamKProblem pr = args.prob[p];
+    const long long pend = pr.u_begin + static_cast<long long>(pr.NCB) * pr.G;
+    const long long uend = u1 < pend ? u1 : pend;
+    const int v0 = uniform(static_cast<int>(u - pr.u_begin));
+    const int v1 = uniform(static_cast<int>(uend - pr.u_begin));
+    const int G = uniform(pr.G);
+    const int xbase = XLDS ? (lds_base[p] + min(c16, M - 1) * lds_stride[p] + lg * WPL * 8) / 2 : 0;
+    const gptr<const uint16_t> xrow =
+        to_global(pr.x) + static_cast<size_t>(min(c16, M - 1)) * pr.K + lg * WPL * 8;
+    const gptr<const uint32_t> wbase = to_global(pr.qw) + lane * WPL;
+    const gptr<const uint16_t> sbase = to_global(pr.sp) + c16;
+    const gptr<uint16_t> yout = to_global(pr.y);
+
+    Words<WPL> rw[P];
+    uint16_t rs[P];
+    u32x4 rx[P][WPL];
+    // load cursor: next unit to load (stops at the last unit: later loads
+    // re-read it, cache hits, never used) and its group
+    int vl = v0;
+    int gl = uniform(v0 % G);
+    auto issue = [&](int slot) {
+      if constexpr (!XLDS) {
+#pragma unroll
+        for (int t = 0; t < WPL; ++t)
+          rx[slot][t] = *reinterpret_cast<gptr<const u32x4>>(xrow + static_cast<size_t>(gl) * GS + 8 * t);
+      }
+      load_words_g<WPL>(rw[slot], wbase + static_cast<size_t>(vl) * 64 * WPL);
+      rs[slot] = sbase[static_cast<size_t>(vl) * 16];
+      if (vl + 1 < v1) {
+        ++vl;
+        if (++gl == G) gl = 0;
+      }
+    };
+#pragma unroll
+    for (int sl = 0; sl < P; ++sl) issue(sl);
+
+    int cb = uniform(v0 / G);
+    int g = uniform(v0 - cb * G);
+    int seg_g0 = g;  // first group of the current column-block segment
+    for (int v = v0; v < v1; v += P) {
+#pragma unroll
+      for (int sl = 0; sl < P; ++sl) {
+        const int vv = v + sl;
+        if (vv < v1) {
+          bf16x8 a[WPL];
+          if constexpr (XLDS) {
+            const uint32_t* xl = xlds + xbase + (g * GS) / 2;
+#pragma unroll
+            for (int t = 0; t < WPL; ++t)
+              a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 4 * t));
+          } else {
+#pragma unroll
+            for (int t = 0; t < WPL; ++t) a[t] = act_frag(rx[sl][t]);
+          }
+          const f32x4 acc = group_product<WPL>(rw[sl], a, bias);
+          const float sc = fp16_bits_to_f32(rs[sl]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(sc, acc[r], yacc[r]);
+          issue(sl);
+
+          if (g == G - 1 || vv == v1 - 1) {
+            // End of this wave's segment of column block cb.
+            const int n = cb * 16 + c16;
+            if (seg_g0 == 0 && g == G - 1) {
+              // The whole column block was ours: store the result.
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int m = 4 * lg + r;
+                if (m < M && n < pr.N) yout[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(yacc[r]);
+              }
+              wait_vmem_all();
+            } else if (publish_part(args, pr, wg, u0, cb, lane, lg, c16, Mr, yacc)) {
+              if (fin_p0 < 0) {
+                fin_p0 = p;
+                fin_cb0 = cb;
+              } else {
+                fin_p1 = p;
+                fin_cb1 = cb;
+              }
+            }
+            yacc = f32x4{0.f, 0.f, 0.f, 0.f};
+            seg_g0 = 0;
+          }
+          if (++g == G) {
+            g = 0;
+            ++cb;
+          }
+        }
+      }
+    }
+    u = uend;
+  }
+  if (fin_p0 >= 0) finalize_block(args, args.prob[fin_p0], fin_cb0, lane, lg, c16, M, Mr);
+  if (fin_p1 >= 0) finalize_block(args, args.prob[fin_p1], fin_cb1, lane, lg, c16, M, Mr);
+}
+
+// =============================================================== launchers
+
 namespace {
 
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyPrefetch = 4;
+#ifndef W4A16_SKINNY_WAVES
+#define W4A16_SKINNY_WAVES 8
+#endif
+#ifndef W4A16_SKINNY_PREFETCH
+#define W4A16_SKINNY_PREFETCH 4
+#endif
+#ifndef W4A16_STREAMK_WAVES
+#define W4A16_STREAMK_WAVES 8
+#endif
+#ifndef W4A16_STREAMK_PREFETCH
+#define W4A16_STREAMK_PREFETCH 4
+#endif
+#ifndef W4A16_STREAMK_WG_PER_CU
+#define W4A16_STREAMK_WG_PER_CU 2
+#endif
+
+constexpr int kSplitWaves = W4A16_SKINNY_WAVES;  // waves per workgroup (split-K ways)
+// groups in flight per wave; fewer at larger row-block counts, whose
+// activation fragments take RB times the registers
+template <int RB>
+constexpr int split_prefetch() {
+  return RB == 1 ? W4A16_SKINNY_PREFETCH : (RB == 2 ? 2 : 1);
+}
 
 template <int GS, int RB>
-hipError_t launch_skinny_t(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_splitk_t(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 15) / 16, (a.M + 16 * RB - 1) / (16 * RB));
-  dim3 block(64 * kSkinnyWaves);
+  dim3 block(64 * kSplitWaves);
   const uint16_t* x = a.x;
   const uint32_t* qw = a.qweight;
   const uint16_t* sp = a.scales;
   uint16_t* y = a.y;
   int M = a.M, N = a.N, K = a.K;
-  void* args[] = {&x, &qw, &sp, &y, &M, &N, &K};
+  void* kargs[] = {&x, &qw, &sp, &y, &M, &N, &K};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&skinny_kernel<GS, RB, kSkinnyWaves, kSkinnyPrefetch>),
-      grid, block, args, 0, stream);
+      reinterpret_cast<const void*>(&splitk_kernel<GS, RB, kSplitWaves, split_prefetch<RB>()>),
+      grid, block, kargs, 0, stream);
 }
 
 template <int GS>
-hipError_t launch_skinny_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_skinny_t<GS, 1>(a, stream);
-  if (a.M <= 32) return launch_skinny_t<GS, 2>(a, stream);
-  return launch_skinny_t<GS, 4>(a, stream);
+hipError_t launch_splitk_g(const GemmArgs& a, hipStream_t stream) {
+  if (a.M <= 16) return launch_splitk_t<GS, 1>(a, stream);
+  if (a.M <= 32) return launch_splitk_t<GS, 2>(a, stream);
+  return launch_splitk_t<GS, 4>(a, stream);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+template <int GS, bool XLDS>
+hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(
+      &streamk_kernel<GS, W4A16_STREAMK_WAVES, W4A16_STREAMK_PREFETCH, XLDS>);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  StreamKArgs copy = sk;
+  void* kargs[] = {&copy};
+  return hipLaunchKernel(fn, dim3(wgs), dim3(64 * W4A16_STREAMK_WAVES), kargs, lds, stream);
+}
+
+template <bool XLDS>
+hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t lds, hipStream_t s) {
+  switch (group) {
+    case 32: return launch_streamk_t<32, XLDS>(sk, wgs, lds, s);
+    case 64: return launch_streamk_t<64, XLDS>(sk, wgs, lds, s);
+    case 128: return launch_streamk_t<128, XLDS>(sk, wgs, lds, s);
+    case 256: return launch_streamk_t<256, XLDS>(sk, wgs, lds, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
   switch (a.group) {
-    case 32: return launch_skinny_g<32>(a, stream);
-    case 64: return launch_skinny_g<64>(a, stream);
-    case 128: return launch_skinny_g<128>(a, stream);
-    case 256: return launch_skinny_g<256>(a, stream);
+    case 32: return launch_splitk_g<32>(a, stream);
+    case 64: return launch_splitk_g<64>(a, stream);
+    case 128: return launch_splitk_g<128>(a, stream);
+    case 256: return launch_splitk_g<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Until the large-M kernel lands, large M runs the skinny kernel with 64-row
+hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
+                          int* counters, hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems || M < 1 || M > 16) return hipErrorInvalidValue;
+  StreamKArgs sk = {};
+  long long units = 0;
+  int cbs = 0;
+  for (int i = 0; i < count; ++i) {
+    StreamKProblem p = probs[i];
+    p.G = p.K / group;
+    p.NCB = (p.N + 15) / 16;
+    p.u_begin = units;
+    p.cb_begin = cbs;
+    units += static_cast<long long>(p.NCB) * p.G;
+    cbs += p.NCB;
+    sk.prob[i] = p;
+  }
+  sk.nprob = count;
+  sk.M = M;
+  sk.units = units;
+  sk.part = part;
+  sk.counters = counters;
+  int wgs = device_cus() * W4A16_STREAMK_WG_PER_CU;
+  if (wgs * W4A16_STREAMK_WAVES > kStreamKMaxWaves) wgs = kStreamKMaxWaves / W4A16_STREAMK_WAVES;
+  // Every counted wave must own at least one unit (NW <= units): the parts of
+  // a column block are then produced by consecutive non-empty waves.
+  long long nw = static_cast<long long>(wgs) * W4A16_STREAMK_WAVES;
+  if (nw > units) nw = units;
+  wgs = static_cast<int>((nw + W4A16_STREAMK_WAVES - 1) / W4A16_STREAMK_WAVES);
+  sk.nwaves = static_cast<int>(nw);
+  // LDS for staged activations: the most any workgroup needs (Mr rows of K + 8
+  // of each problem its units touch). Beyond the budget, activations are read
+  // from global memory instead.
+  const int Mr = M < 16 ? M : 16;
+  long long need = 0;
+  for (int b = 0; b < wgs; ++b) {
+    const long long wb0 = static_cast<long long>(b) * W4A16_STREAMK_WAVES;
+    const long long wb1 = wb0 + W4A16_STREAMK_WAVES < nw ? wb0 + W4A16_STREAMK_WAVES : nw;
+    const long long wu0 = units * wb0 / nw;
+    const long long wu1 = units * wb1 / nw;
+    if (wu1 <= wu0) continue;
+    long long elems = 0;
+    for (int i = 0; i < count; ++i) {
+      const long long pb = sk.prob[i].u_begin;
+      const long long pe = pb + static_cast<long long>(sk.prob[i].NCB) * sk.prob[i].G;
+      if (pe > wu0 && pb < wu1) elems += static_cast<long long>(Mr) * (sk.prob[i].K + 8);
+    }
+    if (elems > need) need = elems;
+  }
+  const size_t lds = static_cast<size_t>(need) * 2;
+  if (lds <= kStreamKLdsBudget) return launch_streamk_x<true>(sk, group, wgs, lds, stream);
+  return launch_streamk_x<false>(sk, group, wgs, 0, stream);
+}
+
+// Until the large-M kernel lands, large M runs the split-K kernel with 64-row
 // tiles (grid.y covers M).
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream) { return launch_skinny(a, stream); }
 
