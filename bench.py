@@ -248,26 +248,83 @@ def check_parity(wl: Workload, layer: int, cols: int = 64):
 
 
 def cpu_baseline(seconds_target: float = 15.0):
-    """The oracle, as it stands, on the host cores: the decode layer set (M = 1)
-    one projection after another until about `seconds_target` of CPU work."""
+    """The oracle, as it stands, on the host cores: decode layer sets (M = 1),
+    projection after projection, layer after layer, until about
+    `seconds_target` seconds of CPU work; throughput in the metric's unit."""
     import synth
     import oracle
     threads = synth.default_threads()
-    done_bytes, t_total, parts = 0, 0.0, []
-    for pi, p in enumerate(synth.LAYER_PROJECTIONS):
-        x, q, s = synth.layer_inputs(0, pi, 1)
-        t0 = time.perf_counter()
-        oracle.gemm(x, q, s, GROUP, threads=threads)
-        dt = time.perf_counter() - t0
-        done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
-        t_total += dt
-        parts.append(p.name)
-        if t_total >= seconds_target:
-            break
+    done_bytes, t_total, count = 0, 0.0, 0
+    layer = 0
+    while t_total < seconds_target and layer < 64:
+        for pi, p in enumerate(synth.LAYER_PROJECTIONS):
+            x, q, s = synth.layer_inputs(layer, pi, 1)
+            t0 = time.perf_counter()
+            oracle.gemm(x, q, s, GROUP, threads=threads)
+            t_total += time.perf_counter() - t0
+            done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
+            count += 1
+        layer += 1
     return {"value": done_bytes / t_total / 1e12, "unit": "TB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"M=1 projections {'+'.join(parts)} of layer 0, group 128, fp64 oracle, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{count} projection GEMMs (decode layer sets M=1 of layers 0..{layer - 1}, "
+                      f"group {GROUP}), fp64 oracle, {t_total:.1f} s of CPU time"}
+
+
+COPY_BYTES = 512 << 20  # calibration kernels: 512 MiB written (fill), 512 MiB read (sum)
+
+
+def copy_calibration(reps: int = 3):
+    """Launch kernels of known traffic a few times -- a fill that writes
+    COPY_BYTES and a reduction that reads them -- so that a PMC run of this
+    script also measures what WRITE_SIZE / FETCH_SIZE report for them."""
+    import torch
+    buf = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        buf.fill_(1)
+        buf.sum()
+    torch.cuda.synchronize()
+
+
+def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel_substr: str, key: str):
+    """HBM bytes per launch of the kernel whose name contains `kernel_substr`,
+    from rocprofv3 --pmc counter collections of FETCH_SIZE and of WRITE_SIZE
+    (KiB per dispatch), each scaled by (known bytes / counter) of the
+    calibration copy in the same run. Writes profiles/traffic.json."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter, calib_substr):
+        vals, calib = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0
+                name = r.get("Kernel_Name", "")
+                if kernel_substr in name:
+                    vals.append(v)
+                elif calib_substr in name:
+                    calib.append(v)
+        return vals, calib
+
+    fv, fc = per_kernel(fetch_csv, "FETCH_SIZE", "reduce_kernel")   # the sum reads COPY_BYTES
+    wv, wc = per_kernel(write_csv, "WRITE_SIZE", "FillFunctor")     # the fill writes COPY_BYTES
+    f_scale = COPY_BYTES / statistics.median(fc) if fc else 1.0
+    w_scale = COPY_BYTES / statistics.median(wc) if wc else 1.0
+    fetch = statistics.median(fv) * f_scale
+    write = statistics.median(wv) * w_scale
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[key] = {"kernel_source_digest": kernel_source_digest(),
+                 "hbm_bytes_per_launch": fetch + write,
+                 "fetch_bytes": fetch, "write_bytes": write,
+                 "fetch_scale": f_scale, "write_scale": w_scale,
+                 "fetch_samples": len(fv), "write_samples": len(wv)}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    return data[key]
 
 
 def main(argv=None):
@@ -280,9 +337,19 @@ def main(argv=None):
                     help="replay the steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--m-list", default="1,16,1024")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain copy of known size (for PMC byte calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="compute profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--traffic-key", default="streamk_grouped|M=1")
+    ap.add_argument("--traffic-kernel", default="streamk_kernel")
     ap.add_argument("--separate", action="store_true",
                     help="four launches per step at every M (no grouped streaming launch)")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        print(json.dumps(traffic_from_pmc(args.traffic_from[0], args.traffic_from[1],
+                                          args.traffic_kernel, args.traffic_key), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the GEMM is not sharded across GPUs in this build)", file=sys.stderr)
@@ -364,6 +431,8 @@ def main(argv=None):
                      "kernel": dom_name},
         "extra": extra,
     }
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line))

@@ -283,6 +283,17 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
     __hip_atomic_store(args.counters + pr.cb_begin + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Loads of one unit for one lane: its packed words, the 32-bit word holding
+// its column's scale (with its neighbour column's, so the load is 32-bit:
+// 16-bit loads would be packed two to a register and tie their waits
+// together) and, without staged activations, its A-operand activations.
+template <int WPL>
+struct UnitLoads {
+  Words<WPL> w;
+  uint32_t s2;
+  u32x4 x[WPL];
+};
+
 template <int GS, int WAVES, int P, bool XLDS>
 __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs args) {
   constexpr int WPL = GS / 32;
@@ -307,8 +318,53 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     return p;
   };
 
+  // ---- per-problem stream state of the wave's current sub-run ----
+  struct Run {
+    int p, v0, v1, G;              // problem, its units [v0, v1), groups per column
+    gptr<const uint16_t> xrow;     // activations of this lane's A row
+    gptr<const uint32_t> wbase;    // this lane's words of unit 0
+    gptr<const uint32_t> sbase;    // this lane's scale pair of unit 0
+  };
+  auto make_run = [&](long long u) {
+    Run r;
+    r.p = problem_of(u);
+    const StreamKProblem& pr = args.prob[r.p];
+    const long long pend = pr.u_begin + static_cast<long long>(pr.NCB) * pr.G;
+    r.v0 = uniform(static_cast<int>(u - pr.u_begin));
+    r.v1 = uniform(static_cast<int>((u1 < pend ? u1 : pend) - pr.u_begin));
+    r.G = uniform(pr.G);
+    r.xrow = to_global(pr.x) + static_cast<size_t>(min(c16, M - 1)) * pr.K + lg * WPL * 8;
+    r.wbase = to_global(pr.qw) + lane * WPL;
+    r.sbase = reinterpret_cast<gptr<const uint32_t>>(to_global(pr.sp) + (c16 & ~1));
+    return r;
+  };
+  // Loads of unit v of the run (clamped to its last unit: loads past it re-read
+  // that unit, cache hits never used, so every load is unconditional).
+  auto load_unit = [&](UnitLoads<WPL>& d, const Run& r, int v) {
+    v = min(v, r.v1 - 1);
+    if constexpr (!XLDS) {
+      const int g = v % r.G;
+#pragma unroll
+      for (int t = 0; t < WPL; ++t)
+        d.x[t] = *reinterpret_cast<gptr<const u32x4>>(r.xrow + static_cast<size_t>(g) * GS + 8 * t);
+    }
+    load_words_g<WPL>(d.w, r.wbase + static_cast<size_t>(v) * 64 * WPL);
+    d.s2 = r.sbase[static_cast<size_t>(v) * 8];
+  };
+
+  UnitLoads<WPL> bufA[P], bufB[P];
+  Run run;
+  const bool active = u1 > u0;
+  if (active) {
+    // The first chunk's weights go out before the activation staging below,
+    // so the two latencies overlap.
+    run = make_run(u0);
+#pragma unroll
+    for (int i = 0; i < P; ++i) load_unit(bufA[i], run, run.v0 + i);
+  }
+
   // Activations for the A operand. With XLDS the workgroup stages the x rows
-  // (M <= 16 rows, permuted into k-slot order) of every problem its units
+  // (min(M,16) rows, permuted into k-slot order) of every problem its units
   // touch into LDS once; otherwise each lane reads them from global memory.
   extern __shared__ uint32_t xlds[];
   int lds_base[kMaxProblems];
@@ -334,17 +390,21 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
           const int chunks = pr.K / 8;
           for (int e = threadIdx.x; e < Mr * chunks; e += 64 * WAVES) {
             const int row = e / chunks, c8 = e - row * chunks;
-            const u32x4 d = *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
+            const u32x4 d =
+                *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
             *reinterpret_cast<bf16x8*>(xlds + (off + row * stride + 8 * c8) / 2) = act_frag(d);
           }
           off += Mr * stride;
         }
       }
     }
-    __syncthreads();
+    // LDS-only fences: the weight loads already in flight keep flying.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
 
-  if (u1 <= u0) return;
+  if (!active) return;
 
   const bf16x8 bias = bias_operand();
   f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
@@ -352,53 +412,26 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   int fin_p0 = -1, fin_cb0 = 0, fin_p1 = -1, fin_cb1 = 0;
 
   // The wave's run, one problem at a time. Within a problem consecutive units
-  // are consecutive tiles, so the cursors are plain pointer increments.
-  for (long long u = u0; u < u1;) {
-    const int p = problem_of(u);
-    const StreamKProblem pr = args.prob[p];
-    const long long pend = pr.u_begin + static_cast<long long>(pr.NCB) * pr.G;
-    const long long uend = u1 < pend ? u1 : pend;
-    const int v0 = uniform(static_cast<int>(u - pr.u_begin));
-    const int v1 = uniform(static_cast<int>(uend - pr.u_begin));
-    const int G = uniform(pr.G);
-    const int xbase = XLDS ? (lds_base[p] + min(c16, M - 1) * lds_stride[p] + lg * WPL * 8) / 2 : 0;
-    const gptr<const uint16_t> xrow =
-        to_global(pr.x) + static_cast<size_t>(min(c16, M - 1)) * pr.K + lg * WPL * 8;
-    const gptr<const uint32_t> wbase = to_global(pr.qw) + lane * WPL;
-    const gptr<const uint16_t> sbase = to_global(pr.sp) + c16;
+  // are consecutive tiles, so the cursors are plain offsets.
+  for (bool first = true;; first = false) {
+    if (!first) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) load_unit(bufA[i], run, run.v0 + i);
+    }
+    const StreamKProblem& pr = args.prob[run.p];
+    const int G = run.G;
+    const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
     const gptr<uint16_t> yout = to_global(pr.y);
-
-    Words<WPL> rw[P];
-    uint16_t rs[P];
-    u32x4 rx[P][WPL];
-    // load cursor: next unit to load (stops at the last unit: later loads
-    // re-read it, cache hits, never used) and its group
-    int vl = v0;
-    int gl = uniform(v0 % G);
-    auto issue = [&](int slot) {
-      if constexpr (!XLDS) {
-#pragma unroll
-        for (int t = 0; t < WPL; ++t)
-          rx[slot][t] = *reinterpret_cast<gptr<const u32x4>>(xrow + static_cast<size_t>(gl) * GS + 8 * t);
-      }
-      load_words_g<WPL>(rw[slot], wbase + static_cast<size_t>(vl) * 64 * WPL);
-      rs[slot] = sbase[static_cast<size_t>(vl) * 16];
-      if (vl + 1 < v1) {
-        ++vl;
-        if (++gl == G) gl = 0;
-      }
-    };
-#pragma unroll
-    for (int sl = 0; sl < P; ++sl) issue(sl);
-
-    int cb = uniform(v0 / G);
-    int g = uniform(v0 - cb * G);
+    int cb = uniform(run.v0 / G);
+    int g = uniform(run.v0 - cb * G);
     int seg_g0 = g;  // first group of the current column-block segment
-    for (int v = v0; v < v1; v += P) {
+
+    // Compute the units of one chunk (buf holds units v .. v+P-1).
+    auto compute_chunk = [&](UnitLoads<WPL> (&buf)[P], int v) {
 #pragma unroll
-      for (int sl = 0; sl < P; ++sl) {
-        const int vv = v + sl;
-        if (vv < v1) {
+      for (int i = 0; i < P; ++i) {
+        const int vv = v + i;
+        if (vv < run.v1) {
           bf16x8 a[WPL];
           if constexpr (XLDS) {
             const uint32_t* xl = xlds + xbase + (g * GS) / 2;
@@ -407,15 +440,15 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
               a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 4 * t));
           } else {
 #pragma unroll
-            for (int t = 0; t < WPL; ++t) a[t] = act_frag(rx[sl][t]);
+            for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
           }
-          const f32x4 acc = group_product<WPL>(rw[sl], a, bias);
-          const float sc = fp16_bits_to_f32(rs[sl]);
+          const f32x4 acc = group_product<WPL>(buf[i].w, a, bias);
+          const uint16_t sbits = static_cast<uint16_t>(buf[i].s2 >> (16 * (c16 & 1)));
+          const float sc = fp16_bits_to_f32(sbits);
 #pragma unroll
           for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(sc, acc[r], yacc[r]);
-          issue(sl);
 
-          if (g == G - 1 || vv == v1 - 1) {
+          if (g == G - 1 || vv == run.v1 - 1) {
             // End of this wave's segment of column block cb.
             const int n = cb * 16 + c16;
             if (seg_g0 == 0 && g == G - 1) {
@@ -428,10 +461,10 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
               wait_vmem_all();
             } else if (publish_part(args, pr, wg, u0, cb, lane, lg, c16, Mr, yacc)) {
               if (fin_p0 < 0) {
-                fin_p0 = p;
+                fin_p0 = run.p;
                 fin_cb0 = cb;
               } else {
-                fin_p1 = p;
+                fin_p1 = run.p;
                 fin_cb1 = cb;
               }
             }
@@ -444,8 +477,23 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
           }
         }
       }
+    };
+
+    // Double-buffered chunks: the next chunk's loads are issued before the
+    // current chunk is computed, so P to 2P units stay in flight.
+    for (int v = run.v0; v < run.v1; v += 2 * P) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) load_unit(bufB[i], run, v + P + i);
+      compute_chunk(bufA, v);
+      if (v + P >= run.v1) break;
+#pragma unroll
+      for (int i = 0; i < P; ++i) load_unit(bufA[i], run, v + 2 * P + i);
+      compute_chunk(bufB, v + P);
     }
-    u = uend;
+
+    const long long next = args.prob[run.p].u_begin + run.v1;
+    if (next >= u1) break;
+    run = make_run(next);
   }
   if (fin_p0 >= 0) finalize_block(args, args.prob[fin_p0], fin_cb0, lane, lg, c16, M, Mr);
   if (fin_p1 >= 0) finalize_block(args, args.prob[fin_p1], fin_cb1, lane, lg, c16, M, Mr);
