@@ -147,61 +147,61 @@ class Workload:
         return sum(flops(self.M, p.N, p.K) for p in self.store.projs)
 
 
-def run_steps(wl: Workload, lib, stream: int, first: int, count: int, events=None, dom=2):
+def run_steps(wl: Workload, lib, stream: int, first: int, count: int, only=None):
     """Launch `count` steps starting at step index `first`. Grouped steps are one
-    launch (all four projections); otherwise four. With `events`, an event pair
-    is recorded around the dominant launch of every step (the grouped launch,
-    or projection `dom`)."""
+    launch (all four projections); otherwise four. With `only`, each step
+    launches just projection `only` (to time the dominant launch by itself)."""
     L = len(wl.args)
     for s in range(first, first + count):
         if wl.grouped:
-            if events is not None:
-                events[s - first][0].record()
             rc = lib.w4a16_gemm_grouped(wl.problems[s % L][1], 4, wl.M, GROUP,
                                         wl.ws.data_ptr(), wl.ws_bytes, stream)
             if rc != 0:
                 raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
-            if events is not None:
-                events[s - first][1].record()
             continue
         la = wl.args[s % L]
         for pi, a in enumerate(la):
-            if events is not None and pi == dom:
-                events[s - first][0].record()
+            if only is not None and pi != only:
+                continue
             rc = lib.w4a16_gemm(*a, stream)
             if rc != 0:
                 raise RuntimeError(f"w4a16_gemm failed with status {rc}")
-            if events is not None and pi == dom:
-                events[s - first][1].record()
 
 
-def time_workload(wl: Workload, steps: int, warmup: int, use_graph: bool):
-    """(ms per step, mean dominant-launch duration in ms, steps timed)."""
+def timed(fn, stream_obj) -> float:
+    """Milliseconds between HIP events recorded on `stream_obj` around fn()."""
+    import torch
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream_obj)
+    fn()
+    t1.record(stream_obj)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def time_workload(wl: Workload, steps: int, warmup: int, use_graph: bool, dom: int = 2):
+    """(ms per step, mean dominant-launch duration in ms, steps timed).
+
+    The dominant launch (the grouped launch, or projection `dom` otherwise) is
+    timed by itself: `steps` back-to-back launches between two events on the
+    stream they are launched on, divided by `steps`."""
     import torch
 
     import w4a16_weight_only_gemm_amd as w4
     lib = w4._lib
-    stream = torch.cuda.current_stream().cuda_stream
+    cur = torch.cuda.current_stream()
+    stream = cur.cuda_stream
     L = len(wl.args)
 
-    # dominant-launch durations, from events around each of its launches
     run_steps(wl, lib, stream, 0, warmup)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    run_steps(wl, lib, stream, 0, steps, events=ev)
-    torch.cuda.synchronize()
-    dom_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-
-    # whole steps, back to back
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
+        s.wait_stream(cur)
         with torch.cuda.stream(s):
             run_steps(wl, lib, s.cuda_stream, 0, L)  # warm the capture stream
-        torch.cuda.current_stream().wait_stream(s)
+        cur.wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
             run_steps(wl, lib, torch.cuda.current_stream().cuda_stream, 0, L)
@@ -209,19 +209,19 @@ def time_workload(wl: Workload, steps: int, warmup: int, use_graph: bool):
             graph.replay()
         reps = max(1, steps // L)
         torch.cuda.synchronize()
-        t0.record()
-        for _ in range(reps):
-            graph.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (reps * L), dom_ms, reps * L
-    run_steps(wl, lib, stream, 0, warmup)
+
+        def replay():
+            for _ in range(reps):
+                graph.replay()
+        step_ms, nsteps = timed(replay, cur) / (reps * L), reps * L
+    else:
+        step_ms, nsteps = timed(lambda: run_steps(wl, lib, stream, 0, steps), cur) / steps, steps
+
+    only = None if wl.grouped else dom
+    run_steps(wl, lib, stream, 0, warmup, only=only)
     torch.cuda.synchronize()
-    t0.record()
-    run_steps(wl, lib, stream, 0, steps)
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, dom_ms, steps
+    dom_ms = timed(lambda: run_steps(wl, lib, stream, 0, steps, only=only), cur) / steps
+    return step_ms, dom_ms, nsteps
 
 
 def check_parity(wl: Workload, layer: int, cols: int = 64):
@@ -256,9 +256,9 @@ def cpu_baseline(seconds_target: float = 15.0):
     threads = synth.default_threads()
     done_bytes, t_total, count = 0, 0.0, 0
     layer = 0
-    while t_total < seconds_target and layer < 64:
+    while t_total < seconds_target:
         for pi, p in enumerate(synth.LAYER_PROJECTIONS):
-            x, q, s = synth.layer_inputs(layer, pi, 1)
+            x, q, s = synth.layer_inputs(layer % 64, pi, 1)
             t0 = time.perf_counter()
             oracle.gemm(x, q, s, GROUP, threads=threads)
             t_total += time.perf_counter() - t0
@@ -267,7 +267,7 @@ def cpu_baseline(seconds_target: float = 15.0):
         layer += 1
     return {"value": done_bytes / t_total / 1e12, "unit": "TB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{count} projection GEMMs (decode layer sets M=1 of layers 0..{layer - 1}, "
+            "sample": f"{count} projection GEMMs (decode layer sets M=1, {layer} layers), "
                       f"group {GROUP}), fp64 oracle, {t_total:.1f} s of CPU time"}
 
 
@@ -276,13 +276,14 @@ COPY_BYTES = 512 << 20  # calibration kernels: 512 MiB written (fill), 512 MiB r
 
 def copy_calibration(reps: int = 3):
     """Launch kernels of known traffic a few times -- a fill that writes
-    COPY_BYTES and a reduction that reads them -- so that a PMC run of this
-    script also measures what WRITE_SIZE / FETCH_SIZE report for them."""
+    COPY_BYTES and a float32 sum that reads them once (float32, so that no
+    widening copy comes first) -- so that a PMC run of this script also
+    measures what WRITE_SIZE / FETCH_SIZE report for them."""
     import torch
-    buf = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    buf = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     for _ in range(reps):
-        buf.fill_(1)
+        buf.fill_(1.0)
         buf.sum()
     torch.cuda.synchronize()
 
@@ -330,8 +331,8 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel_substr: str, key: st
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--graph", action="store_true",
                     help="replay the steps from a captured HIP graph (no host launch cost)")
