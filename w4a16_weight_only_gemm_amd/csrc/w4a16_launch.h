@@ -19,6 +19,8 @@ struct GemmArgs {
 // all pointers 16-byte aligned.
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream);
+// Group sizes the tiled large-M kernel handles (others fall back to split-K).
+bool large_supported(int group);
 
 // ---- stream-K (persistent, several problems per launch, M <= 16) ----
 constexpr int kMaxProblems = 8;

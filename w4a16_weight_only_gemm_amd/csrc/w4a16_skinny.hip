@@ -654,10 +654,6 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
   return launch_streamk_x<false>(sk, group, wgs, 0, stream);
 }
 
-// Until the large-M kernel lands, large M runs the split-K kernel with 64-row
-// tiles (grid.y covers M).
-hipError_t launch_large(const GemmArgs& a, hipStream_t stream) { return launch_skinny(a, stream); }
-
 int choose_path(int M, int N, int K, int group) {
   (void)N;
   (void)K;
