@@ -19,13 +19,16 @@
  * accumulation and a bf16 result rounded to nearest even.
  *
  * Packed format (the pages leave it open; this is the library's definition).
- *   Logical words: word j of output column n holds the codes of k = 8j..8j+7;
- *   the code of k = 8j+i sits in bits 4i..4i+3 as 4-bit two's complement
- *   (q & 0xF). Device arrangement (what w4a16_pack writes and the kernels
- *   read): columns in blocks of 16, the last block padded with zero codes and
- *   zero scales; blocks = ceil(N/16), G = K/group, wpl = group/32.
+ *   Words: word j of output column n holds the codes of k = 8j..8j+7 as
+ *   4-bit two's complement (q & 0xF); the code of k = 8j+i sits in nibble
+ *   (i/2) + 4*(i%2), i.e. bits 4*((i/2) + 4*(i%2)) .. +3: even k in nibbles
+ *   0..3, odd k in nibbles 4..7, so that nibbles v and v+4 become the two
+ *   bf16 halves of one operand register. Device arrangement (what w4a16_pack
+ *   writes and the kernels read): columns in blocks of 16, the last block
+ *   padded with zero codes and zero scales; blocks = ceil(N/16), G = K/group,
+ *   wpl = group/32.
  *   qweight : uint32 [blocks][G][64][wpl]. Tile (b, t) covers 16 columns x one
- *             group; its entry (l, w) is logical word t*(group/8) + (l/16)*wpl + w
+ *             group; its entry (l, w) is word t*(group/8) + (l/16)*wpl + w
  *             of column 16b + (l%16). A tile is exactly the MFMA B operands of
  *             its group for one wavefront, and a block's K range is contiguous.
  *   scales  : fp16 [blocks][G][16]; entry (b, t, c) = s[16b + c][t].

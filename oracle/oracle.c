@@ -31,6 +31,10 @@
  * is stored contiguously as 64 lanes of g/32 consecutive words: lane l holds,
  * for column 16b + (l mod 16), the g/32 logical words that start at word
  * t*(g/8) + (l div 16)*(g/32). Tiles are ordered block-major, then by group.
+ * Within a stored word the eight codes are interleaved: the code of
+ * k = 8j+i sits in nibble (i div 2) + 4 (i mod 2), so nibbles 0..3 hold the
+ * even k and nibbles 4..7 the odd k (nibbles v and v+4 are then codes 2v and
+ * 2v+1, the two 16-bit halves of one register after a shift and a mask).
  * Scales are stored as [block][group][16]: entry (b, t, c) = s[16b + c][t].
   */
 #include <math.h>
@@ -140,12 +144,15 @@ int oracle_gemm_f64(const uint16_t* x, const int8_t* q, const uint16_t* s, doubl
 
 /* ---- the packed format ---- */
 
-/* Logical word j of column n (n < N), from the codes q[n][8j .. 8j+7]. */
-static uint32_t oracle_logical_word(const int8_t* q, int K, int n, int j) {
+/* Nibble of the stored word that holds the code of k = 8j + i. */
+static int oracle_nibble(int i) { return i / 2 + 4 * (i % 2); }
+
+/* Stored word j of column n (n < N), from the codes q[n][8j .. 8j+7]. */
+static uint32_t oracle_stored_word(const int8_t* q, int K, int n, int j) {
   uint32_t word = 0;
   for (int i = 0; i < 8; ++i) {
     uint32_t code = (uint32_t)(q[(size_t)n * K + 8 * j + i] & 0xF);
-    word |= code << (4 * i);
+    word |= code << (4 * oracle_nibble(i));
   }
   return word;
 }
@@ -176,7 +183,7 @@ int oracle_pack(const int8_t* q, const uint16_t* s, uint32_t* qweight, uint16_t*
         for (int w = 0; w < wpl; ++w) {
           const int j = t * (group / 8) + (l / 16) * wpl + w;
           const size_t dst = (((size_t)b * G + t) * 64 + l) * wpl + w;
-          qweight[dst] = n < N ? oracle_logical_word(q, K, n, j) : 0u;
+          qweight[dst] = n < N ? oracle_stored_word(q, K, n, j) : 0u;
         }
       }
       for (int c = 0; c < 16; ++c) {
@@ -198,7 +205,7 @@ int oracle_unpack(const uint32_t* qweight, int8_t* q, int N, int K, int group) {
       const int l = (r / wpl) * 16 + c, w = r % wpl;
       const uint32_t word = qweight[(((size_t)b * G + t) * 64 + l) * wpl + w];
       for (int i = 0; i < 8; ++i) {
-        const int code = (int)((word >> (4 * i)) & 0xF);
+        const int code = (int)((word >> (4 * oracle_nibble(i))) & 0xF);
         q[(size_t)n * K + 8 * j + i] = (int8_t)((code ^ 8) - 8);
       }
     }

@@ -47,44 +47,48 @@ def fp16_to_f64(bits) -> np.ndarray:
 
 # ---------------------------------------------------------------- packing
 #
-# Device arrangement (oracle.c states it in full): logical word j of column n
-# holds the codes of k = 8j..8j+7 (code of k = 8j+i in bits 4i..4i+3, two's
-# complement); tiles of 16 columns x one group are stored lane-major, lane l
-# holding g/32 consecutive logical words of column 16b + l%16 starting at
-# word t*g/8 + (l//16)*g/32; scales are [block][group][16].
+# Device arrangement (oracle.c states it in full): word j of column n holds
+# the codes of k = 8j..8j+7 (two's complement), the code of k = 8j+i in nibble
+# (i // 2) + 4 (i % 2): even k in nibbles 0..3, odd k in nibbles 4..7; tiles of
+# 16 columns x one group are stored lane-major, lane l holding g/32 consecutive
+# words of column 16b + l%16 starting at word t*g/8 + (l//16)*g/32; scales are
+# [block][group][16].
 
-# (codes q[0..7] of one logical word, expected uint32), derived by hand: the
-# code of q[i] is q[i] & 0xF, placed at bits 4i..4i+3.
+# (codes q[0..7] of one word, expected uint32), derived by hand: with
+# c_i = q[i] & 0xF, the hex digits from the most significant down are
+# c7 c5 c3 c1 c6 c4 c2 c0.
 GOLDEN_WORDS = [
-    ([0, 1, 2, 3, 4, 5, 6, 7], 0x76543210),
+    ([0, 1, 2, 3, 4, 5, 6, 7], 0x75316420),
     ([-1] * 8, 0xFFFFFFFF),
     ([-8] * 8, 0x88888888),
-    ([7, -8, 0, 0, 0, 0, 0, 0], 0x00000087),
+    ([7, -8, 0, 0, 0, 0, 0, 0], 0x00080007),
     ([0, 0, 0, 0, 0, 0, 0, -1], 0xF0000000),
-    ([-8, -7, -6, -5, -4, -3, -2, -1], 0xFEDCBA98),
+    ([-8, -7, -6, -5, -4, -3, -2, -1], 0xFDB9ECA8),
     ([1, 0, 0, 0, 0, 0, 0, 0], 0x00000001),
+    ([0, 1, 0, 0, 0, 0, 0, 0], 0x00010000),
     ([0, 0, 0, 0, 0, 0, 0, 7], 0x70000000),
 ]
 
 
 def pin_golden_words(pack):
-    # N = 8 columns (one block, padded to 16), K = 32, group 32 (one word per
-    # lane, one group): lane l holds logical word l // 16 of column l % 16. The
-    # golden codes fill k = 0..7 of each column, so lanes 0..7 hold the golden
-    # words and every other lane (padding columns, or words 1..3) is zero.
-    q = np.zeros((8, 32), dtype=np.int8)
+    # N = 9 columns (one block, padded to 16), K = 32, group 32 (one word per
+    # lane, one group): lane l holds word l // 16 of column l % 16. The golden
+    # codes fill k = 0..7 of each column, so lanes 0..8 hold the golden words
+    # and every other lane (padding columns, or words 1..3) is zero.
+    n = len(GOLDEN_WORDS)
+    q = np.zeros((n, 32), dtype=np.int8)
     q[:, :8] = np.array([c for c, _ in GOLDEN_WORDS], dtype=np.int8)
-    qw, _ = pack(q, fp16_bits(np.ones((8, 1))), 32)
+    qw, _ = pack(q, fp16_bits(np.ones((n, 1))), 32)
     expect = np.zeros(64, dtype=np.uint32)
-    expect[:8] = [w for _, w in GOLDEN_WORDS]
+    expect[:n] = [w for _, w in GOLDEN_WORDS]
     assert np.array_equal(np.asarray(qw).ravel(), expect), [hex(v) for v in np.asarray(qw).ravel()]
-    # one column, codes 0..7 then eight -1: logical words 0x76543210, 0xFFFFFFFF,
-    # 0, 0 land in lanes 0, 16, 32, 48
+    # one column, codes 0..7 then eight -1: words 0x75316420, 0xFFFFFFFF, 0, 0
+    # land in lanes 0, 16, 32, 48
     q2 = np.zeros((1, 32), dtype=np.int8)
     q2[0, :16] = [0, 1, 2, 3, 4, 5, 6, 7] + [-1] * 8
     qw2 = np.asarray(pack(q2, fp16_bits([[1.0]]), 32)[0]).ravel()
     expect2 = np.zeros(64, dtype=np.uint32)
-    expect2[0], expect2[16] = 0x76543210, 0xFFFFFFFF
+    expect2[0], expect2[16] = 0x75316420, 0xFFFFFFFF
     assert np.array_equal(qw2, expect2), [hex(v) for v in qw2]
 
 
@@ -93,14 +97,15 @@ def pin_tile_positions(pack):
     (two words per lane, eight words per column per group, two groups)."""
     q = np.zeros((20, 128), dtype=np.int8)
     q[17, 100] = -3   # block 1, column 1; word 12 = group 1, word 4 of it -> lane 2*16+1 = 33,
-    #                   word 0 of the lane; index ((1*2+1)*64+33)*2 = 450; code 0xD at nibble 4
-    q[2, 7] = 5       # block 0, column 2; word 0, nibble 7 -> lane 2, index 4; 5 << 28
+    #                   word 0 of the lane; index ((1*2+1)*64+33)*2 = 450; k = 8*12 + 4, so
+    #                   i = 4 -> nibble 2: 0xD << 8
+    q[2, 7] = 5       # block 0, column 2; word 0, i = 7 -> nibble 7 -> lane 2, index 4; 5 << 28
     q[19, 127] = -8   # block 1, column 3; word 15 = group 1, word 7 -> lane 3*16+3 = 51,
-    #                   word 1 of the lane; index ((1*2+1)*64+51)*2+1 = 487; 0x8 << 28
+    #                   word 1 of the lane; index ((1*2+1)*64+51)*2+1 = 487; i = 7: 0x8 << 28
     qw = np.asarray(pack(q, fp16_bits(np.ones((20, 2))), 64)[0]).ravel()
     assert qw.size == 2 * 16 * 128 // 8
     expect = np.zeros(512, dtype=np.uint32)
-    expect[450], expect[4], expect[487] = 0x000D0000, 0x50000000, 0x80000000
+    expect[450], expect[4], expect[487] = 0x00000D00, 0x50000000, 0x80000000
     assert np.array_equal(qw, expect), [(i, hex(v)) for i, v in enumerate(qw) if v]
 
 
@@ -121,7 +126,7 @@ def pin_scale_layout(pack):
 
 def pin_pack_roundtrip(pack, unpack):
     rng = np.random.default_rng(7)
-    # every combination of four codes of a logical word (others random), both halves
+    # every combination of four codes of a word (others random), both halves
     combos = np.array(np.meshgrid(*[np.arange(-8, 8)] * 4, indexing="ij")).reshape(4, -1).T
     for half in range(2):
         N = combos.shape[0] // 64                   # 1024 columns, 64 combinations each

@@ -11,7 +11,7 @@ test in step; it runs no device code.
 """
 import pytest
 
-ROWS, BLOCKS, KT, THREADS, MB, NB, WN = 128, 16, 128, 512, 4, 4, 4
+ROWS, BLOCKS, KT, THREADS, MB, NB, WN = 128, 16, 128, 512, 8, 2, 8
 PIECES = KT // 8
 LOADS = ROWS * PIECES // THREADS
 ABYTES = ROWS * KT * 2
@@ -44,21 +44,29 @@ def check_shape(M, N, K, g):
     for mt in range(MT):
         for nt in range(NT):
             m0 = mt * ROWS
+            # staging through a buffer resource based at (row m0, k = 128 t) whose
+            # range ends at the end of x: in-range pieces lie inside x, and rows
+            # beyond M fall outside the range (read as zero)
+            records0 = (M - m0) * K * 2
+            assert 0 < records0 < 2 ** 32
             for t in range(ntiles):
+                base = m0 * K * 2 + t * KT * 2
+                records = records0 - t * KT * 2
+                assert records > 0
                 for tid in range(THREADS):
                     spiece, srow0 = tid % PIECES, tid // PIECES
-                    k = min(t * KT + spiece * 8, K - 8)
-                    assert k >= 0 and k % 8 == 0
                     for i in range(LOADS):
-                        row = min(m0 + srow0 + i * (THREADS // PIECES), M - 1)
-                        assert 0 <= (row * K + k) * 2 and (row * K + k) * 2 + 16 <= M * K * 2
                         lrow = srow0 + i * (THREADS // PIECES)
+                        voff = (lrow * K + spiece * 8) * 2
+                        if voff + 16 <= records:
+                            assert base + voff + 16 <= M * K * 2
+                        else:
+                            assert m0 + lrow >= M or t * KT + spiece * 8 >= K
                         sl = spiece ^ (lrow & 15)
                         assert lrow * KT * 2 + sl * 16 + 16 <= ABYTES
-                        if spiece % c["LPG"] == c["LPG"] - 1:
-                            assert (spiece // c["LPG"]) * ROWS + lrow < c["T"] * ROWS
+                        assert (spiece // c["LPG"]) * ROWS + lrow < c["T"] * ROWS
             for wave in range(8):
-                wm, wn = wave // WN, wave % WN
+                wn = wave
                 for lane in (0, 15, 16, 47, 63):
                     blks = [min(nt * BLOCKS + wn * NB + nb, NCB - 1) for nb in range(NB)]
                     for t in range(ntiles):
@@ -69,18 +77,18 @@ def check_shape(M, N, K, g):
                                 assert (tile * 64 + lane) * c["WPL"] + c["WPL"] <= NCB * 16 * K // 8
                                 assert tile * 16 + (lane & 14) + 2 <= NCB * 16 * G
                             for mb in range(MB):
-                                s0 = gi * ROWS + wm * MB * 16 + mb * 16 + 4 * (lane >> 4)
+                                s0 = gi * ROWS + mb * 16 + 4 * (lane >> 4)
                                 assert s0 % 4 == 0 and s0 + 4 <= c["T"] * ROWS
                         for st in range(4):
                             gi, w = st // c["WPL"], st % c["WPL"]
                             piece = gi * c["LPG"] + (lane >> 4) * c["WPL"] + w
                             assert piece < PIECES
                             for mb in range(MB):
-                                row = wm * MB * 16 + (lane & 15) + mb * 16
+                                row = (lane & 15) + mb * 16
                                 assert row * KT * 2 + (piece ^ (lane & 15)) * 16 + 16 <= ABYTES
             # stores of the tile (every lane)
             for wave in range(8):
-                wm, wn = wave // WN, wave % WN
+                wn = wave
                 for lane in range(64):
                     for nb in range(NB):
                         col = (nt * BLOCKS + wn * NB + nb) * 16 + (lane & 15)
@@ -88,7 +96,7 @@ def check_shape(M, N, K, g):
                             continue
                         for mb in range(MB):
                             for r in range(4):
-                                row = m0 + wm * MB * 16 + mb * 16 + 4 * (lane >> 4) + r
+                                row = m0 + mb * 16 + 4 * (lane >> 4) + r
                                 if row < M:
                                     key = (row, col)
                                     assert key not in stored

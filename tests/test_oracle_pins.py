@@ -146,6 +146,13 @@ def _pack_nibbles_reversed(q, s, g):
     return oracle.pack(q.reshape(q.shape[0], -1, 8)[:, :, ::-1].reshape(q.shape).copy(), s, g)
 
 
+def _pack_sequential_nibbles(q, s, g):
+    # code of k = 8j+i in nibble i (not interleaved): feed the oracle codes
+    # reordered so that its nibble (i // 2) + 4 (i % 2) receives q[8j + that nibble]
+    sigma = [i // 2 + 4 * (i % 2) for i in range(8)]
+    return oracle.pack(q.reshape(q.shape[0], -1, 8)[:, :, sigma].reshape(q.shape).copy(), s, g)
+
+
 def _pack_offset_binary(q, s, g):
     qw, sp = oracle.pack(q, s, g)
     return qw ^ np.uint32(0x88888888), sp
@@ -159,7 +166,7 @@ def _pack_scales_row_major(q, s, g):
 
 
 def _pack_untiled(q, s, g):
-    # logical words in plain [N][K/8] order (columns padded to 16), no lane tiling
+    # words in plain [N][K/8] order (columns padded to 16), no lane tiling
     qw, sp = oracle.pack(q, s, g)
     N, K = q.shape
     Np = oracle.blocks(N) * 16
@@ -176,8 +183,8 @@ def _unpack_offset_binary(qw, N, K, g):
     return oracle.unpack(qw ^ np.uint32(0x88888888), N, K, g)
 
 
-@pytest.mark.parametrize("mutant", [_pack_nibbles_reversed, _pack_offset_binary,
-                                    _pack_scales_row_major, _pack_untiled],
+@pytest.mark.parametrize("mutant", [_pack_nibbles_reversed, _pack_sequential_nibbles,
+                                    _pack_offset_binary, _pack_scales_row_major, _pack_untiled],
                          ids=lambda f: f.__name__)
 def test_planted_pack_mistake_is_caught(mutant):
     caught = _fails_some_pin([lambda: pins.pin_golden_words(mutant),

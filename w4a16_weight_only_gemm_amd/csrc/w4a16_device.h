@@ -1,6 +1,5 @@
 // w4a16_device.h -- device helpers shared by the gfx950 kernels: operand types,
-// in-register dequantization of packed int4 words, the matching permutation of
-// bf16 activation fragments, and number conversions.
+// in-register dequantization of packed int4 words, and number conversions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,16 +39,17 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // bf16 bit pattern of -136.0: sign 1, exponent 134 (2^7), fraction 8/128.
 constexpr uint32_t kBiasPair = 0xC308C308u;
 
-// Biased dequantization of one packed word (eight 4-bit two's-complement codes,
-// code i of k = 8j+i in bits 4i..4i+3). Output register v holds, as a bf16
-// pair, code v in its low half and code v+4 in its high half, each as the
-// exact value 136 + q: (c & 0xF) ^ 8 is the offset code q + 8 in 0..15, and
-// OR-ing it into the fraction of 0x4300 (128.0, whose unit in the last place
-// is 1) gives 128 + q + 8. One shift and one and-xor per register.
+// Biased dequantization of one packed word: eight 4-bit two's-complement
+// codes of k = 8j..8j+7, interleaved so that nibble v holds the code of
+// k = 8j+2v and nibble v+4 that of k = 8j+2v+1. Output register v holds, as a
+// bf16 pair, codes 2v (low half) and 2v+1 (high half), each as the exact
+// value 136 + q: (c & 0xF) ^ 8 is the offset code q + 8 in 0..15, and OR-ing
+// it into the fraction of 0x4300 (128.0, whose unit in the last place is 1)
+// gives 128 + q + 8. One shift and one and-xor per register.
 //
 // MFMA consumes the eight bf16 of a register quad as k-slots 0..7, so the
-// k-slot order of this operand is (0, 4, 1, 5, 2, 6, 3, 7) within the word;
-// the activation fragment must use the same order (act_frag below).
+// operand is in natural k order and pairs with eight consecutive bf16
+// activations loaded as they are stored.
 __device__ __forceinline__ bf16x8 dequant_biased(uint32_t w) {
   u32x4 r;
   r[0] = (w & 0x000F000Fu) ^ 0x43084308u;
@@ -59,18 +59,8 @@ __device__ __forceinline__ bf16x8 dequant_biased(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Eight consecutive bf16 activations x0..x7 (as four dwords, x0 in the low half
-// of d[0]) reordered into the k-slot order of dequant_biased:
-// (x0, x4), (x1, x5), (x2, x6), (x3, x7). v_perm_b32 selects bytes of
-// {src0 = bytes 4..7, src1 = bytes 0..3}.
-__device__ __forceinline__ bf16x8 act_frag(u32x4 d) {
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
-  return __builtin_bit_cast(bf16x8, r);
-}
+// Eight consecutive bf16 activations (four dwords) as an MFMA operand.
+__device__ __forceinline__ bf16x8 act_frag(u32x4 d) { return __builtin_bit_cast(bf16x8, d); }
 
 __device__ __forceinline__ bf16x8 bias_operand() {
   u32x4 r = {kBiasPair, kBiasPair, kBiasPair, kBiasPair};

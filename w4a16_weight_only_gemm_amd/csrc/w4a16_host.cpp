@@ -62,8 +62,11 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
           for (int w = 0; w < wpl; ++w) {
             uint32_t word = 0;
             if (n < static_cast<size_t>(N)) {
-              for (int i = 7; i >= 0; --i)
-                word = (word << 4) | (static_cast<uint32_t>(codes[8 * w + i]) & 0xFu);
+              // nibble v holds the code of k = 2v, nibble v + 4 that of k = 2v + 1
+              for (int v = 3; v >= 0; --v)
+                word = (word << 4) | (static_cast<uint32_t>(codes[8 * w + 2 * v + 1]) & 0xFu);
+              for (int v = 3; v >= 0; --v)
+                word = (word << 4) | (static_cast<uint32_t>(codes[8 * w + 2 * v]) & 0xFu);
             }
             out[(slice * 16 + col) * wpl + w] = word;
           }

@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   }
 
   // Activations for the A operand. With XLDS the workgroup stages the x rows
-  // (min(M,16) rows, permuted into k-slot order) of every problem its units
+  // (min(M,16) rows) of every problem its units
   // touch into LDS once; otherwise each lane reads them from global memory.
   extern __shared__ uint32_t xlds[];
   int lds_base[kMaxProblems];
