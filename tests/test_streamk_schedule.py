@@ -3,10 +3,11 @@ the invariants its correctness rests on, over many shapes and grid sizes:
 
 * the units (problem, column block, group) are split into contiguous,
   non-empty, disjoint runs, one per wave, covering everything exactly once;
-* every column block is either stored whole by one wave, or cut into parts by
+* every super-block (NBW consecutive column blocks: 1 with activations staged
+  in LDS, 4 otherwise) is either stored whole by one wave, or cut into parts by
   consecutive waves whose (wave, slot) partial buffers are distinct, and the
-  per-block counter reaches exactly the number of parts (so exactly one wave
-  finalizes it, and it finds every part);
+  per-super-block counter reaches exactly the number of parts (so exactly one
+  wave finalizes it, and it finds every part);
 * every weight, scale, activation, output, partial, counter and LDS index the
   kernel forms lies inside its buffer.
 
@@ -31,19 +32,29 @@ def owner(u, U, NW):
     return ((u + 1) * NW - 1) // U
 
 
-def plan(problems, M, group, cus=256, wg_per_cu=2):
-    """The launcher's grid: (problem table, units, NW, workgroups, lds bytes)."""
-    table, units, cbs = [], 0, 0
-    for (N, K) in problems:
-        G, NCB = K // group, (N + 15) // 16
-        table.append(dict(N=N, K=K, G=G, NCB=NCB, u_begin=units, cb_begin=cbs))
-        units += NCB * G
-        cbs += NCB
-    wgs = cus * wg_per_cu
-    if wgs * WAVES > MAX_WAVES:
-        wgs = MAX_WAVES // WAVES
-    nw = min(wgs * WAVES, units)
-    wgs = (nw + WAVES - 1) // WAVES
+WIDE = 4
+
+
+def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
+    """The launcher's grid: (problem table, units, NW, workgroups, lds bytes,
+    column blocks, nbw). With nbw None, the launcher's choice: 1 when the
+    activations fit the LDS budget, WIDE otherwise."""
+    def grid(nbw):
+        table, units, sbs, cbs = [], 0, 0, 0
+        for (N, K) in problems:
+            G, NCB = K // group, (N + 15) // 16
+            NSB = (NCB + nbw - 1) // nbw
+            table.append(dict(N=N, K=K, G=G, NCB=NCB, NSB=NSB, u_begin=units, sb_begin=sbs))
+            units += NSB * G
+            sbs += NSB
+            cbs += NCB
+        wgs = cus * wg_per_cu
+        if wgs * WAVES > MAX_WAVES:
+            wgs = MAX_WAVES // WAVES
+        nw = min(wgs * WAVES, units)
+        wgs = (nw + WAVES - 1) // WAVES
+        return table, units, nw, wgs, cbs
+    table, units, nw, wgs, cbs = grid(1)
     Mr = min(M, 16)
     need = 0
     for b in range(wgs):
@@ -52,9 +63,13 @@ def plan(problems, M, group, cus=256, wg_per_cu=2):
         if wu1 <= wu0:
             continue
         e = sum(Mr * (p["K"] + 8) for p in table
-                if p["u_begin"] + p["NCB"] * p["G"] > wu0 and p["u_begin"] < wu1)
+                if p["u_begin"] + p["NSB"] * p["G"] > wu0 and p["u_begin"] < wu1)
         need = max(need, e)
-    return table, units, nw, wgs, need * 2, cbs
+    if nbw is None:
+        nbw = 1 if need * 2 <= LDS_BUDGET else WIDE
+    if nbw != 1:
+        table, units, nw, wgs, cbs = grid(nbw)
+    return table, units, nw, wgs, need * 2, cbs, nbw
 
 
 def problem_of(table, u):
@@ -65,16 +80,18 @@ def problem_of(table, u):
     return p
 
 
-def simulate(problems, M, group, cus=256, wg_per_cu=2):
-    table, U, NW, wgs, lds, total_cbs = plan(problems, M, group, cus, wg_per_cu)
+def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
+    table, U, NW, wgs, lds, total_cbs, nbw = plan(problems, M, group, cus, wg_per_cu, nbw)
     Mr = min(M, 16)
     wpl = group // 32
-    xlds = lds <= LDS_BUDGET
+    xlds = nbw == 1 and lds <= LDS_BUDGET
+    total_sbs = sum(p["NSB"] for p in table)
+    assert total_sbs <= 8 + total_cbs          # counters the host reserves
     covered = {}
-    counters = [0] * total_cbs
-    finalized = [0] * total_cbs
+    counters = [0] * total_sbs
+    finalized = [0] * total_sbs
     part_writers = {}
-    stored_whole = [0] * total_cbs
+    stored_whole = [0] * total_sbs
     for b in range(wgs):
         # LDS staging of the workgroup (problems touched by its waves)
         if xlds:
@@ -101,44 +118,49 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2):
                 p = problem_of(table, u)
                 pr = table[p]
                 v = u - pr["u_begin"]
-                cb, g = v // pr["G"], v % pr["G"]
-                assert cb < pr["NCB"]
-                # weight / scale / activation / LDS indices of this unit
-                tile = cb * pr["G"] + g
-                assert (tile * 64 + 63) * wpl + wpl - 1 < pr["NCB"] * 16 * pr["K"] // 8
-                assert tile * 16 + 15 < pr["NCB"] * 16 * pr["G"]
+                sb, g = v // pr["G"], v % pr["G"]
+                assert sb < pr["NSB"]
+                # weight / scale / activation indices of this unit
+                for j in range(nbw):
+                    tile = min(sb * nbw + j, pr["NCB"] - 1) * pr["G"] + g
+                    assert (tile * 64 + 63) * wpl + wpl - 1 < pr["NCB"] * 16 * pr["K"] // 8
+                    assert tile * 16 + 15 < pr["NCB"] * 16 * pr["G"]
                 row = min(15, M - 1)
                 assert row * pr["K"] + g * group + 3 * wpl * 8 + 8 * (wpl - 1) + 7 < M * pr["K"]
                 if seg_g0 is None:
                     seg_g0 = g
                 if g == pr["G"] - 1 or u == u1 - 1:
-                    gcb = pr["cb_begin"] + cb
+                    gsb = pr["sb_begin"] + sb
                     if seg_g0 == 0 and g == pr["G"] - 1:
-                        stored_whole[gcb] += 1
+                        stored_whole[gsb] += 1
                     else:
-                        ucb0 = pr["u_begin"] + cb * pr["G"]
-                        wfirst, wlast = owner(ucb0, U, NW), owner(ucb0 + pr["G"] - 1, U, NW)
+                        usb0 = pr["u_begin"] + sb * pr["G"]
+                        wfirst, wlast = owner(usb0, U, NW), owner(usb0 + pr["G"] - 1, U, NW)
                         nseg = wlast - wfirst + 1
                         assert nseg >= 2
                         assert wfirst <= wg <= wlast
-                        slot = 0 if u0 >= ucb0 else 1
+                        slot = 0 if u0 >= usb0 else 1
                         key = (wg, slot)
                         assert key not in part_writers, key
-                        part_writers[key] = gcb
-                        assert (wg * 2 + slot + 1) * Mr * 16 <= MAX_WAVES * 2 * Mr * 16
-                        counters[gcb] += 1
-                        if counters[gcb] == nseg:
-                            finalized[gcb] += 1
+                        part_writers[key] = gsb
+                        # last float of this wave's part, against the workspace size
+                        assert ((wg * 2 + slot) * WIDE + nbw) * Mr * 16 <= MAX_WAVES * 2 * WIDE * Mr * 16
+                        counters[gsb] += 1
+                        if counters[gsb] == nseg:
+                            finalized[gsb] += 1
                             # the finalizer reads the part of every wave in [wfirst, wlast]
                             for w in range(wfirst, wlast + 1):
-                                ws = 0 if first_unit(w, U, NW) >= ucb0 else 1
-                                assert part_writers.get((w, ws)) == gcb, (w, ws, gcb)
+                                ws = 0 if first_unit(w, U, NW) >= usb0 else 1
+                                assert part_writers.get((w, ws)) == gsb, (w, ws, gsb)
                     seg_g0 = 0
     assert len(covered) == U and sorted(covered) == list(range(U))
-    for gcb in range(total_cbs):
-        assert stored_whole[gcb] + finalized[gcb] == 1, gcb
-        assert finalized[gcb] == 0 or counters[gcb] >= 2
-    return dict(U=U, NW=NW, wgs=wgs, lds=lds, xlds=xlds)
+    for gsb in range(total_sbs):
+        assert stored_whole[gsb] + finalized[gsb] == 1, gsb
+        assert finalized[gsb] == 0 or counters[gsb] >= 2
+    # every column block is in exactly one super-block
+    for pr in table:
+        assert pr["NSB"] * nbw >= pr["NCB"] > (pr["NSB"] - 1) * nbw
+    return dict(U=U, NW=NW, wgs=wgs, lds=lds, xlds=xlds, nbw=nbw)
 
 
 LAYER = [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]
@@ -149,7 +171,17 @@ def test_layer_set_grouped(M):
     info = simulate(LAYER, M, 128)
     assert info["NW"] == 4096
     if M == 1:
-        assert info["xlds"] and info["lds"] <= LDS_BUDGET
+        assert info["xlds"] and info["lds"] <= LDS_BUDGET and info["nbw"] == 1
+    if M == 16:
+        assert not info["xlds"] and info["nbw"] == WIDE
+
+
+@pytest.mark.parametrize("nbw", [1, WIDE])
+@pytest.mark.parametrize("case", [([(200, 384)], 16, 64), ([(33, 512)], 7, 128),
+                                  ([(100, 64), (300, 128), (17, 96)], 9, 32), (LAYER[:2], 16, 128)])
+def test_forced_block_widths(case, nbw):
+    problems, M, g = case
+    simulate(problems, M, g, nbw=nbw)
 
 
 @pytest.mark.parametrize("proj", LAYER)

@@ -204,7 +204,7 @@ size_t streamk_counter_bytes(long long total_columns) {
 
 size_t streamk_part_bytes(int M) {
   const int rows = M < 16 ? M : 16;
-  return static_cast<size_t>(kStreamKMaxWaves) * 2 * rows * 16 * sizeof(float);
+  return static_cast<size_t>(kStreamKMaxWaves) * 2 * kStreamKWideBlocks * rows * 16 * sizeof(float);
 }
 
 }  // namespace w4a16_internal

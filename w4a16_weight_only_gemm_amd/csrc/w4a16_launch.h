@@ -35,8 +35,9 @@ struct StreamKProblem {
   int N, K;
   // filled in by launch_streamk
   int G, NCB;               // groups per column, 16-column blocks
-  long long u_begin;        // first unit (column block, group) of this problem
-  int cb_begin;             // first column block (index of its counter)
+  int NSB;                  // super-blocks (NBW consecutive column blocks each)
+  long long u_begin;        // first unit (super-block, group) of this problem
+  int sb_begin;             // first super-block (index of its counter)
 };
 
 struct StreamKArgs {
@@ -45,9 +46,14 @@ struct StreamKArgs {
   int M;
   long long units;          // total units over all problems
   int nwaves;               // waves that own units (<= units)
-  float* part;              // [kStreamKMaxWaves][2][min(M,16)][16] fp32 parts
-  int* counters;            // one per column block, zero between calls
+  float* part;              // [kStreamKMaxWaves][2][NBW][min(M,16)][16] fp32 parts
+  int* counters;            // one per super-block, zero between calls
 };
+
+// Column blocks per stream-K unit: 1 when the activations are staged in LDS,
+// kStreamKWideBlocks when each wave reads them itself (then one activation
+// fragment serves that many weight tiles).
+constexpr int kStreamKWideBlocks = 4;
 
 // Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints,
 // rounded up to 256 bytes), then the parts.

@@ -221,32 +221,41 @@ __device__ __forceinline__ int unit_owner(long long u, long long U, int NW) {
 // increment is issued; the reader's loads depend on its increment's result
 // and so happen after it. Compiler barriers keep the generated order.
 
-// Part of column block cb (of problem pr) that this wave (wg, whose run starts
-// at unit u0) computed: publish it and count it. Returns true when it was the
-// last part of the block to arrive; the caller then finalizes the block (after
-// its own stream, so the hot loop holds no inner loops). The parts of a block
-// come from the consecutive waves owning its first to last unit; a wave's slot
-// is 0 for the first block of its run and 1 for the last.
+// Part of super-block sb (NBW column blocks of problem pr) that this wave
+// (wg, whose run starts at unit u0) computed: publish it and count it. Returns
+// true when it was the last part of the super-block to arrive; the caller then
+// finalizes it (after its own stream, so the hot loop holds no inner loops).
+// The parts of a super-block come from the consecutive waves owning its first
+// to last unit; a wave's slot is 0 for the first super-block of its run and 1
+// for the last.
+template <int NBW>
 __device__ __forceinline__ bool publish_part(const StreamKArgs& args, const StreamKProblem& pr,
-                                             int wg, long long u0, int cb, int lane, int lg,
-                                             int c16, int Mr, f32x4 yacc) {
+                                             int wg, long long u0, int sb, int lane, int lg,
+                                             int c16, int Mr, const f32x4 (&yacc)[NBW]) {
   const long long U = args.units;
   const int NW = args.nwaves;
-  const long long ucb0 = pr.u_begin + static_cast<long long>(cb) * pr.G;
-  const int nseg = unit_owner(ucb0 + pr.G - 1, U, NW) - unit_owner(ucb0, U, NW) + 1;
-  const int slot = (u0 >= ucb0) ? 0 : 1;
-  float* mine = args.part + (static_cast<size_t>(wg) * 2 + slot) * Mr * 16;
+  const long long usb0 = pr.u_begin + static_cast<long long>(sb) * pr.G;
+  const int nseg = unit_owner(usb0 + pr.G - 1, U, NW) - unit_owner(usb0, U, NW) + 1;
+  const int slot = (u0 >= usb0) ? 0 : 1;
+  float* mine = args.part + (static_cast<size_t>(wg) * 2 + slot) * NBW * Mr * 16;
+  // Rows at or past Mr are padding rows, computed from a repeat of row M - 1
+  // and so equal to row Mr - 1: storing them there (same value) keeps every
+  // store unconditional.
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * lg + r;
-    if (m < Mr) __hip_atomic_store(mine + m * 16 + c16, yacc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = min(4 * lg + r, Mr - 1);
+      __hip_atomic_store(mine + (j * Mr + m) * 16 + c16, yacc[j][r], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   wait_vmem_all();  // the part is complete before it is counted
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   int old = 0;
   if (lane == 0)
-    old = __hip_atomic_fetch_add(args.counters + pr.cb_begin + cb, 1, __ATOMIC_RELAXED,
+    old = __hip_atomic_fetch_add(args.counters + pr.sb_begin + sb, 1, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
   const bool last = uniform(__shfl(old, 0)) == nseg - 1;
   wait_vmem_all();
@@ -254,47 +263,68 @@ __device__ __forceinline__ bool publish_part(const StreamKArgs& args, const Stre
   return last;
 }
 
-// Sum the parts of column block cb of problem pr in wave order, store the bf16
-// result and reset the block's counter for the next call.
+// Sum the parts of super-block sb of problem pr in wave order, store the bf16
+// results of its column blocks and reset its counter for the next call.
+template <int NBW>
 __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const StreamKProblem& pr,
-                                               int cb, int lane, int lg, int c16, int M, int Mr) {
+                                               int sb, int lane, int lg, int c16, int M, int Mr) {
   const long long U = args.units;
   const int NW = args.nwaves;
-  const long long ucb0 = pr.u_begin + static_cast<long long>(cb) * pr.G;
-  const int wfirst = unit_owner(ucb0, U, NW);
-  const int wlast = unit_owner(ucb0 + pr.G - 1, U, NW);
-  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  const long long usb0 = pr.u_begin + static_cast<long long>(sb) * pr.G;
+  const int wfirst = unit_owner(usb0, U, NW);
+  const int wlast = unit_owner(usb0 + pr.G - 1, U, NW);
+  float sum[NBW][4];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
+  // Branch-free loads (padding rows read row Mr - 1 and are never stored), so
+  // a part's loads are all in flight together.
   for (int w = wfirst; w <= wlast; ++w) {
-    const int ws = (wave_first_unit(w, U, NW) >= ucb0) ? 0 : 1;
-    float* part = args.part + (static_cast<size_t>(w) * 2 + ws) * Mr * 16;
+    const int ws = (wave_first_unit(w, U, NW) >= usb0) ? 0 : 1;
+    float* part = args.part + (static_cast<size_t>(w) * 2 + ws) * NBW * Mr * 16;
+    float v[NBW][4];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = min(4 * lg + r, Mr - 1);
+        v[j][r] = __hip_atomic_load(part + (j * Mr + m) * 16 + c16, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[j][r] += v[j][r];
+  }
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int n = (sb * NBW + j) * 16 + c16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * lg + r;
-      if (m < Mr) sum[r] += __hip_atomic_load(part + m * 16 + c16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (m < M && n < pr.N)
+        to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(sum[j][r]);
     }
   }
-  const int n = cb * 16 + c16;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * lg + r;
-    if (m < M && n < pr.N) to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(sum[r]);
-  }
   if (lane == 0)
-    __hip_atomic_store(args.counters + pr.cb_begin + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(args.counters + pr.sb_begin + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads of one unit for one lane: its packed words, the 32-bit word holding
-// its column's scale (with its neighbour column's, so the load is 32-bit:
-// 16-bit loads would be packed two to a register and tie their waits
-// together) and, without staged activations, its A-operand activations.
-template <int WPL>
+// Loads of one unit for one lane: for each of its NBW column blocks the packed
+// words and the 32-bit word holding this lane's column scale (with its
+// neighbour column's, so the load is 32-bit: 16-bit loads would be packed two
+// to a register and tie their waits together) and, without staged
+// activations, its A-operand activations (shared by the NBW blocks).
+template <int WPL, int NBW>
 struct UnitLoads {
-  Words<WPL> w;
-  uint32_t s2;
+  Words<WPL> w[NBW];
+  uint32_t s2[NBW];
   u32x4 x[WPL];
 };
 
-template <int GS, int WAVES, int P, bool XLDS>
+template <int GS, int WAVES, int P, bool XLDS, int NBW>
 __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs args) {
   constexpr int WPL = GS / 32;
   const int lane = threadIdx.x & 63;
@@ -320,39 +350,49 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
 
   // ---- per-problem stream state of the wave's current sub-run ----
   struct Run {
-    int p, v0, v1, G;              // problem, its units [v0, v1), groups per column
+    int p, v0, v1, G, NCB;         // problem, its units [v0, v1), groups, column blocks
     gptr<const uint16_t> xrow;     // activations of this lane's A row
-    gptr<const uint32_t> wbase;    // this lane's words of unit 0
-    gptr<const uint32_t> sbase;    // this lane's scale pair of unit 0
+    gptr<const uint32_t> wbase;    // this lane's words of tile 0
+    gptr<const uint32_t> sbase;    // this lane's scale pair of tile 0
   };
   auto make_run = [&](long long u) {
     Run r;
     r.p = problem_of(u);
     const StreamKProblem& pr = args.prob[r.p];
-    const long long pend = pr.u_begin + static_cast<long long>(pr.NCB) * pr.G;
+    const long long pend = pr.u_begin + static_cast<long long>(pr.NSB) * pr.G;
     r.v0 = uniform(static_cast<int>(u - pr.u_begin));
     r.v1 = uniform(static_cast<int>((u1 < pend ? u1 : pend) - pr.u_begin));
     r.G = uniform(pr.G);
+    r.NCB = uniform(pr.NCB);
     r.xrow = to_global(pr.x) + static_cast<size_t>(min(c16, M - 1)) * pr.K + lg * WPL * 8;
     r.wbase = to_global(pr.qw) + lane * WPL;
     r.sbase = reinterpret_cast<gptr<const uint32_t>>(to_global(pr.sp) + (c16 & ~1));
     return r;
   };
   // Loads of unit v of the run (clamped to its last unit: loads past it re-read
-  // that unit, cache hits never used, so every load is unconditional).
-  auto load_unit = [&](UnitLoads<WPL>& d, const Run& r, int v) {
+  // that unit, cache hits never used, so every load is unconditional). Unit v
+  // is group v % G of super-block v / G; with NBW = 1 it is tile v itself.
+  auto load_unit = [&](UnitLoads<WPL, NBW>& d, const Run& r, int v) {
     v = min(v, r.v1 - 1);
+    const int sb = NBW == 1 ? 0 : uniform(v / r.G);
+    const int g = NBW == 1 ? 0 : v - sb * r.G;
     if constexpr (!XLDS) {
-      const int g = v % r.G;
+      const int gx = NBW == 1 ? v % r.G : g;
 #pragma unroll
       for (int t = 0; t < WPL; ++t)
-        d.x[t] = *reinterpret_cast<gptr<const u32x4>>(r.xrow + static_cast<size_t>(g) * GS + 8 * t);
+        d.x[t] = *reinterpret_cast<gptr<const u32x4>>(r.xrow + static_cast<size_t>(gx) * GS + 8 * t);
     }
-    load_words_g<WPL>(d.w, r.wbase + static_cast<size_t>(v) * 64 * WPL);
-    d.s2 = r.sbase[static_cast<size_t>(v) * 8];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      // tile of column block sb*NBW + j (blocks past the last re-read it)
+      const size_t tile = NBW == 1 ? static_cast<size_t>(v)
+                                   : static_cast<size_t>(min(sb * NBW + j, r.NCB - 1)) * r.G + g;
+      load_words_g<WPL>(d.w[j], r.wbase + tile * 64 * WPL);
+      d.s2[j] = r.sbase[tile * 8];
+    }
   };
 
-  UnitLoads<WPL> bufA[P], bufB[P];
+  UnitLoads<WPL, NBW> bufA[P], bufB[P];
   Run run;
   const bool active = u1 > u0;
   if (active) {
@@ -364,8 +404,8 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   }
 
   // Activations for the A operand. With XLDS the workgroup stages the x rows
-  // (min(M,16) rows) of every problem its units
-  // touch into LDS once; otherwise each lane reads them from global memory.
+  // (min(M,16) rows) of every problem its units touch into LDS once;
+  // otherwise each lane reads them from global memory.
   extern __shared__ uint32_t xlds[];
   int lds_base[kMaxProblems];
   int lds_stride[kMaxProblems];
@@ -392,7 +432,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
             const int row = e / chunks, c8 = e - row * chunks;
             const u32x4 d =
                 *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
-            *reinterpret_cast<bf16x8*>(xlds + (off + row * stride + 8 * c8) / 2) = act_frag(d);
+            *reinterpret_cast<u32x4*>(xlds + (off + row * stride + 8 * c8) / 2) = d;
           }
           off += Mr * stride;
         }
@@ -407,12 +447,14 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   if (!active) return;
 
   const bf16x8 bias = bias_operand();
-  f32x4 yacc = {0.f, 0.f, 0.f, 0.f};
-  // Blocks this wave must finalize (at most its first and last): problem, block.
-  int fin_p0 = -1, fin_cb0 = 0, fin_p1 = -1, fin_cb1 = 0;
+  f32x4 yacc[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Super-blocks this wave must finalize (at most its first and last).
+  int fin_p0 = -1, fin_sb0 = 0, fin_p1 = -1, fin_sb1 = 0;
 
   // The wave's run, one problem at a time. Within a problem consecutive units
-  // are consecutive tiles, so the cursors are plain offsets.
+  // are consecutive groups of a super-block, so the cursors are plain offsets.
   for (bool first = true;; first = false) {
     if (!first) {
 #pragma unroll
@@ -422,12 +464,12 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     const int G = run.G;
     const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
     const gptr<uint16_t> yout = to_global(pr.y);
-    int cb = uniform(run.v0 / G);
-    int g = uniform(run.v0 - cb * G);
-    int seg_g0 = g;  // first group of the current column-block segment
+    int sb = uniform(run.v0 / G);
+    int g = uniform(run.v0 - sb * G);
+    int seg_g0 = g;  // first group of the current super-block segment
 
     // Compute the units of one chunk (buf holds units v .. v+P-1).
-    auto compute_chunk = [&](UnitLoads<WPL> (&buf)[P], int v) {
+    auto compute_chunk = [&](UnitLoads<WPL, NBW> (&buf)[P], int v) {
 #pragma unroll
       for (int i = 0; i < P; ++i) {
         const int vv = v + i;
@@ -442,38 +484,58 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
 #pragma unroll
             for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
           }
-          const f32x4 acc = group_product<WPL>(buf[i].w, a, bias);
-          const uint16_t sbits = static_cast<uint16_t>(buf[i].s2 >> (16 * (c16 & 1)));
-          const float sc = fp16_bits_to_f32(sbits);
+          if constexpr (NBW == 1) {
+            const f32x4 acc = group_product<WPL>(buf[i].w[0], a, bias);
+            const float sc = fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[0] >> (16 * (c16 & 1))));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(sc, acc[r], yacc[r]);
+            for (int r = 0; r < 4; ++r) yacc[0][r] = __builtin_fmaf(sc, acc[r], yacc[0][r]);
+          } else {
+            // -136 * (row sums of the group) once, as the start of every block's sum
+            f32x4 accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+              f32x4 acc = accb;
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[j].w[t]), acc);
+              const float sc =
+                  fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[j] >> (16 * (c16 & 1))));
+#pragma unroll
+              for (int r = 0; r < 4; ++r) yacc[j][r] = __builtin_fmaf(sc, acc[r], yacc[j][r]);
+            }
+          }
 
           if (g == G - 1 || vv == run.v1 - 1) {
-            // End of this wave's segment of column block cb.
-            const int n = cb * 16 + c16;
+            // End of this wave's segment of super-block sb.
             if (seg_g0 == 0 && g == G - 1) {
-              // The whole column block was ours: store the result.
+              // The whole super-block was ours: store the results.
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int m = 4 * lg + r;
-                if (m < M && n < pr.N) yout[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(yacc[r]);
+              for (int j = 0; j < NBW; ++j) {
+                const int n = (sb * NBW + j) * 16 + c16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int m = 4 * lg + r;
+                  if (m < M && n < pr.N) yout[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(yacc[j][r]);
+                }
               }
               wait_vmem_all();
-            } else if (publish_part(args, pr, wg, u0, cb, lane, lg, c16, Mr, yacc)) {
+            } else if (publish_part<NBW>(args, pr, wg, u0, sb, lane, lg, c16, Mr, yacc)) {
               if (fin_p0 < 0) {
                 fin_p0 = run.p;
-                fin_cb0 = cb;
+                fin_sb0 = sb;
               } else {
                 fin_p1 = run.p;
-                fin_cb1 = cb;
+                fin_sb1 = sb;
               }
             }
-            yacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             seg_g0 = 0;
           }
           if (++g == G) {
             g = 0;
-            ++cb;
+            ++sb;
           }
         }
       }
@@ -495,8 +557,8 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     if (next >= u1) break;
     run = make_run(next);
   }
-  if (fin_p0 >= 0) finalize_block(args, args.prob[fin_p0], fin_cb0, lane, lg, c16, M, Mr);
-  if (fin_p1 >= 0) finalize_block(args, args.prob[fin_p1], fin_cb1, lane, lg, c16, M, Mr);
+  if (fin_p0 >= 0) finalize_block<NBW>(args, args.prob[fin_p0], fin_sb0, lane, lg, c16, M, Mr);
+  if (fin_p1 >= 0) finalize_block<NBW>(args, args.prob[fin_p1], fin_sb1, lane, lg, c16, M, Mr);
 }
 
 // =============================================================== launchers
@@ -564,10 +626,21 @@ int device_cus() {
   return cached[dev];
 }
 
-template <int GS, bool XLDS>
+#ifndef W4A16_STREAMK_WIDE_PREFETCH
+#define W4A16_STREAMK_WIDE_PREFETCH 1
+#endif
+
+// Units in flight per wave: a wide unit carries NBW weight tiles, so fewer of
+// them keep the same bytes in flight within the register budget.
+template <int NBW>
+constexpr int streamk_prefetch() {
+  return NBW == 1 ? W4A16_STREAMK_PREFETCH : W4A16_STREAMK_WIDE_PREFETCH;
+}
+
+template <int GS, bool XLDS, int NBW>
 hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(
-      &streamk_kernel<GS, W4A16_STREAMK_WAVES, W4A16_STREAMK_PREFETCH, XLDS>);
+      &streamk_kernel<GS, W4A16_STREAMK_WAVES, streamk_prefetch<NBW>(), XLDS, NBW>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -578,15 +651,42 @@ hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStrea
   return hipLaunchKernel(fn, dim3(wgs), dim3(64 * W4A16_STREAMK_WAVES), kargs, lds, stream);
 }
 
+// Activations staged in LDS: one column block per unit. Read by each wave:
+// kStreamKWideBlocks column blocks per unit.
 template <bool XLDS>
 hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t lds, hipStream_t s) {
+  constexpr int NBW = XLDS ? 1 : kStreamKWideBlocks;
   switch (group) {
-    case 32: return launch_streamk_t<32, XLDS>(sk, wgs, lds, s);
-    case 64: return launch_streamk_t<64, XLDS>(sk, wgs, lds, s);
-    case 128: return launch_streamk_t<128, XLDS>(sk, wgs, lds, s);
-    case 256: return launch_streamk_t<256, XLDS>(sk, wgs, lds, s);
+    case 32: return launch_streamk_t<32, XLDS, NBW>(sk, wgs, lds, s);
+    case 64: return launch_streamk_t<64, XLDS, NBW>(sk, wgs, lds, s);
+    case 128: return launch_streamk_t<128, XLDS, NBW>(sk, wgs, lds, s);
+    case 256: return launch_streamk_t<256, XLDS, NBW>(sk, wgs, lds, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Units of the problems with NBW column blocks per super-block, and the grid:
+// fills sk (units, nwaves, problem offsets) and returns the workgroup count.
+int plan_streamk(StreamKArgs& sk, int nbw) {
+  long long units = 0;
+  int sbs = 0;
+  for (int i = 0; i < sk.nprob; ++i) {
+    StreamKProblem& p = sk.prob[i];
+    p.NSB = (p.NCB + nbw - 1) / nbw;
+    p.u_begin = units;
+    p.sb_begin = sbs;
+    units += static_cast<long long>(p.NSB) * p.G;
+    sbs += p.NSB;
+  }
+  sk.units = units;
+  int wgs = device_cus() * W4A16_STREAMK_WG_PER_CU;
+  if (wgs * W4A16_STREAMK_WAVES > kStreamKMaxWaves) wgs = kStreamKMaxWaves / W4A16_STREAMK_WAVES;
+  // Every counted wave must own at least one unit (NW <= units): the parts of
+  // a super-block are then produced by consecutive non-empty waves.
+  long long nw = static_cast<long long>(wgs) * W4A16_STREAMK_WAVES;
+  if (nw > units) nw = units;
+  sk.nwaves = static_cast<int>(nw);
+  return static_cast<int>((nw + W4A16_STREAMK_WAVES - 1) / W4A16_STREAMK_WAVES);
 }
 
 }  // namespace
@@ -605,34 +705,23 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
                           int* counters, hipStream_t stream) {
   if (count < 1 || count > kMaxProblems || M < 1 || M > 16) return hipErrorInvalidValue;
   StreamKArgs sk = {};
-  long long units = 0;
-  int cbs = 0;
   for (int i = 0; i < count; ++i) {
     StreamKProblem p = probs[i];
     p.G = p.K / group;
     p.NCB = (p.N + 15) / 16;
-    p.u_begin = units;
-    p.cb_begin = cbs;
-    units += static_cast<long long>(p.NCB) * p.G;
-    cbs += p.NCB;
     sk.prob[i] = p;
   }
   sk.nprob = count;
   sk.M = M;
-  sk.units = units;
   sk.part = part;
   sk.counters = counters;
-  int wgs = device_cus() * W4A16_STREAMK_WG_PER_CU;
-  if (wgs * W4A16_STREAMK_WAVES > kStreamKMaxWaves) wgs = kStreamKMaxWaves / W4A16_STREAMK_WAVES;
-  // Every counted wave must own at least one unit (NW <= units): the parts of
-  // a column block are then produced by consecutive non-empty waves.
-  long long nw = static_cast<long long>(wgs) * W4A16_STREAMK_WAVES;
-  if (nw > units) nw = units;
-  wgs = static_cast<int>((nw + W4A16_STREAMK_WAVES - 1) / W4A16_STREAMK_WAVES);
-  sk.nwaves = static_cast<int>(nw);
-  // LDS for staged activations: the most any workgroup needs (Mr rows of K + 8
-  // of each problem its units touch). Beyond the budget, activations are read
-  // from global memory instead.
+  // LDS for staged activations (one column block per unit): the most any
+  // workgroup needs (Mr rows of K + 8 of each problem its units touch).
+  // Beyond the budget, each wave reads activations itself and takes
+  // kStreamKWideBlocks column blocks per unit instead.
+  int wgs = plan_streamk(sk, 1);
+  const long long units = sk.units;
+  const long long nw = sk.nwaves;
   const int Mr = M < 16 ? M : 16;
   long long need = 0;
   for (int b = 0; b < wgs; ++b) {
@@ -644,13 +733,14 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
     long long elems = 0;
     for (int i = 0; i < count; ++i) {
       const long long pb = sk.prob[i].u_begin;
-      const long long pe = pb + static_cast<long long>(sk.prob[i].NCB) * sk.prob[i].G;
+      const long long pe = pb + static_cast<long long>(sk.prob[i].NSB) * sk.prob[i].G;
       if (pe > wu0 && pb < wu1) elems += static_cast<long long>(Mr) * (sk.prob[i].K + 8);
     }
     if (elems > need) need = elems;
   }
   const size_t lds = static_cast<size_t>(need) * 2;
   if (lds <= kStreamKLdsBudget) return launch_streamk_x<true>(sk, group, wgs, lds, stream);
+  wgs = plan_streamk(sk, kStreamKWideBlocks);
   return launch_streamk_x<false>(sk, group, wgs, 0, stream);
 }
 
