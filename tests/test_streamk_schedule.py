@@ -35,10 +35,14 @@ def owner(u, U, NW):
 WIDE = 4
 
 
+WIDE_WG_PER_CU = 1
+
+
 def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     """The launcher's grid: (problem table, units, NW, workgroups, lds bytes,
     column blocks, nbw). With nbw None, the launcher's choice: 1 when the
-    activations fit the LDS budget, WIDE otherwise."""
+    activations fit the LDS budget, WIDE otherwise (with WIDE_WG_PER_CU
+    workgroups per compute unit)."""
     def grid(nbw):
         table, units, sbs, cbs = [], 0, 0, 0
         for (N, K) in problems:
@@ -48,7 +52,7 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
             units += NSB * G
             sbs += NSB
             cbs += NCB
-        wgs = cus * wg_per_cu
+        wgs = cus * (wg_per_cu if nbw == 1 else WIDE_WG_PER_CU)
         if wgs * WAVES > MAX_WAVES:
             wgs = MAX_WAVES // WAVES
         nw = min(wgs * WAVES, units)
@@ -169,7 +173,7 @@ LAYER = [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]
 @pytest.mark.parametrize("M", [1, 2, 16])
 def test_layer_set_grouped(M):
     info = simulate(LAYER, M, 128)
-    assert info["NW"] == 4096
+    assert info["NW"] == (4096 if info["nbw"] == 1 else 2048)
     if M == 1:
         assert info["xlds"] and info["lds"] <= LDS_BUDGET and info["nbw"] == 1
     if M == 16:

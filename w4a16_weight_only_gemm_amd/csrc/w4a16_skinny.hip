@@ -278,12 +278,12 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
   for (int j = 0; j < NBW; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
-  // Branch-free loads (padding rows read row Mr - 1 and are never stored), so
-  // a part's loads are all in flight together.
-  for (int w = wfirst; w <= wlast; ++w) {
+  // Branch-free loads (padding rows read row Mr - 1 and are never stored), two
+  // parts at a time, so their loads are all in flight together. The sum runs
+  // in wave order.
+  auto load_part = [&](float (&v)[NBW][4], int w) {
     const int ws = (wave_first_unit(w, U, NW) >= usb0) ? 0 : 1;
     float* part = args.part + (static_cast<size_t>(w) * 2 + ws) * NBW * Mr * 16;
-    float v[NBW][4];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
 #pragma unroll
@@ -293,10 +293,24 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
                                     __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  };
+  int w = wfirst;
+  for (; w + 1 <= wlast; w += 2) {
+    float v0[NBW][4], v1[NBW][4];
+    load_part(v0, w);
+    load_part(v1, w + 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sum[j][r] += v[j][r];
+      for (int r = 0; r < 4; ++r) sum[j][r] = (sum[j][r] + v0[j][r]) + v1[j][r];
+  }
+  if (w <= wlast) {
+    float v0[NBW][4];
+    load_part(v0, w);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[j][r] += v0[j][r];
   }
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -629,6 +643,9 @@ int device_cus() {
 #ifndef W4A16_STREAMK_WIDE_PREFETCH
 #define W4A16_STREAMK_WIDE_PREFETCH 1
 #endif
+#ifndef W4A16_STREAMK_WIDE_WG_PER_CU
+#define W4A16_STREAMK_WIDE_WG_PER_CU 1
+#endif
 
 // Units in flight per wave: a wide unit carries NBW weight tiles, so fewer of
 // them keep the same bytes in flight within the register budget.
@@ -679,7 +696,7 @@ int plan_streamk(StreamKArgs& sk, int nbw) {
     sbs += p.NSB;
   }
   sk.units = units;
-  int wgs = device_cus() * W4A16_STREAMK_WG_PER_CU;
+  int wgs = device_cus() * (nbw == 1 ? W4A16_STREAMK_WG_PER_CU : W4A16_STREAMK_WIDE_WG_PER_CU);
   if (wgs * W4A16_STREAMK_WAVES > kStreamKMaxWaves) wgs = kStreamKMaxWaves / W4A16_STREAMK_WAVES;
   // Every counted wave must own at least one unit (NW <= units): the parts of
   // a super-block are then produced by consecutive non-empty waves.
