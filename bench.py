@@ -49,6 +49,72 @@ def ceiling_tokens_per_s(bandwidth_gbs: float, bytes_per_token_gb: float) -> flo
     return bandwidth_gbs / bytes_per_token_gb
 
 
+# ---------------------------------------------------------------------------
+# Step-time model: the t_step(B) equation of the throughput page's "One weight
+# read, shared by every stream" section, with the per-stream terms of its
+# "What one more stream costs on this model" section. Units: bytes, seconds,
+# bytes/s, FLOP, FLOP/s.
+
+GIB = 1 << 30
+MIB = 1 << 20
+KIB = 1 << 10
+
+
+def kv_bytes_per_token(attn_layers: int, kv_heads: int, head_dim: int, elem_bytes: float) -> float:
+    """KV cache per token of context: K and V of every attention layer."""
+    return attn_layers * 2 * kv_heads * head_dim * elem_bytes
+
+
+def state_bytes(layers: int, heads: int, key_dim: int, value_dim: int, elem_bytes: float) -> float:
+    """Recurrent state of one stream: one key_dim x value_dim matrix per head per layer."""
+    return layers * heads * key_dim * value_dim * elem_bytes
+
+
+def step_time(B: float, W: float, BW: float, eta: float = 1.0, S: float = 0.0, kappa: float = 0.0,
+              L: float = 0.0, r: float = 1.0, F: float = 0.0, P: float = float("inf")) -> float:
+    """t_step(B) = max((W + B (2S + kappa L)) / (eta BW), B r F / P): the step
+    reads the weights once and each stream's state (read and written) and KV
+    cache, or is bound by the arithmetic of B r positions, whichever is longer."""
+    memory = (W + B * (2.0 * S + kappa * L)) / (eta * BW)
+    compute = B * r * F / P
+    return max(memory, compute)
+
+
+def aggregate_tokens_per_s(B: float, tau: float, t_step_s: float) -> float:
+    """Aggregate decode rate: B streams keep tau tokens each per step."""
+    return B * tau / t_step_s
+
+
+def per_stream_tokens_per_s(tau: float, t_step_s: float) -> float:
+    return tau / t_step_s
+
+
+def crossover_streams(W: float, BW: float, F: float, P: float, eta: float = 1.0, S: float = 0.0,
+                      kappa: float = 0.0, L: float = 0.0, r: float = 1.0) -> float:
+    """Stream count where the two terms of t_step meet (the bend):
+    (W + B a) / (eta BW) = B r F / P with a = 2S + kappa L."""
+    a = 2.0 * S + kappa * L
+    per_stream_compute = r * F / P
+    per_stream_memory = a / (eta * BW)
+    if per_stream_compute <= per_stream_memory:
+        return float("inf")
+    return (W / (eta * BW)) / (per_stream_compute - per_stream_memory)
+
+
+def fit_step_model(rows, step_s, W: float, per_row_bytes: float, flops_per_row: float,
+                   BW: float):
+    """Fit the two machine parameters of t_step to measured step times of a
+    GEMM sweep (rows[i] activation rows take step_s[i] seconds): eta is the
+    best bandwidth fraction seen on the memory line (W + rows * per_row_bytes
+    per step), P the best arithmetic rate seen (rows * flops_per_row per step).
+    Both are envelopes, so the fitted model never predicts a time below a
+    measured one. Returns (eta, P, bend rows)."""
+    eta = max((W + m * per_row_bytes) / (BW * t) for m, t in zip(rows, step_s))
+    P = max(m * flops_per_row / t for m, t in zip(rows, step_s))
+    bend = crossover_streams(W, BW, flops_per_row, P, eta=eta, S=per_row_bytes / 2.0)
+    return eta, P, bend
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_weight_only_gemm_amd", "csrc")
@@ -328,6 +394,91 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel_substr: str, key: st
     return data[key]
 
 
+SWEEP_ROWS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024)
+
+
+def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
+    """The full-step sweep: a stack of `layers` layer sets (64 by default, the
+    27B-class depth), each step one pass over every layer's four projections
+    at M rows; per-M step time, then the step-time model fitted to it."""
+    import torch
+
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    store = LayerStore(layers)
+    projs = store.projs
+    W = store.weight_bytes
+    per_row = layers * sum(2 * (p.K + p.N) for p in projs)          # x in, y out per row
+    flops_row = layers * sum(2 * p.K * p.N for p in projs)
+    cur = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    out = []
+    for M in rows:
+        # activations ~N(0, 1) in bf16, one set per layer and projection
+        xs = [[torch.randn((M, p.K), generator=gen, device="cuda").to(torch.bfloat16) for p in projs]
+              for _ in range(layers)]
+        ys = [[torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
+              for _ in range(layers)]
+        grouped = M <= 16
+        cols = sum(p.N for p in projs)
+        ws_bytes = w4.w4a16_workspace_bytes(M, cols)
+        ws = torch.zeros(max(1, ws_bytes // 4), dtype=torch.int32, device="cuda")
+        launches = []
+        for layer in range(layers):
+            entries = [(xs[layer][i], store.layers[layer][i][0], store.layers[layer][i][1],
+                        ys[layer][i], p.N, p.K) for i, p in enumerate(projs)]
+            if grouped:
+                arr = w4.make_problems(entries)
+                launches.append(("g", arr))
+            else:
+                launches.append(("s", [(e[0].data_ptr(), e[1].data_ptr(), e[2].data_ptr(),
+                                        e[3].data_ptr(), M, e[4], e[5], GROUP) for e in entries]))
+        import ctypes
+        stream = cur.cuda_stream
+
+        def one_pass():
+            for kind, a in launches:
+                if kind == "g":
+                    rc = lib.w4a16_gemm_grouped(ctypes.cast(a, ctypes.c_void_p).value, len(projs), M,
+                                                GROUP, ws.data_ptr(), ws_bytes, stream)
+                    if rc != 0:
+                        raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
+                else:
+                    for args in a:
+                        rc = lib.w4a16_gemm(*args, stream)
+                        if rc != 0:
+                            raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+
+        one_pass()
+        torch.cuda.synchronize()
+
+        def timed_passes():
+            for _ in range(passes):
+                one_pass()
+        ms = timed(timed_passes, cur) / passes
+        b = W + M * per_row
+        f = M * flops_row
+        row = {"M": M, "ms_per_step": ms, "tbps": b / (ms * 1e-3) / 1e12,
+               "tflops": f / (ms * 1e-3) / 1e12, "positions_per_s": M / (ms * 1e-3),
+               "hbm_frac": b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+               "mfma_frac": f / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+        out.append(row)
+        print(f"# sweep M={M}: {ms:.3f} ms/step, {row['tbps']:.2f} TB/s, {row['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del xs, ys, ws, launches
+        torch.cuda.empty_cache()
+    eta, P, bend = fit_step_model([r["M"] for r in out], [r["ms_per_step"] * 1e-3 for r in out],
+                                  W, per_row, flops_row, HBM_PEAK_GBS * 1e9)
+    return {"workload": f"{layers}-layer stack of the decode layer set (qkv, o, gate_up, down), group "
+                        f"{GROUP}; one step = every layer's four projections at M rows",
+            "weight_bytes": W, "rows": out,
+            "model": {"eta": eta, "P_tflops": P / 1e12, "bend_rows": bend,
+                      "bw_gbs": HBM_PEAK_GBS, "per_row_bytes": per_row, "flops_per_row": flops_row,
+                      "note": "t_step(M) = max((W + M a) / (eta BW), M F / P), eta and P the "
+                              "best fractions seen over the sweep"}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +497,11 @@ def main(argv=None):
     ap.add_argument("--traffic-kernel", default="streamk_kernel")
     ap.add_argument("--separate", action="store_true",
                     help="four launches per step at every M (no grouped streaming launch)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="full-step sweep over a layer stack at M = 1..1024 and the step-time "
+                         "model fitted to it (one JSON object), instead of the headline line")
+    ap.add_argument("--sweep-layers", type=int, default=64)
+    ap.add_argument("--sweep-passes", type=int, default=5)
     args = ap.parse_args(argv)
     if args.traffic_from:
         print(json.dumps(traffic_from_pmc(args.traffic_from[0], args.traffic_from[1],
@@ -362,6 +518,9 @@ def main(argv=None):
         return 2
     torch.cuda.set_device(0)
     import w4a16_weight_only_gemm_amd  # noqa: F401  (fails loudly without the library)
+    if args.sweep:
+        print(json.dumps(run_sweep(args.sweep_layers, args.sweep_passes)))
+        return 0
 
     t0 = time.time()
     store = LayerStore(args.layers)
