@@ -180,7 +180,7 @@ class Workload:
         import w4a16_weight_only_gemm_amd as w4
         self.M = M
         self.store = store
-        self.grouped = grouped and M <= 16
+        self.grouped = grouped
         self.x, self.y = [], []
         for layer in range(len(store.layers)):
             xs, ys = [], []
@@ -420,7 +420,7 @@ def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
               for _ in range(layers)]
         ys = [[torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
               for _ in range(layers)]
-        grouped = M <= 16
+        grouped = True
         cols = sum(p.N for p in projs)
         ws_bytes = w4.w4a16_workspace_bytes(M, cols)
         ws = torch.zeros(max(1, ws_bytes // 4), dtype=torch.int32, device="cuda")
@@ -471,7 +471,8 @@ def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
     eta, P, bend = fit_step_model([r["M"] for r in out], [r["ms_per_step"] * 1e-3 for r in out],
                                   W, per_row, flops_row, HBM_PEAK_GBS * 1e9)
     return {"workload": f"{layers}-layer stack of the decode layer set (qkv, o, gate_up, down), group "
-                        f"{GROUP}; one step = every layer's four projections at M rows",
+                        f"{GROUP}; one step = every layer's four projections at M rows, one grouped "
+                        f"launch per layer",
             "weight_bytes": W, "rows": out,
             "model": {"eta": eta, "P_tflops": P / 1e12, "bend_rows": bend,
                       "bw_gbs": HBM_PEAK_GBS, "per_row_bytes": per_row, "flops_per_row": flops_row,

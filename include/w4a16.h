@@ -114,11 +114,12 @@ int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* 
 /*
  * Workspace of the streaming entry points below, for M activation rows and
  * `total_columns` output columns (the sum of N over the problems of a call):
- * per-block counters followed by fp32 partial sums. Device memory owned by the
- * caller, 256-byte aligned, zero-filled once before its first use; every call
- * leaves the counters at zero again, so it is reused without clearing. One
- * workspace must not serve two calls that can run at the same time. Returns 0
- * for M < 0 or total_columns < 0.
+ * per-block (M <= 16) or per-tile (M > 16) counters followed by fp32 partial
+ * sums: 2 MB at M = 1, 34 MB at M = 16, up to 84 MB for M > 64. Device memory owned
+ * by the caller, 256-byte aligned, zero-filled once before its first use;
+ * every call leaves the counters at zero again, so it is reused without
+ * clearing. One workspace must not serve two calls that can run at the same
+ * time. Returns 0 for M < 0 or total_columns < 0.
  */
 size_t w4a16_workspace_bytes(int M, long long total_columns);
 
@@ -126,11 +127,14 @@ size_t w4a16_workspace_bytes(int M, long long total_columns);
  * As w4a16_gemm, using a workspace (see w4a16_workspace_bytes(M, N)). For
  * M <= 16 this runs the streaming kernel: a persistent grid whose waves split
  * the packed weights into equal contiguous runs, combining the column blocks
- * cut between waves through the workspace (deterministically: parts are summed
- * in a fixed order). Larger M runs the kernels of w4a16_gemm. Extra errors:
- * W4A16_ERR_INVALID_ARG for a null or too small workspace (checked only when
- * the streaming kernel runs), W4A16_ERR_MISALIGNED for a workspace that is not
- * 256-byte aligned.
+ * cut between waves through the workspace. For larger M (group 32, 64 or
+ * 128) a persistent grid of MFMA workgroups splits the (tile, k-tile) work
+ * evenly, combining the tiles cut between workgroups through the workspace.
+ * Both sum parts in a fixed order, so results are deterministic. Group 256 at
+ * M > 16 runs the kernels of w4a16_gemm and does not use the workspace.
+ * Extra errors: W4A16_ERR_INVALID_ARG for a null or too small workspace
+ * (checked only when a streaming kernel runs), W4A16_ERR_MISALIGNED for a
+ * workspace that is not 256-byte aligned.
  */
 int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
                   int K, int group, void* workspace, size_t workspace_bytes,
@@ -147,12 +151,13 @@ typedef struct w4a16_problem {
 } w4a16_problem;
 
 /*
- * Several GEMMs that share M and the group size, in one launch when M <= 16
- * (for example the four projections of one layer at a decode step: one weight
- * stream and one launch instead of four). `problems` is host memory read
- * during the call; count is 1..W4A16_MAX_PROBLEMS. The workspace is sized by
+ * Several GEMMs that share M and the group size, in one launch (for example
+ * the four projections of one layer: one weight stream and one launch instead
+ * of four). `problems` is host memory read during the call; count is
+ * 1..W4A16_MAX_PROBLEMS. The workspace is sized by
  * w4a16_workspace_bytes(M, sum of N). Each problem is validated as in
- * w4a16_gemm; for M > 16 the problems run one after another on `stream`.
+ * w4a16_gemm; with group 256 at M > 16 the problems run one after another on
+ * `stream` without the workspace.
  */
 #define W4A16_MAX_PROBLEMS 8
 int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int group,

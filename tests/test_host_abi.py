@@ -144,7 +144,11 @@ def test_workspace_sizes():
     a = w4.w4a16_workspace_bytes(1, 52224)
     b = w4.w4a16_workspace_bytes(16, 52224)
     assert 0 < a < b
-    assert w4.w4a16_workspace_bytes(16, 52224) == w4.w4a16_workspace_bytes(64, 52224)
+    # M > 16: per-tile counters and register-major parts of the MFMA tiles,
+    # growing with the tile height (32, 64, 128 rows)
+    c, d, e = (w4.w4a16_workspace_bytes(m, 52224) for m in (17, 64, 1024))
+    assert 0 < c < d < e
+    assert w4.w4a16_workspace_bytes(65, 52224) == w4.w4a16_workspace_bytes(128, 52224)
     assert w4.w4a16_workspace_bytes(0, 160) % 256 == 0
 
 

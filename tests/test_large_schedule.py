@@ -110,3 +110,105 @@ def check_shape(M, N, K, g):
 ])
 def test_shapes_in_bounds_and_covered(shape):
     check_shape(*shape)
+
+
+# ---------------------------------------------------------------- stream-K grid
+# Mirrors large_streamk_kernel and its launcher: units are (problem, tile,
+# k-tile), tiles row-tile fastest; workgroup w of NW owns units
+# [U*w/NW, U*(w+1)/NW); a tile cut between workgroups is published by each of
+# them into (workgroup, slot) and summed by the last to arrive.
+
+MAX_WG = 320
+MAXP = 8
+
+
+def sk_rows(M):
+    return 32 if M <= 32 else (64 if M <= 64 else 128)
+
+
+def sk_plan(problems, M, g, cus=256):
+    rows = sk_rows(M)
+    T = max(1, KT // g)
+    table, units, tiles = [], 0, 0
+    for (N, K) in problems:
+        G, NCB = K // g, (N + 15) // 16
+        MT, NT, KTL = (M + rows - 1) // rows, (NCB + 15) // 16, (G + T - 1) // T
+        table.append(dict(N=N, K=K, G=G, NCB=NCB, MT=MT, NT=NT, KT=KTL, u_begin=units,
+                          t_begin=tiles))
+        units += MT * NT * KTL
+        tiles += MT * NT
+    nw = min(cus, MAX_WG, units)
+    return table, units, nw, tiles, rows
+
+
+def sk_counter_ints(M, cols):
+    rows = sk_rows(M)
+    return ((M + rows - 1) // rows) * (MAXP + (cols + 255) // 256)
+
+
+def sk_simulate(problems, M, g, cus=256):
+    table, U, NW, tiles, rows = sk_plan(problems, M, g, cus)
+    regs = rows // 16 * 2 * 4
+    assert tiles <= sk_counter_ints(M, sum(N for N, _ in problems))
+    assert sorted(xcd_b for xcd_b in (tile_of(b, NW) for b in range(NW))) == list(range(NW))
+    first = lambda w: U * w // NW
+    owner = lambda u: ((u + 1) * NW - 1) // U
+    covered, counters, finals, stored, writers = set(), {}, {}, {}, {}
+    for w in range(NW):
+        u0, u1 = first(w), first(w + 1)
+        assert u1 > u0
+        u = u0
+        while u < u1:
+            p = max(i for i, t in enumerate(table) if u >= t["u_begin"])
+            pr = table[p]
+            v = u - pr["u_begin"]
+            tile, k0 = v // pr["KT"], v % pr["KT"]
+            assert tile < pr["MT"] * pr["NT"]
+            tu0 = pr["u_begin"] + tile * pr["KT"]
+            seg_end = min(tu0 + pr["KT"], u1)
+            k1 = k0 + (seg_end - u)
+            for uu in range(u, seg_end):
+                assert uu not in covered
+                covered.add(uu)
+            key = pr["t_begin"] + tile
+            if k0 == 0 and k1 == pr["KT"]:
+                stored[key] = stored.get(key, 0) + 1
+            else:
+                slot = 0 if u0 >= tu0 else 1
+                assert (w, slot) not in writers
+                writers[(w, slot)] = key
+                # last float of this wave's part region, wave 7, register regs-1, lane 63
+                last = (((w * 2 + slot) * 8 + 7) * regs + regs - 1) * 64 + 63
+                assert last < MAX_WG * 2 * 8 * regs * 64
+                nseg = owner(tu0 + pr["KT"] - 1) - owner(tu0) + 1
+                assert nseg >= 2 and owner(tu0) <= w <= owner(tu0 + pr["KT"] - 1)
+                counters[key] = counters.get(key, 0) + 1
+                if counters[key] == nseg:
+                    finals[key] = finals.get(key, 0) + 1
+                    for ww in range(owner(tu0), owner(tu0 + pr["KT"] - 1) + 1):
+                        s2 = 0 if first(ww) >= tu0 else 1
+                        assert writers.get((ww, s2)) == key
+            u = seg_end
+    assert covered == set(range(U))
+    for key in range(tiles):
+        assert stored.get(key, 0) + finals.get(key, 0) == 1, key
+    return dict(U=U, NW=NW, tiles=tiles, rows=rows)
+
+
+LAYER = [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]
+
+
+@pytest.mark.parametrize("M", [17, 32, 33, 64, 65, 128, 200, 256, 1024])
+def test_streamk_layer_set(M):
+    info = sk_simulate(LAYER, M, 128)
+    assert info["NW"] == 256
+
+
+@pytest.mark.parametrize("case", [
+    ([(272, 384)], 129, 128), ([(40, 96)], 200, 32), ([(4112, 192)], 300, 64), ([(16, 32)], 17, 32),
+    ([(512, 1152), (300, 640), (48, 128)], 70, 64), ([(5000, 4096)] * 8, 40, 128),
+])
+@pytest.mark.parametrize("cus", [1, 7, 80, 256, 400])
+def test_streamk_small_and_ragged(case, cus):
+    problems, M, g = case
+    sk_simulate(problems, M, g, cus)

@@ -36,6 +36,7 @@ WIDE = 4
 
 
 WIDE_WG_PER_CU = 1
+WIDE_MAX_WAVES = 4096
 
 
 def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
@@ -53,8 +54,9 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
             sbs += NSB
             cbs += NCB
         wgs = cus * (wg_per_cu if nbw == 1 else WIDE_WG_PER_CU)
-        if wgs * WAVES > MAX_WAVES:
-            wgs = MAX_WAVES // WAVES
+        max_waves = MAX_WAVES if nbw == 1 else WIDE_MAX_WAVES
+        if wgs * WAVES > max_waves:
+            wgs = max_waves // WAVES
         nw = min(wgs * WAVES, units)
         wgs = (nw + WAVES - 1) // WAVES
         return table, units, nw, wgs, cbs
@@ -148,7 +150,8 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                         assert key not in part_writers, key
                         part_writers[key] = gsb
                         # last float of this wave's part, against the workspace size
-                        assert ((wg * 2 + slot) * WIDE + nbw) * Mr * 16 <= MAX_WAVES * 2 * WIDE * Mr * 16
+                        part_floats = max(MAX_WAVES * 2, WIDE_MAX_WAVES * 2 * WIDE) * Mr * 16
+                        assert ((wg * 2 + slot) * nbw + nbw) * Mr * 16 <= part_floats
                         counters[gsb] += 1
                         if counters[gsb] == nseg:
                             finalized[gsb] += 1

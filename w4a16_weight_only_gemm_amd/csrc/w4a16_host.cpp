@@ -120,6 +120,9 @@ int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, 
 
 size_t w4a16_workspace_bytes(int M, long long total_columns) {
   if (M < 0 || total_columns < 0) return 0;
+  if (M > 16)
+    return w4a16_internal::large_streamk_counter_bytes(M, total_columns) +
+           w4a16_internal::large_streamk_part_bytes(M);
   return w4a16_internal::streamk_counter_bytes(total_columns) +
          w4a16_internal::streamk_part_bytes(M);
 }
@@ -140,8 +143,18 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
       return W4A16_ERR_MISALIGNED;
     columns += p.N;
   }
-  if (M > 16) {
-    // Large M: the per-problem kernels, one launch each.
+  w4a16_internal::StreamKProblem probs[W4A16_MAX_PROBLEMS] = {};
+  for (int i = 0; i < count; ++i) {
+    probs[i].x = static_cast<const uint16_t*>(problems[i].x);
+    probs[i].qw = static_cast<const uint32_t*>(problems[i].qweight);
+    probs[i].sp = static_cast<const uint16_t*>(problems[i].scales);
+    probs[i].y = static_cast<uint16_t*>(problems[i].y);
+    probs[i].N = problems[i].N;
+    probs[i].K = problems[i].K;
+  }
+  if (M > 16 && !w4a16_internal::large_streamk_fits(probs, count, M, group)) {
+    // Group 256 or 32-bit buffer ranges exceeded: the per-problem kernels,
+    // one launch each, no workspace.
     for (int i = 0; i < count; ++i) {
       const w4a16_problem& p = problems[i];
       const int rc = w4a16_gemm_ex(p.x, p.qweight, p.scales, p.y, M, p.N, p.K, group,
@@ -153,27 +166,23 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
   if (!workspace || workspace_bytes < w4a16_workspace_bytes(M, columns))
     return W4A16_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return W4A16_ERR_MISALIGNED;
-  w4a16_internal::StreamKProblem probs[W4A16_MAX_PROBLEMS] = {};
-  for (int i = 0; i < count; ++i) {
-    probs[i].x = static_cast<const uint16_t*>(problems[i].x);
-    probs[i].qw = static_cast<const uint32_t*>(problems[i].qweight);
-    probs[i].sp = static_cast<const uint16_t*>(problems[i].scales);
-    probs[i].y = static_cast<uint16_t*>(problems[i].y);
-    probs[i].N = problems[i].N;
-    probs[i].K = problems[i].K;
-  }
   char* ws = static_cast<char*>(workspace);
   int* counters = reinterpret_cast<int*>(ws);
-  float* part = reinterpret_cast<float*>(ws + w4a16_internal::streamk_counter_bytes(columns));
-  const hipError_t err =
-      w4a16_internal::launch_streamk(probs, count, M, group, part, counters, stream);
+  hipError_t err;
+  if (M > 16) {
+    float* part = reinterpret_cast<float*>(
+        ws + w4a16_internal::large_streamk_counter_bytes(M, columns));
+    err = w4a16_internal::launch_large_streamk(probs, count, M, group, part, counters, stream);
+  } else {
+    float* part = reinterpret_cast<float*>(ws + w4a16_internal::streamk_counter_bytes(columns));
+    err = w4a16_internal::launch_streamk(probs, count, M, group, part, counters, stream);
+  }
   return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
 int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
                   int K, int group, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
-  if (M > 16) return w4a16_gemm_ex(x, qweight, scales, y, M, N, K, group, W4A16_PATH_AUTO, stream);
   w4a16_problem p = {x, qweight, scales, y, N, K};
   if (M == 0) return W4A16_OK;
   if (!x || !qweight || !scales || !y) return W4A16_ERR_INVALID_ARG;
@@ -204,7 +213,10 @@ size_t streamk_counter_bytes(long long total_columns) {
 
 size_t streamk_part_bytes(int M) {
   const int rows = M < 16 ? M : 16;
-  return static_cast<size_t>(kStreamKMaxWaves) * 2 * kStreamKWideBlocks * rows * 16 * sizeof(float);
+  // the larger of the two layouts: narrow units (one block) or wide ones
+  const size_t narrow = static_cast<size_t>(kStreamKMaxWaves) * 2;
+  const size_t wide = static_cast<size_t>(kStreamKWideMaxWaves) * 2 * kStreamKWideBlocks;
+  return (narrow > wide ? narrow : wide) * rows * 16 * sizeof(float);
 }
 
 }  // namespace w4a16_internal

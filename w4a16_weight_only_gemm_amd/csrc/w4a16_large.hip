@@ -3,16 +3,16 @@
 // Past the point where the weight stream stops being the bottleneck, the
 // GEMM is bound by matrix arithmetic (ai.satyajit.si page, section "What one
 // more stream costs on this model": once the rows' arithmetic catches up with
-// the weight traffic, each extra row adds its full share of compute). This
-// kernel is therefore a tiled MFMA GEMM in which every operand byte is reused
-// as often as registers and LDS allow:
+// the weight traffic, each extra row adds its full share of compute). The
+// kernels here are therefore tiled MFMA GEMMs in which every operand byte is
+// reused as often as registers and LDS allow:
 //
-//  * A workgroup computes a 128 x 256 output tile with 8 waves side by side
-//    along N, each a 128 x 32 sub-tile: 8 x 2 blocks of
-//    v_mfma_f32_16x16x32_bf16. Every dequantized weight register feeds 8
-//    MFMAs, and no two waves dequantize the same weights.
-//  * K advances in tiles of 128. The workgroup stages the 128 x 128 bf16
-//    activation tile into LDS (double-buffered, one barrier per tile),
+//  * An output tile is R x 256 (R = 32, 64 or 128 rows) and belongs to one
+//    workgroup of 8 waves side by side along N, each an R x 32 sub-tile of
+//    (R/16) x 2 blocks of v_mfma_f32_16x16x32_bf16. Every dequantized weight
+//    register feeds R/16 MFMAs, and no two waves dequantize the same weights.
+//  * K advances in k-tiles of 128. The workgroup stages the R x 128 bf16
+//    activation tile into LDS (double-buffered, one barrier per k-tile),
 //    XOR-swizzled by row so that both the staging writes and the fragment
 //    reads are free of bank conflicts.
 //  * Packed weights go straight from the tiled format into registers: a
@@ -22,14 +22,24 @@
 //    kernels). Instead of a second MFMA against a -136 operand, the bias is
 //    removed by starting each group's accumulation from -136 * sum_k x[m][k]
 //    over the group: those row sums are formed once per workgroup while the
-//    activation tile is staged (8 values per lane, then a DPP reduction) and
+//    activation tile is staged (bf16 dot products, then a DPP reduction) and
 //    kept in LDS next to the tile. Every MFMA then does useful work.
 //  * The group's fp32 partial is scaled by its fp16 scale and added to the
 //    running fp32 result, as in the other kernels.
-//  * Workgroups are numbered so that the 8 XCDs (which take workgroups round
-//    robin) each own a contiguous range of tiles, row tiles fastest: the row
-//    tiles that share a column tile's weights run together on one XCD and
-//    find those weights in its L2.
+//
+// Two schedules share that tile engine:
+//  * large_kernel: one workgroup per 128 x 256 tile, the whole K range; needs
+//    no workspace. Workgroups are numbered so that the 8 XCDs (which take
+//    workgroups round robin) each own a contiguous range of tiles, row tiles
+//    fastest: the row tiles that share a column tile's weights run together
+//    on one XCD and find those weights in its L2.
+//  * large_streamk_kernel: a persistent grid splits the (problem, tile,
+//    k-tile) iterations of up to 8 problems evenly, so the machine stays full
+//    whatever the tile count (at M = 128 one layer has only about 200 tiles
+//    for 256 compute units). Tiles cut between workgroups are combined
+//    through a caller workspace: each workgroup publishes its part, and the
+//    last to arrive (an atomic counter per tile) sums the parts in workgroup
+//    order, so the result does not depend on timing.
 //
 // Group sizes 32, 64 and 128 are handled here (a k-tile holds 4, 2 or 1
 // whole groups). Rows beyond M read as zero (buffer range), column blocks
@@ -45,25 +55,28 @@ namespace w4a16_internal {
 namespace {
 
 constexpr int kLgWaves = 8;                   // all along N
-constexpr int kLgMB = 8;                      // 16-row blocks per wave (all 128 rows)
 constexpr int kLgNB = 2;                      // 16-column blocks per wave
-constexpr int kLgRows = kLgMB * 16;           // 128 rows per workgroup tile
 constexpr int kLgBlocks = kLgWaves * kLgNB;   // 16 column blocks = 256 columns
 constexpr int kLgThreads = kLgWaves * 64;
-constexpr int kLgKT = 128;                    // k per tile
-constexpr int kLgPieces = kLgKT / 8;          // 16-byte pieces per row per tile
-constexpr int kLgLoads = kLgRows * kLgPieces / kLgThreads;  // pieces staged per thread
+constexpr int kLgKT = 128;                    // k per k-tile
+constexpr int kLgPieces = kLgKT / 8;          // 16-byte pieces per row per k-tile
 constexpr int kLgRowBytes = kLgKT * 2;
-constexpr int kLgABytes = kLgRows * kLgRowBytes;            // 32 KB per buffer
+constexpr int kLgRowStep = kLgThreads / kLgPieces;  // 32 rows staged per pass
 
-template <int GS>
+// Tile geometry and LDS layout for group size GS and MB 16-row blocks.
+template <int GS, int MB>
 struct LgCfg {
+  static_assert(MB == 2 || MB == 4 || MB == 8, "32, 64 or 128 rows per tile");
+  static constexpr int Rows = MB * 16;
+  static constexpr int Loads = Rows * kLgPieces / kLgThreads;  // pieces staged per thread
+  static constexpr int ABytes = Rows * kLgRowBytes;
   static constexpr int T = kLgKT / GS;        // groups per k-tile
   static constexpr int WPL = GS / 32;         // MFMA steps (words per lane) per group
   static constexpr int LPG = GS / 8;          // staging lanes per group
-  static constexpr int SBytes = T * kLgRows * 4;
-  static constexpr int BufBytes = kLgABytes + SBytes;
+  static constexpr int SBytes = T * Rows * 4;
+  static constexpr int BufBytes = ABytes + SBytes;
   static constexpr size_t Lds = 2 * static_cast<size_t>(BufBytes);
+  static constexpr int Regs = MB * kLgNB * 4;  // accumulator floats per lane
 };
 
 template <int CTRL>
@@ -102,16 +115,6 @@ __device__ __forceinline__ float group_lane_sum(float v) {
   return v;
 }
 
-struct StageRegs {
-  u32x4 d[kLgLoads];
-};
-
-template <int GS>
-struct BRegs {
-  uint32_t w[kLgNB][LgCfg<GS>::T * LgCfg<GS>::WPL];  // 4 words per block per tile
-  uint32_t s[kLgNB][LgCfg<GS>::T];                   // scale pairs (fp16 x 2)
-};
-
 // Buffer resource over [base, base + bytes): loads at offsets at or beyond
 // `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -119,77 +122,111 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+template <int GS, int MB>
+struct StageRegs {
+  u32x4 d[LgCfg<GS, MB>::Loads];
+};
+
 template <int GS>
-__global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT, int NT) {
-  using C = LgCfg<GS>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lg_lds[];
+struct BRegs {
+  uint32_t w[kLgNB][kLgKT / 32];    // 4 words per block per k-tile
+  uint32_t s[kLgNB][kLgKT / GS];    // scale pairs (fp16 x 2) per group
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int wn = wave;
-  const int M = a.M, N = a.N, K = a.K;
-  const int G = K / GS;
-  const int NCB = (N + 15) / 16;
-  const int ntiles = (G + C::T - 1) / C::T;
+template <int MB>
+struct Acc {
+  f32x4 v[MB][kLgNB];
+};
 
-  // Tile of this workgroup: XCD x (= blockIdx % 8) owns a contiguous range of
-  // the MT * NT tiles, row tiles fastest.
-  const int total = MT * NT;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int tile = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int mt = tile % MT, nt = tile / MT;
-  const int m0 = mt * kLgRows;
-
-  // ---- activation staging: thread stages piece `spiece` (8 values) of rows
-  // srow0 + 32 i. Loads go through a buffer resource based at (row m0, k of
-  // the tile) and ending at the end of x, so rows beyond M read as zero. ----
-  const int spiece = tid % kLgPieces;
-  const int srow0 = tid / kLgPieces;
-  constexpr int kRowStep = kLgThreads / kLgPieces;   // 32
-  const uint32_t xbytes = static_cast<uint32_t>(M - m0) * static_cast<uint32_t>(K) * 2u;
-  const uint16_t* xrow0 = a.x + static_cast<size_t>(m0) * K;
-  uint32_t voff[kLgLoads];
+template <int MB>
+__device__ __forceinline__ void zero(Acc<MB>& a) {
 #pragma unroll
-  for (int i = 0; i < kLgLoads; ++i)
-    voff[i] = (static_cast<uint32_t>(srow0 + i * kRowStep) * K + spiece * 8) * 2u;
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kLgNB; ++nb) a.v[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
-  auto stage_load = [&](StageRegs& r, int t) {
+// LDS-only barrier: global loads in flight keep flying.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ------------------------------------------------------------------ tile engine
+//
+// One workgroup's view of one output tile: rows m0 .. m0 + Rows - 1, column
+// blocks 16 nt .. 16 nt + 15 (wave w owns blocks 16 nt + 2w, 16 nt + 2w + 1).
+// kloop() accumulates k-tiles [k0, k1) into acc; every wave of the workgroup
+// must call it with the same arguments (it holds workgroup barriers).
+template <int GS, int MB>
+struct TileEngine {
+  using C = LgCfg<GS, MB>;
+  unsigned char* lds;
+  int tid, lane, wave;
+  int M, N, K, G, NCB, m0, nt;
+  const uint16_t* xrow0;
+  uint32_t xbytes;
+  __amdgpu_buffer_rsrc_t rq, rs;
+  int blk[kLgNB];
+
+  __device__ __forceinline__ void setup(unsigned char* lds_, const uint16_t* x, const uint32_t* qw,
+                                        const uint16_t* sp, int M_, int N_, int K_, int m0_,
+                                        int nt_) {
+    lds = lds_;
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = uniform(tid >> 6);
+    M = M_;
+    N = N_;
+    K = K_;
+    G = K / GS;
+    NCB = (N + 15) / 16;
+    m0 = m0_;
+    nt = nt_;
+    xbytes = static_cast<uint32_t>(M - m0) * static_cast<uint32_t>(K) * 2u;
+    xrow0 = x + static_cast<size_t>(m0) * K;
+    rq = make_rsrc(qw, static_cast<uint32_t>(NCB) * 16u * static_cast<uint32_t>(K) / 2u);
+    rs = make_rsrc(sp, static_cast<uint32_t>(NCB) * 16u * static_cast<uint32_t>(G) * 2u);
+#pragma unroll
+    for (int nb = 0; nb < kLgNB; ++nb) {
+      const int b = nt * kLgBlocks + wave * kLgNB + nb;
+      blk[nb] = b < NCB ? b : NCB - 1;
+    }
+  }
+
+  // ---- activation staging: thread stages piece tid % 16 (8 values) of rows
+  // tid / 16 + 32 i, through a buffer resource based at (row m0, k of the
+  // k-tile) and ending at the end of x, so rows beyond M read as zero ----
+  __device__ __forceinline__ void stage_load(StageRegs<GS, MB>& r, int t) const {
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc(xrow0 + t * kLgKT, xbytes - static_cast<uint32_t>(t) * (kLgKT * 2));
+    const int spiece = tid % kLgPieces, srow0 = tid / kLgPieces;
 #pragma unroll
-    for (int i = 0; i < kLgLoads; ++i) r.d[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff[i], 0, 0);
-  };
-  auto stage_store = [&](const StageRegs& r, int buf) {
-    unsigned char* base = lg_lds + buf * C::BufBytes;
-    float* sums = reinterpret_cast<float*>(base + kLgABytes);
+    for (int i = 0; i < C::Loads; ++i) {
+      const uint32_t voff =
+          (static_cast<uint32_t>(srow0 + i * kLgRowStep) * K + spiece * 8) * 2u;
+      r.d[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void stage_store(const StageRegs<GS, MB>& r, int buf) const {
+    unsigned char* base = lds + buf * C::BufBytes;
+    float* sums = reinterpret_cast<float*>(base + C::ABytes);
+    const int spiece = tid % kLgPieces, srow0 = tid / kLgPieces;
 #pragma unroll
-    for (int i = 0; i < kLgLoads; ++i) {
-      const int row = srow0 + i * kRowStep;
+    for (int i = 0; i < C::Loads; ++i) {
+      const int row = srow0 + i * kLgRowStep;
       const float s = group_lane_sum<C::LPG>(neg136_sum8(r.d[i]));
-      sums[(spiece / C::LPG) * kLgRows + row] = s;  // every lane of the group: same value
+      sums[(spiece / C::LPG) * C::Rows + row] = s;  // every lane of the group: same value
       const int sl = spiece ^ (row & 15);
       *reinterpret_cast<u32x4*>(base + row * kLgRowBytes + sl * 16) = r.d[i];
     }
-  };
-
-  // ---- weights and scales of this wave's 4 column blocks: wave-uniform tile
-  // offsets, one lane offset ----
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(a.qweight, static_cast<uint32_t>(NCB) * 16u * static_cast<uint32_t>(K) / 2u);
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(a.scales, static_cast<uint32_t>(NCB) * 16u * static_cast<uint32_t>(G) * 2u);
-  const uint32_t qlane = static_cast<uint32_t>(lane) * C::WPL * 4u;
-  const uint32_t slane = static_cast<uint32_t>(lane & 14) * 2u;
-  int blk[kLgNB];
-#pragma unroll
-  for (int nb = 0; nb < kLgNB; ++nb) {
-    int b = nt * kLgBlocks + wn * kLgNB + nb;
-    blk[nb] = b < NCB ? b : NCB - 1;
   }
-  auto load_b = [&](BRegs<GS>& r, int t) {
+
+  // ---- this wave's weights and scales of k-tile t ----
+  __device__ __forceinline__ void load_b(BRegs<GS>& r, int t) const {
+    const uint32_t qlane = static_cast<uint32_t>(lane) * C::WPL * 4u;
+    const uint32_t slane = static_cast<uint32_t>(lane & 14) * 2u;
 #pragma unroll
     for (int gi = 0; gi < C::T; ++gi) {
       int grp = t * C::T + gi;
@@ -213,46 +250,39 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT
             __builtin_amdgcn_raw_buffer_load_b32(rs, slane, static_cast<int>(tile_idx * 32u), 0);
       }
     }
-  };
-
-  f32x4 yacc[kLgMB][kLgNB];
-#pragma unroll
-  for (int mb = 0; mb < kLgMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < kLgNB; ++nb) yacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int arow = lane & 15;                            // A fragment row (block 0)
-  const int jgrp = lane >> 4;                            // k-slice of the lane
-  const int shalf = (lane & 1) * 16;                     // scale half of the pair
+  }
 
   // One k-tile: 4 MFMA steps of 32 k. Step st belongs to group st / WPL of the
-  // tile; a group's accumulation starts from its -136 * row-sum tile and ends
-  // with the scaled add into yacc.
-  auto compute = [&](const BRegs<GS>& b, int t, int buf) {
-    const unsigned char* base = lg_lds + buf * C::BufBytes;
-    const float* sums = reinterpret_cast<const float*>(base + kLgABytes);
-    f32x4 acc[kLgNB][kLgMB];
-    f32x4 bias[kLgMB];
+  // k-tile; a group's accumulation starts from its -136 * row-sum tile and
+  // ends with the scaled add into acc_out.
+  __device__ __forceinline__ void compute(Acc<MB>& acc_out, const BRegs<GS>& b, int t,
+                                          int buf) const {
+    const unsigned char* base = lds + buf * C::BufBytes;
+    const float* sums = reinterpret_cast<const float*>(base + C::ABytes);
+    const int arow = lane & 15, jgrp = lane >> 4;
+    const int shalf = (lane & 1) * 16;
+    f32x4 acc[kLgNB][MB];
+    f32x4 bias[MB];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int gi = st / C::WPL, w = st % C::WPL;
-      if (C::T > 1 && t * C::T + gi >= G) break;  // ragged last tile (uniform)
+      if (C::T > 1 && t * C::T + gi >= G) break;  // ragged last k-tile (uniform)
       if (w == 0) {
 #pragma unroll
-        for (int mb = 0; mb < kLgMB; ++mb)
-          bias[mb] = *reinterpret_cast<const f32x4*>(sums + gi * kLgRows + mb * 16 + 4 * jgrp);
+        for (int mb = 0; mb < MB; ++mb)
+          bias[mb] = *reinterpret_cast<const f32x4*>(sums + gi * C::Rows + mb * 16 + 4 * jgrp);
       }
       const int piece = gi * C::LPG + jgrp * C::WPL + w;
-      bf16x8 af[kLgMB];
+      bf16x8 af[MB];
 #pragma unroll
-      for (int mb = 0; mb < kLgMB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const bf16x8*>(base + (arow + mb * 16) * kLgRowBytes +
                                                  ((piece ^ (lane & 15)) * 16));
 #pragma unroll
       for (int nb = 0; nb < kLgNB; ++nb) {
         const bf16x8 bq = dequant_biased(b.w[nb][st]);
 #pragma unroll
-        for (int mb = 0; mb < kLgMB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
           acc[nb][mb] = mfma16(af[mb], bq, w == 0 ? bias[mb] : acc[nb][mb]);
       }
       if (w == C::WPL - 1) {
@@ -260,62 +290,218 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT
         for (int nb = 0; nb < kLgNB; ++nb) {
           const float sc = fp16_bits_to_f32(static_cast<uint16_t>(b.s[nb][gi] >> shalf));
 #pragma unroll
-          for (int mb = 0; mb < kLgMB; ++mb) yacc[mb][nb] += sc * acc[nb][mb];
+          for (int mb = 0; mb < MB; ++mb) acc_out.v[mb][nb] += sc * acc[nb][mb];
         }
       }
     }
-  };
-
-  // ---- pipeline: tile t computes from LDS buffer t & 1 while tile t + 1 is
-  // loaded into registers and then staged into the other buffer. Weight
-  // registers alternate between two sets (no copies). ----
-  StageRegs sr;
-  BRegs<GS> b0, b1;
-  stage_load(sr, 0);
-  load_b(b0, 0);
-  stage_store(sr, 0);
-  __syncthreads();
-  auto iter = [&](int t, const BRegs<GS>& cur, BRegs<GS>& nxt) {
-    const int tn = t + 1 < ntiles ? t + 1 : t;   // the last iteration reloads (unused)
-    stage_load(sr, tn);
-    load_b(nxt, tn);
-    __builtin_amdgcn_sched_barrier(0);            // issue the loads before the math
-    compute(cur, t, t & 1);
-    stage_store(sr, (t + 1) & 1);
-    // LDS-only barrier: global loads of the next tile may stay in flight
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    iter(t, b0, b1);
-    if (t + 1 >= ntiles) break;
-    iter(t + 1, b1, b0);
   }
 
-  // ---- epilogue: bf16 (RNE) stores of the rows and columns that exist ----
-  gptr<uint16_t> yg = to_global(a.y);
+  // k-tiles [k0, k1): k-tile t computes from LDS buffer (t - k0) & 1 while
+  // k-tile t + 1 is loaded into registers and then staged into the other
+  // buffer. Weight registers alternate between two sets (no copies). Every
+  // k-tile ends with a workgroup barrier, so the LDS buffers are free on
+  // return.
+  __device__ __forceinline__ void kloop(Acc<MB>& acc, int k0, int k1) const {
+    StageRegs<GS, MB> sr;
+    BRegs<GS> b0, b1;
+    stage_load(sr, k0);
+    load_b(b0, k0);
+    stage_store(sr, 0);
+    lds_barrier();
+    auto iter = [&](int t, const BRegs<GS>& cur, BRegs<GS>& nxt) {
+      const int tn = t + 1 < k1 ? t + 1 : t;   // the last iteration reloads (unused)
+      const int buf = (t - k0) & 1;
+      stage_load(sr, tn);
+      load_b(nxt, tn);
+      __builtin_amdgcn_sched_barrier(0);       // issue the loads before the math
+      compute(acc, cur, t, buf);
+      stage_store(sr, buf ^ 1);
+      lds_barrier();
+    };
+    for (int t = k0; t < k1; t += 2) {
+      iter(t, b0, b1);
+      if (t + 1 >= k1) break;
+      iter(t + 1, b1, b0);
+    }
+  }
+
+  // bf16 (RNE) stores of the rows and columns that exist.
+  __device__ __forceinline__ void store(const Acc<MB>& acc, uint16_t* y) const {
+    gptr<uint16_t> yg = to_global(y);
+    const int jgrp = lane >> 4;
 #pragma unroll
-  for (int nb = 0; nb < kLgNB; ++nb) {
-    const int col = (nt * kLgBlocks + wn * kLgNB + nb) * 16 + (lane & 15);
-    if (col >= N) continue;
+    for (int nb = 0; nb < kLgNB; ++nb) {
+      const int col = (nt * kLgBlocks + wave * kLgNB + nb) * 16 + (lane & 15);
+      if (col >= N) continue;
 #pragma unroll
-    for (int mb = 0; mb < kLgMB; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + mb * 16 + 4 * jgrp + r;
-        if (row < M) yg[static_cast<size_t>(row) * N + col] = f32_to_bf16_bits(yacc[mb][nb][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + mb * 16 + 4 * jgrp + r;
+          if (row < M) yg[static_cast<size_t>(row) * N + col] = f32_to_bf16_bits(acc.v[mb][nb][r]);
+        }
       }
     }
   }
+};
+
+// Workgroup b of `total` in XCD-grouped order: XCD x (= b % 8) owns a
+// contiguous range of the indices.
+__device__ __forceinline__ int xcd_grouped(int b, int total) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
 }
+
+// =================================================== one workgroup per tile
+
+template <int GS>
+__global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT, int NT) {
+  constexpr int MB = 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lg_lds[];
+  const int tile = xcd_grouped(blockIdx.x, MT * NT);
+  const int mt = tile % MT, nt = tile / MT;
+  TileEngine<GS, MB> e;
+  e.setup(lg_lds, a.x, a.qweight, a.scales, a.M, a.N, a.K, mt * LgCfg<GS, MB>::Rows, nt);
+  Acc<MB> acc;
+  zero(acc);
+  const int kt = (e.G + LgCfg<GS, MB>::T - 1) / LgCfg<GS, MB>::T;
+  e.kloop(acc, 0, kt);
+  e.store(acc, a.y);
+}
+
+// ============================================================ stream-K grid
+
+// Workgroup w of NW owns units [U*w/NW, U*(w+1)/NW) of U.
+__device__ __forceinline__ long long lg_first_unit(int w, long long U, int NW) {
+  return U * w / NW;
+}
+// Owner of unit u: the largest w with floor(U*w/NW) <= u.
+__device__ __forceinline__ int lg_unit_owner(long long u, long long U, int NW) {
+  return static_cast<int>(((u + 1) * NW - 1) / U);
+}
+
+// Cross-workgroup hand-off of a tile's parts, without device-wide fences (a
+// device-scope fence writes back and invalidates the whole L2 of this chip):
+//   writer: every wave stores its part with agent-scope atomic stores and
+//           waits for them (vmcnt 0); after a workgroup barrier one lane
+//           increments the tile's counter (agent-scope atomic).
+//   reader: the workgroup whose increment completes the count reads every
+//           part with agent-scope atomic loads, issued only after the
+//           increment returned (its result is handed over through LDS).
+// A part is stored register-major (float r of lane l at r * 64 + l of the
+// wave's region), the layout every workgroup shares for a tile, so each
+// store and load instruction covers 256 contiguous bytes.
+template <int GS, int MB>
+__global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const LargeSKArgs args) {
+  using C = LgCfg<GS, MB>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lg_lds[];
+  __shared__ int last_flag;
+  const long long U = args.units;
+  const int NW = args.nwg;
+  const int wg = xcd_grouped(blockIdx.x, NW);
+  const long long u0 = lg_first_unit(wg, U, NW);
+  const long long u1 = lg_first_unit(wg + 1, U, NW);
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+
+  auto problem_of = [&](long long u) {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxProblems; ++i)
+      if (i < args.nprob && u >= args.prob[i].u_begin) p = i;
+    return p;
+  };
+  auto part_of = [&](int w, int slot) {
+    return args.part + ((static_cast<size_t>(w) * 2 + slot) * kLgWaves + wave) * C::Regs * 64;
+  };
+
+  TileEngine<GS, MB> e;
+  Acc<MB> acc;
+  int fin_p[2] = {-1, -1}, fin_tile[2] = {0, 0};
+  int nfin = 0;
+  for (long long u = u0; u < u1;) {
+    const int p = problem_of(u);
+    const LargeProblem& pr = args.prob[p];
+    const int v = uniform(static_cast<int>(u - pr.u_begin));
+    const int tile = uniform(v / pr.KT);
+    const int k0 = v - tile * pr.KT;
+    const long long tile_u0 = pr.u_begin + static_cast<long long>(tile) * pr.KT;
+    const long long seg_end = tile_u0 + pr.KT < u1 ? tile_u0 + pr.KT : u1;
+    const int k1 = k0 + static_cast<int>(seg_end - u);
+    e.setup(lg_lds, pr.x, pr.qw, pr.sp, args.M, pr.N, pr.K, (tile % pr.MT) * C::Rows,
+            tile / pr.MT);
+    zero(acc);
+    e.kloop(acc, k0, k1);
+    if (k0 == 0 && k1 == pr.KT) {
+      e.store(acc, pr.y);
+    } else {
+      // publish this workgroup's part of the tile and count it
+      const int slot = u0 >= tile_u0 ? 0 : 1;
+      float* mine = part_of(wg, slot);
+      const float* flat = reinterpret_cast<const float*>(&acc);
+#pragma unroll
+      for (int r = 0; r < C::Regs; ++r)
+        __hip_atomic_store(mine + r * 64 + lane, flat[r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      wait_vmem_all();  // this wave's part is complete
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();  // ... and so is every wave's
+      if (tid == 0) {
+        const int nseg =
+            lg_unit_owner(tile_u0 + pr.KT - 1, U, NW) - lg_unit_owner(tile_u0, U, NW) + 1;
+        const int old = __hip_atomic_fetch_add(args.counters + pr.t_begin + tile, 1,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = old == nseg - 1;
+      }
+      lds_barrier();
+      if (last_flag) {
+        fin_p[nfin] = p;
+        fin_tile[nfin] = tile;
+        ++nfin;
+      }
+      lds_barrier();  // the flag is read before it is rewritten
+    }
+    u = seg_end;
+  }
+
+  // Finalize the tiles whose last part arrived here: sum the parts in
+  // workgroup order, store bf16, reset the counter for the next call.
+  for (int i = 0; i < nfin; ++i) {
+    const LargeProblem& pr = args.prob[fin_p[i]];
+    const int tile = fin_tile[i];
+    const long long tile_u0 = pr.u_begin + static_cast<long long>(tile) * pr.KT;
+    const int wfirst = lg_unit_owner(tile_u0, U, NW);
+    const int wlast = lg_unit_owner(tile_u0 + pr.KT - 1, U, NW);
+    zero(acc);
+    float* sum = reinterpret_cast<float*>(&acc);
+    for (int w = wfirst; w <= wlast; ++w) {
+      const float* part = part_of(w, lg_first_unit(w, U, NW) >= tile_u0 ? 0 : 1);
+      float v[C::Regs];
+#pragma unroll
+      for (int r = 0; r < C::Regs; ++r)
+        v[r] = __hip_atomic_load(part + r * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int r = 0; r < C::Regs; ++r) sum[r] += v[r];
+    }
+    e.setup(lg_lds, pr.x, pr.qw, pr.sp, args.M, pr.N, pr.K, (tile % pr.MT) * C::Rows,
+            tile / pr.MT);
+    e.store(acc, pr.y);
+    if (tid == 0)
+      __hip_atomic_store(args.counters + pr.t_begin + tile, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ================================================================ launchers
 
 template <int GS>
 hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
+  constexpr int MB = 8;
   const int NCB = (a.N + 15) / 16;
   const int NT = (NCB + kLgBlocks - 1) / kLgBlocks;
   const void* fn = reinterpret_cast<const void*>(&large_kernel<GS>);
-  const size_t lds = LgCfg<GS>::Lds;
+  const size_t lds = LgCfg<GS, MB>::Lds;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
@@ -323,14 +509,14 @@ hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
   // of x (and the packed weights must stay below 4 GB, checked by the caller).
   const long long row_bytes = 2LL * a.K;
   long long rows_per_launch = (0xFFFFFFFFLL - 16) / row_bytes;
-  rows_per_launch -= rows_per_launch % kLgRows;
-  if (rows_per_launch < kLgRows) return hipErrorInvalidValue;
+  rows_per_launch -= rows_per_launch % LgCfg<GS, MB>::Rows;
+  if (rows_per_launch < LgCfg<GS, MB>::Rows) return hipErrorInvalidValue;
   for (long long r0 = 0; r0 < a.M; r0 += rows_per_launch) {
     GemmArgs part = a;
     part.M = static_cast<int>(a.M - r0 < rows_per_launch ? a.M - r0 : rows_per_launch);
     part.x = a.x + r0 * a.K;
     part.y = a.y + r0 * a.N;
-    int MT = (part.M + kLgRows - 1) / kLgRows;
+    int MT = (part.M + LgCfg<GS, MB>::Rows - 1) / LgCfg<GS, MB>::Rows;
     const long long total = static_cast<long long>(MT) * NT;
     if (total < 1 || total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     int ntc = NT;
@@ -340,6 +526,48 @@ hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int GS, int MB>
+hipError_t launch_large_sk_t(LargeSKArgs& sk, hipStream_t stream) {
+  using C = LgCfg<GS, MB>;
+  long long units = 0;
+  int tiles = 0;
+  for (int i = 0; i < sk.nprob; ++i) {
+    LargeProblem& p = sk.prob[i];
+    p.G = p.K / GS;
+    p.NCB = (p.N + 15) / 16;
+    p.MT = (sk.M + C::Rows - 1) / C::Rows;
+    p.NT = (p.NCB + kLgBlocks - 1) / kLgBlocks;
+    p.KT = (p.G + C::T - 1) / C::T;
+    p.u_begin = units;
+    p.t_begin = tiles;
+    units += static_cast<long long>(p.MT) * p.NT * p.KT;
+    tiles += p.MT * p.NT;
+  }
+  sk.units = units;
+  long long nwg = static_cast<long long>(device_cus());
+  if (nwg > kLargeMaxWorkgroups) nwg = kLargeMaxWorkgroups;
+  if (nwg > units) nwg = units;  // every workgroup owns at least one unit
+  sk.nwg = static_cast<int>(nwg);
+  const void* fn = reinterpret_cast<const void*>(&large_streamk_kernel<GS, MB>);
+  const size_t lds = C::Lds;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  void* kargs[] = {&sk};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kLgThreads), kargs, lds,
+                         stream);
+}
+
+template <int MB>
+hipError_t launch_large_sk_g(LargeSKArgs& sk, int group, hipStream_t stream) {
+  switch (group) {
+    case 32: return launch_large_sk_t<32, MB>(sk, stream);
+    case 64: return launch_large_sk_t<64, MB>(sk, stream);
+    case 128: return launch_large_sk_t<128, MB>(sk, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -355,6 +583,53 @@ hipError_t launch_large(const GemmArgs& a, hipStream_t stream) {
     case 64: return launch_large_t<64>(a, stream);
     case 128: return launch_large_t<128>(a, stream);
     default: return launch_skinny(a, stream);  // group 256: split-K kernel
+  }
+}
+
+int large_streamk_rows(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : 128); }
+
+size_t large_streamk_counter_bytes(int M, long long total_columns) {
+  const long long rows = large_streamk_rows(M);
+  const long long mt = (static_cast<long long>(M) + rows - 1) / rows;
+  const long long ints = mt * (kMaxProblems + (total_columns + 255) / 256);
+  return static_cast<size_t>((ints * 4 + 255) / 256 * 256);
+}
+
+size_t large_streamk_part_bytes(int M) {
+  const int regs = large_streamk_rows(M) / 16 * kLgNB * 4;
+  return static_cast<size_t>(kLargeMaxWorkgroups) * 2 * kLgWaves * regs * 64 * sizeof(float);
+}
+
+bool large_streamk_fits(const StreamKProblem* probs, int count, int M, int group) {
+  if (!large_supported(group)) return false;
+  for (int i = 0; i < count; ++i) {
+    const long long xbytes = 2LL * M * probs[i].K;
+    const long long qbytes = static_cast<long long>((probs[i].N + 15) / 16) * 16 * probs[i].K / 2;
+    if (xbytes > 0xFFFFFFF0LL || qbytes > 0xFFFFFFF0LL) return false;
+  }
+  return true;
+}
+
+hipError_t launch_large_streamk(const StreamKProblem* probs, int count, int M, int group,
+                                float* part, int* counters, hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems || M < 1) return hipErrorInvalidValue;
+  LargeSKArgs sk = {};
+  for (int i = 0; i < count; ++i) {
+    sk.prob[i].x = probs[i].x;
+    sk.prob[i].qw = probs[i].qw;
+    sk.prob[i].sp = probs[i].sp;
+    sk.prob[i].y = probs[i].y;
+    sk.prob[i].N = probs[i].N;
+    sk.prob[i].K = probs[i].K;
+  }
+  sk.nprob = count;
+  sk.M = M;
+  sk.part = part;
+  sk.counters = counters;
+  switch (large_streamk_rows(M)) {
+    case 32: return launch_large_sk_g<2>(sk, group, stream);
+    case 64: return launch_large_sk_g<4>(sk, group, stream);
+    default: return launch_large_sk_g<8>(sk, group, stream);
   }
 }
 

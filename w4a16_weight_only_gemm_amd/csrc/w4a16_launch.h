@@ -54,6 +54,7 @@ struct StreamKArgs {
 // kStreamKWideBlocks when each wave reads them itself (then one activation
 // fragment serves that many weight tiles).
 constexpr int kStreamKWideBlocks = 4;
+constexpr int kStreamKWideMaxWaves = 4096;      // grid cap with wide units
 
 // Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints,
 // rounded up to 256 bytes), then the parts.
@@ -62,6 +63,46 @@ size_t streamk_part_bytes(int M);
 
 hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
                           int* counters, hipStream_t stream);
+
+// ---- stream-K large-M path (tiles of 32, 64 or 128 rows x 256 columns) ----
+constexpr int kLargeMaxWorkgroups = 320;  // persistent grid never exceeds this
+
+struct LargeProblem {
+  const uint16_t* x;
+  const uint32_t* qw;
+  const uint16_t* sp;
+  uint16_t* y;
+  int N, K;
+  // filled in by launch_large_streamk
+  int G, NCB;               // groups per column, 16-column blocks
+  int MT, NT, KT;           // row tiles, column tiles, k-tiles per tile
+  long long u_begin;        // first unit (tile, k-tile) of this problem
+  int t_begin;              // first tile (index of its counter)
+};
+
+struct LargeSKArgs {
+  LargeProblem prob[kMaxProblems];
+  int nprob;
+  int M;
+  long long units;          // total units over all problems
+  int nwg;                  // workgroups, each owning at least one unit
+  float* part;              // [kLargeMaxWorkgroups][2][8 waves][regs][64 lanes] fp32 parts
+  int* counters;            // one per tile, zero between calls
+};
+
+// Tile rows used for M rows, and the workspace layout: counters first
+// (rounded up to 256 bytes), then the parts.
+int large_streamk_rows(int M);
+size_t large_streamk_counter_bytes(int M, long long total_columns);
+size_t large_streamk_part_bytes(int M);
+// True when the problems can run on the stream-K large path (group size and
+// 32-bit buffer ranges).
+bool large_streamk_fits(const StreamKProblem* probs, int count, int M, int group);
+hipError_t launch_large_streamk(const StreamKProblem* probs, int count, int M, int group,
+                                float* part, int* counters, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cus();
 
 // M-dispatch: W4A16_PATH_SKINNY or W4A16_PATH_LARGE for a supported shape.
 int choose_path(int M, int N, int K, int group);

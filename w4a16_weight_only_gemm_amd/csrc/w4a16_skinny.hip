@@ -625,20 +625,6 @@ hipError_t launch_splitk_g(const GemmArgs& a, hipStream_t stream) {
   return launch_splitk_t<GS, 4>(a, stream);
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cached[dev] = cus;
-  }
-  return cached[dev];
-}
 
 #ifndef W4A16_STREAMK_WIDE_PREFETCH
 #define W4A16_STREAMK_WIDE_PREFETCH 1
@@ -697,7 +683,8 @@ int plan_streamk(StreamKArgs& sk, int nbw) {
   }
   sk.units = units;
   int wgs = device_cus() * (nbw == 1 ? W4A16_STREAMK_WG_PER_CU : W4A16_STREAMK_WIDE_WG_PER_CU);
-  if (wgs * W4A16_STREAMK_WAVES > kStreamKMaxWaves) wgs = kStreamKMaxWaves / W4A16_STREAMK_WAVES;
+  const int max_waves = nbw == 1 ? kStreamKMaxWaves : kStreamKWideMaxWaves;
+  if (wgs * W4A16_STREAMK_WAVES > max_waves) wgs = max_waves / W4A16_STREAMK_WAVES;
   // Every counted wave must own at least one unit (NW <= units): the parts of
   // a super-block are then produced by consecutive non-empty waves.
   long long nw = static_cast<long long>(wgs) * W4A16_STREAMK_WAVES;
@@ -707,6 +694,21 @@ int plan_streamk(StreamKArgs& sk, int nbw) {
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
   switch (a.group) {
