@@ -2,11 +2,16 @@
 
 A step is one pass of the hot path over one batch: the four projections of one
 27B-class layer (qkv 5120x7168, o 6144x5120, gate+up 5120x34816, down
-17408x5120, group 128) at M activation rows, each a w4a16_gemm call through the
-C ABI. Weights are packed once per layer and kept in HBM; successive steps cycle
-through --layers distinct layer sets (1.39 GB at the default 8) so that no step
-finds its weights in the 256 MB last-level cache. Inputs are resident on the
-device before the timed region starts.
+17408x5120, group 128) at M activation rows, one w4a16_gemm_grouped call through
+the C ABI (--separate: four w4a16_gemm calls). Weights are packed once per layer
+and kept in HBM; successive steps cycle through --layers distinct layer sets
+(1.39 GB at the default 8) so that no step finds its weights in the 256 MB
+last-level cache. Inputs are resident on the device before the timed region
+starts. The default warmup is long enough (3000 steps) for the clocks to reach
+their sustained level before timing.
+
+  python bench.py --sweep   the full-step sweep over a 64-layer stack at
+                            M = 1 .. 1024 with the step-time model fitted to it
 
 The headline line reports the decode layer set (M = 1) in HBM TB/s over
 algorithmic bytes (packed weights + scales + activations + outputs, counted once
@@ -484,7 +489,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--graph", action="store_true",
                     help="replay the steps from a captured HIP graph (no host launch cost)")
@@ -495,7 +500,7 @@ def main(argv=None):
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="compute profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--traffic-key", default="streamk_grouped|M=1")
-    ap.add_argument("--traffic-kernel", default="streamk_kernel")
+    ap.add_argument("--traffic-kernel", default="::streamk_kernel<")
     ap.add_argument("--separate", action="store_true",
                     help="four launches per step at every M (no grouped streaming launch)")
     ap.add_argument("--sweep", action="store_true",
