@@ -485,6 +485,54 @@ def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
                               "best fractions seen over the sweep"}}
 
 
+HEAD_N, HEAD_K = 248320, 5120
+HEAD_ROWS = (1, 2, 4, 8, 16)
+
+
+def run_head(steps: int, warmup: int, rows=HEAD_ROWS):
+    """The output-head workload: one projection of N = 248,320 rows over K = 5120
+    (635 MB of packed weights, larger than the last-level cache), at M rows,
+    through the workspace entry point; one step = one call."""
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, 4), HEAD_N, HEAD_K)
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, 4), HEAD_N, HEAD_K // GROUP)
+    qw, sp = w4.w4a16_pack(q, s, GROUP)
+    del q, s
+    qw = torch.from_numpy(qw.view(np.int32)).to("cuda")
+    sp = torch.from_numpy(sp.view(np.int16)).to("cuda")
+    cur = torch.cuda.current_stream()
+    out = []
+    for M in rows:
+        x = torch.from_numpy(synth.gen_x(synth.tensor_id(synth.KIND_X, 0, 4, M), M, HEAD_K)
+                             .view(np.int16)).to("cuda")
+        y = torch.empty((M, HEAD_N), dtype=torch.int16, device="cuda")
+        nb = w4.w4a16_workspace_bytes(M, HEAD_N)
+        ws = torch.zeros(max(1, nb // 4), dtype=torch.int32, device="cuda")
+        args = (x.data_ptr(), qw.data_ptr(), sp.data_ptr(), y.data_ptr(), M, HEAD_N, HEAD_K, GROUP,
+                ws.data_ptr(), nb, cur.cuda_stream)
+
+        def calls(n):
+            for _ in range(n):
+                rc = lib.w4a16_gemm_ws(*args)
+                if rc != 0:
+                    raise RuntimeError(f"w4a16_gemm_ws failed with status {rc}")
+        calls(warmup)
+        torch.cuda.synchronize()
+        ms = timed(lambda: calls(steps), cur) / steps
+        b = algorithmic_bytes(M, HEAD_N, HEAD_K, GROUP)
+        out.append({"M": M, "ms_per_call": ms, "tbps": b / (ms * 1e-3) / 1e12,
+                    "hbm_frac": b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)})
+        print(f"# head M={M}: {ms * 1e3:.1f} us/call, {out[-1]['tbps']:.2f} TB/s", file=sys.stderr,
+              flush=True)
+    return {"workload": f"output head N={HEAD_N} K={HEAD_K}, group {GROUP}, w4a16_gemm_ws",
+            "rows": out}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,6 +556,9 @@ def main(argv=None):
                          "model fitted to it (one JSON object), instead of the headline line")
     ap.add_argument("--sweep-layers", type=int, default=64)
     ap.add_argument("--sweep-passes", type=int, default=5)
+    ap.add_argument("--head", action="store_true",
+                    help="output-head workload (N = 248,320, K = 5120) at M = 1..16 (one JSON "
+                         "object), instead of the headline line")
     args = ap.parse_args(argv)
     if args.traffic_from:
         print(json.dumps(traffic_from_pmc(args.traffic_from[0], args.traffic_from[1],
@@ -526,6 +577,9 @@ def main(argv=None):
     import w4a16_weight_only_gemm_amd  # noqa: F401  (fails loudly without the library)
     if args.sweep:
         print(json.dumps(run_sweep(args.sweep_layers, args.sweep_passes)))
+        return 0
+    if args.head:
+        print(json.dumps(run_head(args.steps, min(args.warmup, 1000))))
         return 0
 
     t0 = time.time()

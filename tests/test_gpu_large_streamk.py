@@ -99,13 +99,14 @@ def test_streamk_large_grouped_problems(M):
             assert all(np.array_equal(a, b) for a, b in zip(first, outs))
 
 
+@pytest.mark.parametrize("layer", [0, 63])
 @pytest.mark.parametrize("M", [64, 1024])
-def test_streamk_large_layer_set_sampled(M):
+def test_streamk_large_layer_set_sampled(M, layer):
     """The four projections of a layer in one launch at full size: all rows of
-    256 sampled columns of each."""
+    256 sampled columns of each (layers 0 and 63 of the 64-layer stack)."""
     import torch
     import w4a16_weight_only_gemm_amd as w4
-    data = [synth.layer_inputs(0, i, M) for i in range(4)]
+    data = [synth.layer_inputs(layer, i, M) for i in range(4)]
     probs = [Problem(x, q, s, synth.GROUP) for (x, q, s) in data]
     ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in probs]
     ws = workspace(M, sum(p.N for p in probs))
@@ -113,7 +114,7 @@ def test_streamk_large_layer_set_sampled(M):
                           synth.GROUP, ws)
     torch.cuda.synchronize()
     for i, ((x, q, s), y, pj) in enumerate(zip(data, ys, synth.LAYER_PROJECTIONS)):
-        cols = np.sort(np.random.default_rng(i * 5 + M).choice(pj.N, 256, replace=False))
+        cols = np.sort(np.random.default_rng(i * 5 + M + layer).choice(pj.N, 256, replace=False))
         cols[0], cols[-1] = 0, pj.N - 1
         yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[:, cols]
         r = tolerance_ratio(yb, oracle.gemm(x, q[cols], s[cols], synth.GROUP,
@@ -140,3 +141,19 @@ def test_streamk_large_workspace_errors():
     torch.cuda.synchronize()
     yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert tolerance_ratio(yb, oracle.gemm(x, q, s, g)) <= 1.0
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_output_head_sampled(M):
+    """The output-head shape (N = 248,320 rows of K = 5120) through the
+    workspace entry point: all rows of 512 sampled columns, first and last
+    included."""
+    N, K, g = 248320, 5120, 128
+    x, q, s = _inputs(70 + M, M, N, K, g)
+    prob = Problem(x, q, s, g)
+    y = run_ws(prob, workspace(M, N))
+    cols = np.sort(np.random.default_rng(M).choice(N, 512, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    r = tolerance_ratio(y[:, cols], oracle.gemm(x, q[cols], s[cols], g, threads=synth.default_threads()))
+    log(f"head M={M}: ratio {r:.4f}")
+    assert r <= 1.0

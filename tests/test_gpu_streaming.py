@@ -94,12 +94,14 @@ def _layer_problems(M, layer=0):
     return probs, data
 
 
+@pytest.mark.parametrize("layer", [0, 63])
 @pytest.mark.parametrize("M", [1, 16])
-def test_layer_set_grouped_full(M):
-    """The four projections of a layer in one launch, every output checked."""
+def test_layer_set_grouped_full(M, layer):
+    """The four projections of a layer in one launch, every output checked
+    (layers 0 and 63: the first and last of the 64-layer stack)."""
     import torch
     import w4a16_weight_only_gemm_amd as w4
-    probs, data = _layer_problems(M)
+    probs, data = _layer_problems(M, layer)
     ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in probs]
     ws = workspace(M, sum(p.N for p in probs))
     entries = [(p.x, p.qw, p.sp, y, p.N, p.K) for p, y in zip(probs, ys)]
