@@ -4,16 +4,20 @@ the invariants its correctness rests on, over many shapes and grid sizes:
 * the units (problem, column block, group) are split into contiguous,
   non-empty, disjoint runs, one per wave, covering everything exactly once;
 * every super-block (NBW consecutive column blocks: 1 with activations staged
-  in LDS, 4 otherwise) is either stored whole by one wave, or cut into parts by
-  consecutive waves whose (wave, slot) partial buffers are distinct, and the
-  per-super-block counter reaches exactly the number of parts (so exactly one
-  wave finalizes it, and it finds every part);
+  in LDS, 4 otherwise) is stored exactly once: whole by one wave during its
+  stream, or cut, in which case the waves keep their parts in LDS slots
+  (wave, slot) that are distinct, the workgroup's leading wave sums exactly
+  the slots written for that super-block, and either stores the result (the
+  workgroup holds it whole) or publishes one part per workgroup in distinct
+  workspace slots (workgroup, slot), with a counter that reaches exactly the
+  number of those parts, so exactly one workgroup finalizes it and it finds
+  every part;
 * every weight, scale, activation, output, partial, counter and LDS index the
   kernel forms lies inside its buffer.
 
-It mirrors the kernel's integer formulas (wave ranges, unit owners, slots) and
-the launcher's grid and LDS sizing, so a change to either must keep this test
-in step; it runs no device code.
+It mirrors the kernel's integer formulas (wave ranges, unit owners, slots,
+leading waves) and the launcher's grid and LDS sizing, so a change to either
+must keep this test in step; it runs no device code.
 """
 import itertools
 
@@ -39,11 +43,15 @@ WIDE_WG_PER_CU = 1
 WIDE_MAX_WAVES = 4096
 
 
+def lds_part_bytes(M, nbw):
+    return WAVES * 2 * nbw * min(M, 16) * 16 * 4
+
+
 def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
-    """The launcher's grid: (problem table, units, NW, workgroups, lds bytes,
-    column blocks, nbw). With nbw None, the launcher's choice: 1 when the
-    activations fit the LDS budget, WIDE otherwise (with WIDE_WG_PER_CU
-    workgroups per compute unit)."""
+    """The launcher's grid: (problem table, units, NW, workgroups, staged
+    activation bytes, column blocks, nbw). With nbw None, the launcher's
+    choice: 1 when the staged activations and the LDS parts fit the LDS
+    budget, WIDE otherwise (with WIDE_WG_PER_CU workgroups per compute unit)."""
     def grid(nbw):
         table, units, sbs, cbs = [], 0, 0, 0
         for (N, K) in problems:
@@ -71,11 +79,12 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
         e = sum(Mr * (p["K"] + 8) for p in table
                 if p["u_begin"] + p["NSB"] * p["G"] > wu0 and p["u_begin"] < wu1)
         need = max(need, e)
+    x_bytes = (need * 2 + 15) // 16 * 16
     if nbw is None:
-        nbw = 1 if need * 2 <= LDS_BUDGET else WIDE
+        nbw = 1 if x_bytes + lds_part_bytes(M, 1) <= LDS_BUDGET else WIDE
     if nbw != 1:
         table, units, nw, wgs, cbs = grid(nbw)
-    return table, units, nw, wgs, need * 2, cbs, nbw
+    return table, units, nw, wgs, x_bytes, cbs, nbw
 
 
 def problem_of(table, u):
@@ -87,30 +96,46 @@ def problem_of(table, u):
 
 
 def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
-    table, U, NW, wgs, lds, total_cbs, nbw = plan(problems, M, group, cus, wg_per_cu, nbw)
+    table, U, NW, wgs, x_bytes, total_cbs, nbw = plan(problems, M, group, cus, wg_per_cu, nbw)
     Mr = min(M, 16)
     wpl = group // 32
-    xlds = nbw == 1 and lds <= LDS_BUDGET
+    xlds = nbw == 1 and x_bytes + lds_part_bytes(M, 1) <= LDS_BUDGET
+    # LDS layout: staged activations (XLDS only), then the waves' parts
+    part_off = x_bytes if xlds else 0
+    lds = part_off + lds_part_bytes(M, nbw)
+    part_floats = nbw * Mr * 16
     total_sbs = sum(p["NSB"] for p in table)
     assert total_sbs <= 8 + total_cbs          # counters the host reserves
+    ws_part_floats = max(MAX_WAVES * 2, WIDE_MAX_WAVES * 2 * WIDE) * Mr * 16
+
+    def sb_of(u):
+        pr = table[problem_of(table, u)]
+        sb = (u - pr["u_begin"]) // pr["G"]
+        s0 = pr["u_begin"] + sb * pr["G"]
+        return pr["sb_begin"] + sb, s0, s0 + pr["G"]
+
+    def wg_of(u):
+        return owner(u, U, NW) // WAVES
+
     covered = {}
     counters = [0] * total_sbs
-    finalized = [0] * total_sbs
-    part_writers = {}
-    stored_whole = [0] * total_sbs
+    nseg_of = {}
+    emitted = [0] * total_sbs
+    ws_parts = {}
     for b in range(wgs):
+        W0 = first_unit(min(b * WAVES, NW), U, NW)
+        W1 = first_unit(min((b + 1) * WAVES, NW), U, NW)
         # LDS staging of the workgroup (problems touched by its waves)
         if xlds:
-            wu0 = first_unit(b * WAVES, U, NW)
-            wu1 = first_unit(min((b + 1) * WAVES, NW), U, NW)
             off = 0
-            if wu1 > wu0:
-                for i in range(problem_of(table, wu0), problem_of(table, wu1 - 1) + 1):
+            if W1 > W0:
+                for i in range(problem_of(table, W0), problem_of(table, W1 - 1) + 1):
                     stride = table[i]["K"] + 8
                     # last 16-byte write: row Mr-1, chunk K/8-1
                     last = off + (Mr - 1) * stride + 8 * (table[i]["K"] // 8 - 1) + 8
-                    assert last * 2 <= lds, (b, i)
+                    assert last * 2 <= x_bytes, (b, i)
                     off += Mr * stride
+        lds_parts = {}                      # (local wave, slot) -> super-block
         for wave in range(WAVES):
             wg = b * WAVES + wave
             if wg >= NW:
@@ -138,32 +163,61 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                 if g == pr["G"] - 1 or u == u1 - 1:
                     gsb = pr["sb_begin"] + sb
                     if seg_g0 == 0 and g == pr["G"] - 1:
-                        stored_whole[gsb] += 1
+                        emitted[gsb] += 1
                     else:
                         usb0 = pr["u_begin"] + sb * pr["G"]
-                        wfirst, wlast = owner(usb0, U, NW), owner(usb0 + pr["G"] - 1, U, NW)
-                        nseg = wlast - wfirst + 1
-                        assert nseg >= 2
-                        assert wfirst <= wg <= wlast
                         slot = 0 if u0 >= usb0 else 1
-                        key = (wg, slot)
-                        assert key not in part_writers, key
-                        part_writers[key] = gsb
-                        # last float of this wave's part, against the workspace size
-                        part_floats = max(MAX_WAVES * 2, WIDE_MAX_WAVES * 2 * WIDE) * Mr * 16
-                        assert ((wg * 2 + slot) * nbw + nbw) * Mr * 16 <= part_floats
-                        counters[gsb] += 1
-                        if counters[gsb] == nseg:
-                            finalized[gsb] += 1
-                            # the finalizer reads the part of every wave in [wfirst, wlast]
-                            for w in range(wfirst, wlast + 1):
-                                ws = 0 if first_unit(w, U, NW) >= usb0 else 1
-                                assert part_writers.get((w, ws)) == gsb, (w, ws, gsb)
+                        assert (wave, slot) not in lds_parts, (b, wave, slot)
+                        lds_parts[(wave, slot)] = gsb
+                        # last float of this slot in LDS
+                        assert part_off + ((wave * 2 + slot) + 1) * part_floats * 4 <= lds
                     seg_g0 = 0
+        # hand-off after the stream: each wave's led super-blocks
+        read = set()
+        for wave in range(WAVES):
+            wg = b * WAVES + wave
+            if wg >= NW:
+                continue
+            u0, u1 = first_unit(wg, U, NW), first_unit(wg + 1, U, NW)
+            for k in range(2):
+                u = u0 if k == 0 else u1 - 1
+                gsb, s0, s1 = sb_of(u)
+                if k == 1 and s0 <= u0:
+                    break
+                if k == 0 and s0 < u0 and wave > 0:
+                    continue
+                if s0 >= u0 and s1 <= u1:
+                    continue
+                vlast = owner(min(s1, W1) - 1, U, NW)
+                assert wg <= vlast < min((b + 1) * WAVES, NW)
+                for v in range(wg, vlast + 1):
+                    slot = 0 if first_unit(v, U, NW) >= s0 else 1
+                    key = (v - b * WAVES, slot)
+                    assert lds_parts.get(key) == gsb, (b, key, gsb)
+                    assert key not in read
+                    read.add(key)
+                if s0 >= W0 and s1 <= W1:
+                    emitted[gsb] += 1
+                    continue
+                slot = 0 if W0 >= s0 else 1
+                assert (b, slot) not in ws_parts
+                ws_parts[(b, slot)] = gsb
+                assert ((b * 2 + slot) + 1) * part_floats <= ws_part_floats
+                nseg = wg_of(s1 - 1) - wg_of(s0) + 1
+                assert nseg >= 2
+                nseg_of[gsb] = nseg
+                counters[gsb] += 1
+                if counters[gsb] == nseg:
+                    emitted[gsb] += 1
+                    for c in range(wg_of(s0), wg_of(s1 - 1) + 1):
+                        cs = 0 if first_unit(c * WAVES, U, NW) >= s0 else 1
+                        assert ws_parts.get((c, cs)) == gsb, (c, cs, gsb)
+        assert read == set(lds_parts), (b, set(lds_parts) - read)
     assert len(covered) == U and sorted(covered) == list(range(U))
     for gsb in range(total_sbs):
-        assert stored_whole[gsb] + finalized[gsb] == 1, gsb
-        assert finalized[gsb] == 0 or counters[gsb] >= 2
+        assert emitted[gsb] == 1, gsb
+        if gsb in nseg_of:
+            assert counters[gsb] == nseg_of[gsb]
     # every column block is in exactly one super-block
     for pr in table:
         assert pr["NSB"] * nbw >= pr["NCB"] > (pr["NSB"] - 1) * nbw

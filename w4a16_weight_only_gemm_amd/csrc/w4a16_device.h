@@ -33,6 +33,14 @@ __device__ __forceinline__ gptr<T> to_global(T* p) {
 // hot loop's later waits exact.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// keep flying (a plain __syncthreads would also wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A wave-uniform value moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

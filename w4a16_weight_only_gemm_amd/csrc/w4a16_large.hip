@@ -146,13 +146,6 @@ __device__ __forceinline__ void zero(Acc<MB>& a) {
     for (int nb = 0; nb < kLgNB; ++nb) a.v[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// LDS-only barrier: global loads in flight keep flying.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ------------------------------------------------------------------ tile engine
 //
 // One workgroup's view of one output tile: rows m0 .. m0 + Rows - 1, column

@@ -46,8 +46,9 @@ struct StreamKArgs {
   int M;
   long long units;          // total units over all problems
   int nwaves;               // waves that own units (<= units)
-  float* part;              // [kStreamKMaxWaves][2][NBW][min(M,16)][16] fp32 parts
+  float* part;              // [workgroups][2][NBW][min(M,16)][16] fp32 parts
   int* counters;            // one per super-block, zero between calls
+  int lds_part_off;         // LDS offset (in 4-byte words) of the waves' parts
 };
 
 // Column blocks per stream-K unit: 1 when the activations are staged in LDS,

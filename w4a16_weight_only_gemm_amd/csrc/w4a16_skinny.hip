@@ -208,47 +208,81 @@ __device__ __forceinline__ int unit_owner(long long u, long long U, int NW) {
   return static_cast<int>(((u + 1) * NW - 1) / U);
 }
 
-// Cross-workgroup hand-off of a column block's parts, without device-wide
-// fences (on this chip a device-scope fence writes back and invalidates the
-// whole L2, which costs more than the GEMM itself). Instead every access that
-// crosses waves is an agent-scope atomic, coherent across the L2s of all
-// XCDs:
+// Hand-off of the super-blocks that stream-K cuts, in two levels, both after
+// the stream, so that no wave waits on memory while it streams:
+//  1. inside the workgroup: a wave keeps its part of a super-block cut at the
+//     start or end of its run in LDS (slot 0 for the first super-block of its
+//     run, 1 for the last); after the stream, one barrier, and the first wave
+//     of the workgroup that overlaps such a super-block sums the parts of the
+//     workgroup's waves in wave order;
+//  2. across workgroups: a super-block that extends past the workgroup's
+//     units is published as one part per workgroup through the workspace and
+//     counted by an atomic counter per super-block; the workgroup whose
+//     increment completes the count sums the parts in workgroup order.
+// Either way the summation order is fixed, so the result does not depend on
+// timing. Level 2 uses no device-wide fences (on this chip a device-scope
+// fence writes back and invalidates the whole L2, which costs more than the
+// GEMM itself). Every access that crosses workgroups is an agent-scope atomic,
+// coherent across the L2s of all XCDs:
 //   writer: atomic stores of the part; wait until they complete (vmcnt 0);
-//           atomic increment of the block's counter.
+//           atomic increment of the super-block's counter.
 //   reader: the wave whose increment completes the count reads every part
 //           with atomic loads, issued only after the increment returned.
 // The writer's stores are complete, hence visible device-wide, before its
 // increment is issued; the reader's loads depend on its increment's result
 // and so happen after it. Compiler barriers keep the generated order.
 
-// Part of super-block sb (NBW column blocks of problem pr) that this wave
-// (wg, whose run starts at unit u0) computed: publish it and count it. Returns
-// true when it was the last part of the super-block to arrive; the caller then
-// finalizes it (after its own stream, so the hot loop holds no inner loops).
-// The parts of a super-block come from the consecutive waves owning its first
-// to last unit; a wave's slot is 0 for the first super-block of its run and 1
-// for the last.
+// Index of this lane's value (column block j, row m, column c16) in a part of
+// NBW x Mr x 16 floats. Rows at or past Mr are padding rows, computed from a
+// repeat of row M - 1 and so equal to row Mr - 1: they map there (same value),
+// which keeps every part access unconditional.
 template <int NBW>
-__device__ __forceinline__ bool publish_part(const StreamKArgs& args, const StreamKProblem& pr,
-                                             int wg, long long u0, int sb, int lane, int lg,
-                                             int c16, int Mr, const f32x4 (&yacc)[NBW]) {
+__device__ __forceinline__ int part_index(int j, int m, int c16, int Mr) {
+  return (j * Mr + min(m, Mr - 1)) * 16 + c16;
+}
+
+// Store the bf16 results of super-block sb (rows 4*lg + r of column c16 of
+// each of its NBW column blocks).
+template <int NBW>
+__device__ __forceinline__ void store_block(const StreamKProblem& pr, int sb, const float (&v)[NBW][4],
+                                            int lg, int c16, int M) {
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int n = (sb * NBW + j) * 16 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (m < M && n < pr.N) to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(v[j][r]);
+    }
+  }
+}
+
+// Workgroup of the wave that owns unit u.
+template <int WAVES>
+__device__ __forceinline__ int unit_wg(long long u, long long U, int NW) {
+  return unit_owner(u, U, NW) / WAVES;
+}
+
+// Level 2, writer: publish workgroup b's part v of super-block sb (units
+// [s0, s1) of problem pr) and count it. Returns true when it was the last part
+// to arrive; the caller then finalizes the super-block. A workgroup's slot is
+// 0 for the super-block holding its first unit W0, 1 for the one holding its last.
+template <int NBW, int WAVES>
+__device__ __forceinline__ bool publish_wg_part(const StreamKArgs& args, const StreamKProblem& pr,
+                                                int b, long long W0, long long s0, long long s1,
+                                                int sb, int lane, int lg, int c16, int Mr,
+                                                const float (&v)[NBW][4]) {
   const long long U = args.units;
   const int NW = args.nwaves;
-  const long long usb0 = pr.u_begin + static_cast<long long>(sb) * pr.G;
-  const int nseg = unit_owner(usb0 + pr.G - 1, U, NW) - unit_owner(usb0, U, NW) + 1;
-  const int slot = (u0 >= usb0) ? 0 : 1;
-  float* mine = args.part + (static_cast<size_t>(wg) * 2 + slot) * NBW * Mr * 16;
-  // Rows at or past Mr are padding rows, computed from a repeat of row M - 1
-  // and so equal to row Mr - 1: storing them there (same value) keeps every
-  // store unconditional.
+  const int nseg = unit_wg<WAVES>(s1 - 1, U, NW) - unit_wg<WAVES>(s0, U, NW) + 1;
+  const int slot = (W0 >= s0) ? 0 : 1;
+  float* mine = args.part + (static_cast<size_t>(b) * 2 + slot) * NBW * Mr * 16;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = min(4 * lg + r, Mr - 1);
-      __hip_atomic_store(mine + (j * Mr + m) * 16 + c16, yacc[j][r], __ATOMIC_RELAXED,
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(mine + part_index<NBW>(j, 4 * lg + r, c16, Mr), v[j][r], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   wait_vmem_all();  // the part is complete before it is counted
@@ -263,65 +297,54 @@ __device__ __forceinline__ bool publish_part(const StreamKArgs& args, const Stre
   return last;
 }
 
-// Sum the parts of super-block sb of problem pr in wave order, store the bf16
-// results of its column blocks and reset its counter for the next call.
-template <int NBW>
+// Level 2, reader: sum the workgroup parts of super-block sb (units [s0, s1)
+// of problem pr) in workgroup order, store the bf16 results and reset its
+// counter for the next call.
+template <int NBW, int WAVES>
 __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const StreamKProblem& pr,
-                                               int sb, int lane, int lg, int c16, int M, int Mr) {
+                                               long long s0, long long s1, int sb, int lane,
+                                               int lg, int c16, int M, int Mr) {
   const long long U = args.units;
   const int NW = args.nwaves;
-  const long long usb0 = pr.u_begin + static_cast<long long>(sb) * pr.G;
-  const int wfirst = unit_owner(usb0, U, NW);
-  const int wlast = unit_owner(usb0 + pr.G - 1, U, NW);
+  const int bfirst = unit_wg<WAVES>(s0, U, NW);
+  const int blast = unit_wg<WAVES>(s1 - 1, U, NW);
   float sum[NBW][4];
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
-  // Branch-free loads (padding rows read row Mr - 1 and are never stored), two
-  // parts at a time, so their loads are all in flight together. The sum runs
-  // in wave order.
-  auto load_part = [&](float (&v)[NBW][4], int w) {
-    const int ws = (wave_first_unit(w, U, NW) >= usb0) ? 0 : 1;
-    float* part = args.part + (static_cast<size_t>(w) * 2 + ws) * NBW * Mr * 16;
+  // Two parts at a time, so their loads are all in flight together; the sum
+  // runs in workgroup order.
+  auto load_part = [&](float (&v)[NBW][4], int b) {
+    const int slot = (wave_first_unit(b * WAVES, U, NW) >= s0) ? 0 : 1;
+    float* part = args.part + (static_cast<size_t>(b) * 2 + slot) * NBW * Mr * 16;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = min(4 * lg + r, Mr - 1);
-        v[j][r] = __hip_atomic_load(part + (j * Mr + m) * 16 + c16, __ATOMIC_RELAXED,
+      for (int r = 0; r < 4; ++r)
+        v[j][r] = __hip_atomic_load(part + part_index<NBW>(j, 4 * lg + r, c16, Mr), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
   };
-  int w = wfirst;
-  for (; w + 1 <= wlast; w += 2) {
+  int b = bfirst;
+  for (; b + 1 <= blast; b += 2) {
     float v0[NBW][4], v1[NBW][4];
-    load_part(v0, w);
-    load_part(v1, w + 1);
+    load_part(v0, b);
+    load_part(v1, b + 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sum[j][r] = (sum[j][r] + v0[j][r]) + v1[j][r];
   }
-  if (w <= wlast) {
+  if (b <= blast) {
     float v0[NBW][4];
-    load_part(v0, w);
+    load_part(v0, b);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sum[j][r] += v0[j][r];
   }
-#pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    const int n = (sb * NBW + j) * 16 + c16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * lg + r;
-      if (m < M && n < pr.N)
-        to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(sum[j][r]);
-    }
-  }
+  store_block<NBW>(pr, sb, sum, lg, c16, M);
   if (lane == 0)
     __hip_atomic_store(args.counters + pr.sb_begin + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -452,127 +475,163 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
         }
       }
     }
-    // LDS-only fences: the weight loads already in flight keep flying.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    lds_barrier();  // LDS only: the weight loads already in flight keep flying
   }
+  // This wave's LDS parts: [2 slots][NBW][Mr][16] fp32 (level 1 of the hand-off).
+  float* const lparts = reinterpret_cast<float*>(xlds + args.lds_part_off);
+  float* const mylds = lparts + wave * 2 * NBW * Mr * 16;
 
-  if (!active) return;
+  if (active) {
+    const bf16x8 bias = bias_operand();
+    f32x4 yacc[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16x8 bias = bias_operand();
-  f32x4 yacc[NBW];
+    // The wave's run, one problem at a time. Within a problem consecutive units
+    // are consecutive groups of a super-block, so the cursors are plain offsets.
+    for (bool first = true;; first = false) {
+      if (!first) {
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Super-blocks this wave must finalize (at most its first and last).
-  int fin_p0 = -1, fin_sb0 = 0, fin_p1 = -1, fin_sb1 = 0;
+        for (int i = 0; i < P; ++i) load_unit(bufA[i], run, run.v0 + i);
+      }
+      const StreamKProblem& pr = args.prob[run.p];
+      const int G = run.G;
+      const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
+      int sb = uniform(run.v0 / G);
+      int g = uniform(run.v0 - sb * G);
+      int seg_g0 = g;  // first group of the current super-block segment
 
-  // The wave's run, one problem at a time. Within a problem consecutive units
-  // are consecutive groups of a super-block, so the cursors are plain offsets.
-  for (bool first = true;; first = false) {
-    if (!first) {
+      // Compute the units of one chunk (buf holds units v .. v+P-1).
+      auto compute_chunk = [&](UnitLoads<WPL, NBW> (&buf)[P], int v) {
 #pragma unroll
-      for (int i = 0; i < P; ++i) load_unit(bufA[i], run, run.v0 + i);
-    }
-    const StreamKProblem& pr = args.prob[run.p];
-    const int G = run.G;
-    const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
-    const gptr<uint16_t> yout = to_global(pr.y);
-    int sb = uniform(run.v0 / G);
-    int g = uniform(run.v0 - sb * G);
-    int seg_g0 = g;  // first group of the current super-block segment
-
-    // Compute the units of one chunk (buf holds units v .. v+P-1).
-    auto compute_chunk = [&](UnitLoads<WPL, NBW> (&buf)[P], int v) {
+        for (int i = 0; i < P; ++i) {
+          const int vv = v + i;
+          if (vv < run.v1) {
+            bf16x8 a[WPL];
+            if constexpr (XLDS) {
+              const uint32_t* xl = xlds + xbase + (g * GS) / 2;
 #pragma unroll
-      for (int i = 0; i < P; ++i) {
-        const int vv = v + i;
-        if (vv < run.v1) {
-          bf16x8 a[WPL];
-          if constexpr (XLDS) {
-            const uint32_t* xl = xlds + xbase + (g * GS) / 2;
+              for (int t = 0; t < WPL; ++t)
+                a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 4 * t));
+            } else {
 #pragma unroll
-            for (int t = 0; t < WPL; ++t)
-              a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xl + 4 * t));
-          } else {
-#pragma unroll
-            for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
-          }
-          if constexpr (NBW == 1) {
-            const f32x4 acc = group_product<WPL>(buf[i].w[0], a, bias);
-            const float sc = fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[0] >> (16 * (c16 & 1))));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[0][r] = __builtin_fmaf(sc, acc[r], yacc[0][r]);
-          } else {
-            // -136 * (row sums of the group) once, as the start of every block's sum
-            f32x4 accb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-              f32x4 acc = accb;
-#pragma unroll
-              for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[j].w[t]), acc);
-              const float sc =
-                  fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[j] >> (16 * (c16 & 1))));
-#pragma unroll
-              for (int r = 0; r < 4; ++r) yacc[j][r] = __builtin_fmaf(sc, acc[r], yacc[j][r]);
+              for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
             }
-          }
-
-          if (g == G - 1 || vv == run.v1 - 1) {
-            // End of this wave's segment of super-block sb.
-            if (seg_g0 == 0 && g == G - 1) {
-              // The whole super-block was ours: store the results.
+            if constexpr (NBW == 1) {
+              const f32x4 acc = group_product<WPL>(buf[i].w[0], a, bias);
+              const float sc = fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[0] >> (16 * (c16 & 1))));
+#pragma unroll
+              for (int r = 0; r < 4; ++r) yacc[0][r] = __builtin_fmaf(sc, acc[r], yacc[0][r]);
+            } else {
+              // -136 * (row sums of the group) once, as the start of every block's sum
+              f32x4 accb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
 #pragma unroll
               for (int j = 0; j < NBW; ++j) {
-                const int n = (sb * NBW + j) * 16 + c16;
+                f32x4 acc = accb;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int m = 4 * lg + r;
-                  if (m < M && n < pr.N) yout[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(yacc[j][r]);
-                }
-              }
-              wait_vmem_all();
-            } else if (publish_part<NBW>(args, pr, wg, u0, sb, lane, lg, c16, Mr, yacc)) {
-              if (fin_p0 < 0) {
-                fin_p0 = run.p;
-                fin_sb0 = sb;
-              } else {
-                fin_p1 = run.p;
-                fin_sb1 = sb;
+                for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[j].w[t]), acc);
+                const float sc =
+                    fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[j] >> (16 * (c16 & 1))));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[j][r] = __builtin_fmaf(sc, acc[r], yacc[j][r]);
               }
             }
+
+            if (g == G - 1 || vv == run.v1 - 1) {
+              // End of this wave's segment of super-block sb.
+              if (seg_g0 == 0 && g == G - 1) {
+                // The whole super-block was ours: store the results. The wait
+                // keeps the compiler's later load waits exact (see wait_vmem_all).
+                float out[NBW][4];
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            seg_g0 = 0;
-          }
-          if (++g == G) {
-            g = 0;
-            ++sb;
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) out[j][r] = yacc[j][r];
+                store_block<NBW>(pr, sb, out, lg, c16, M);
+                wait_vmem_all();
+              } else {
+                // Cut: keep the part in LDS (slot 0 for the first super-block
+                // of the run, 1 for the last) until the stream has ended.
+                const long long usb0 = pr.u_begin + static_cast<long long>(sb) * G;
+                float* mine = mylds + (u0 >= usb0 ? 0 : NBW * Mr * 16);
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) mine[part_index<NBW>(j, 4 * lg + r, c16, Mr)] = yacc[j][r];
+              }
+#pragma unroll
+              for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+              seg_g0 = 0;
+            }
+            if (++g == G) {
+              g = 0;
+              ++sb;
+            }
           }
         }
+      };
+
+      // Double-buffered chunks: the next chunk's loads are issued before the
+      // current chunk is computed, so P to 2P units stay in flight.
+      for (int v = run.v0; v < run.v1; v += 2 * P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) load_unit(bufB[i], run, v + P + i);
+        compute_chunk(bufA, v);
+        if (v + P >= run.v1) break;
+#pragma unroll
+        for (int i = 0; i < P; ++i) load_unit(bufA[i], run, v + 2 * P + i);
+        compute_chunk(bufB, v + P);
       }
-    };
 
-    // Double-buffered chunks: the next chunk's loads are issued before the
-    // current chunk is computed, so P to 2P units stay in flight.
-    for (int v = run.v0; v < run.v1; v += 2 * P) {
-#pragma unroll
-      for (int i = 0; i < P; ++i) load_unit(bufB[i], run, v + P + i);
-      compute_chunk(bufA, v);
-      if (v + P >= run.v1) break;
-#pragma unroll
-      for (int i = 0; i < P; ++i) load_unit(bufA[i], run, v + 2 * P + i);
-      compute_chunk(bufB, v + P);
+      const long long next = args.prob[run.p].u_begin + run.v1;
+      if (next >= u1) break;
+      run = make_run(next);
     }
-
-    const long long next = args.prob[run.p].u_begin + run.v1;
-    if (next >= u1) break;
-    run = make_run(next);
   }
-  if (fin_p0 >= 0) finalize_block<NBW>(args, args.prob[fin_p0], fin_sb0, lane, lg, c16, M, Mr);
-  if (fin_p1 >= 0) finalize_block<NBW>(args, args.prob[fin_p1], fin_sb1, lane, lg, c16, M, Mr);
+
+  // ---- hand-off of the cut super-blocks (after every wave's stream) ----
+  lds_barrier();  // every wave's LDS parts are in place
+  if (!active) return;
+  const int b = blockIdx.x;
+  const long long W0 = wave_first_unit(b * WAVES, U, NW);
+  const long long W1 = wave_first_unit(min((b + 1) * WAVES, NW), U, NW);
+  // A wave leads the cut super-blocks that it is the workgroup's first wave
+  // to overlap: the one holding its first unit (unless an earlier wave of the
+  // workgroup overlaps it too) and the one holding its last unit.
+  for (int k = 0; k < 2; ++k) {
+    const long long u = k == 0 ? u0 : u1 - 1;
+    const int p = problem_of(u);
+    const StreamKProblem& pr = args.prob[p];
+    const int G = uniform(pr.G);
+    const int sb = uniform(static_cast<int>((u - pr.u_begin) / G));
+    const long long s0 = pr.u_begin + static_cast<long long>(sb) * G;
+    const long long s1 = s0 + G;
+    if (k == 1 && s0 <= u0) break;             // the run's last super-block is its first
+    if (k == 0 && s0 < u0 && wave > 0) continue;  // led by an earlier wave of the workgroup
+    if (s0 >= u0 && s1 <= u1) continue;        // whole: stored during the stream
+    // Level 1: the parts of this workgroup's waves, in wave order.
+    float sum[NBW][4];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
+    const int vlast = unit_owner((s1 < W1 ? s1 : W1) - 1, U, NW);
+    for (int v = wg; v <= vlast; ++v) {
+      const float* part = lparts + ((v - b * WAVES) * 2 + (wave_first_unit(v, U, NW) >= s0 ? 0 : 1)) *
+                                       NBW * Mr * 16;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum[j][r] += part[part_index<NBW>(j, 4 * lg + r, c16, Mr)];
+    }
+    if (s0 >= W0 && s1 <= W1) {
+      store_block<NBW>(pr, sb, sum, lg, c16, M);  // the workgroup owns it whole
+    } else if (publish_wg_part<NBW, WAVES>(args, pr, b, W0, s0, s1, sb, lane, lg, c16, Mr, sum)) {
+      finalize_block<NBW, WAVES>(args, pr, s0, s1, sb, lane, lg, c16, M, Mr);  // level 2
+    }
+  }
 }
 
 // =============================================================== launchers
@@ -668,6 +727,11 @@ hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t ld
   }
 }
 
+// LDS for the waves' parts of cut super-blocks: [waves][2][nbw][min(M,16)][16] fp32.
+size_t streamk_lds_part_bytes(int M, int nbw) {
+  return static_cast<size_t>(W4A16_STREAMK_WAVES) * 2 * nbw * (M < 16 ? M : 16) * 16 * sizeof(float);
+}
+
 // Units of the problems with NBW column blocks per super-block, and the grid:
 // fills sk (units, nwaves, problem offsets) and returns the workgroup count.
 int plan_streamk(StreamKArgs& sk, int nbw) {
@@ -757,10 +821,16 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
     }
     if (elems > need) need = elems;
   }
-  const size_t lds = static_cast<size_t>(need) * 2;
-  if (lds <= kStreamKLdsBudget) return launch_streamk_x<true>(sk, group, wgs, lds, stream);
+  // The waves' parts (level 1 of the hand-off) follow the staged activations.
+  const size_t x_bytes = (static_cast<size_t>(need) * 2 + 15) / 16 * 16;
+  const size_t lds = x_bytes + streamk_lds_part_bytes(M, 1);
+  if (lds <= kStreamKLdsBudget) {
+    sk.lds_part_off = static_cast<int>(x_bytes / 4);
+    return launch_streamk_x<true>(sk, group, wgs, lds, stream);
+  }
   wgs = plan_streamk(sk, kStreamKWideBlocks);
-  return launch_streamk_x<false>(sk, group, wgs, 0, stream);
+  sk.lds_part_off = 0;
+  return launch_streamk_x<false>(sk, group, wgs, streamk_lds_part_bytes(M, kStreamKWideBlocks), stream);
 }
 
 int choose_path(int M, int N, int K, int group) {
