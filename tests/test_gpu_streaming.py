@@ -113,9 +113,53 @@ def test_layer_set_grouped_full(M, layer):
             r = tolerance_ratio(yb, oracle.gemm(x, q, s, synth.GROUP, threads=synth.default_threads()))
             log(f"grouped M={M} {p.name} rep {rep}: ratio {r:.4f}")
             assert r <= 1.0
-    # counters are back to zero
-    ncount = w4.w4a16_workspace_bytes(0, sum(p.N for p in probs)) // 4
-    assert int(ws[:ncount].abs().sum().item()) == 0
+    assert _handoff_state_clean(ws, M, sum(p.N for p in probs))
+
+
+def _handoff_state_clean(ws, M, total_columns):
+    """True when the workspace's counters and swap slots (the regions that
+    must be zero between calls) are zero. Region sizes as the library lays
+    them out: counters, then one slot per output value of every super-block
+    (column blocks plus 8 problems x 5 blocks of slack) for min(M, 16) rows."""
+    import w4a16_weight_only_gemm_amd as w4
+    ncount = w4.w4a16_workspace_bytes(0, total_columns)
+    nslot = (((total_columns + 15) // 16 + 40) * 16 * min(M, 16) * 4 + 255) // 256 * 256
+    return int(ws[:(ncount + nslot) // 4].abs().sum().item()) == 0
+
+
+# Narrow, deep problems: super-blocks spread over three or more workgroups
+# (the counted hand-off), several problems in one launch; the last case also
+# has super-blocks shared by exactly two workgroups (the swap) at M = 1.
+DEEP = [[(16, 8192, 32)], [(48, 16384, 64)], [(64, 8192, 32), (200, 4096, 32)],
+        [(16, 2048, 32), (40, 8192, 32), (24, 1024, 32)], [(16, 16384, 32), (6144, 2048, 32)]]
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("case", list(enumerate(DEEP)), ids=lambda c: str(c[0]))
+def test_deep_problems_handoff(case, M):
+    import torch
+    import w4a16_weight_only_gemm_amd as w4
+    cid, shapes = case
+    g = shapes[0][2]
+    data = [_inputs(60 + 4 * cid + i, M, N, K, g) for i, (N, K, _) in enumerate(shapes)]
+    probs = [Problem(x, q, s, g) for (x, q, s) in data]
+    ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in probs]
+    total = sum(p.N for p in probs)
+    ws = workspace(M, total)
+    entries = [(p.x, p.qw, p.sp, y, p.N, p.K) for p, y in zip(probs, ys)]
+    log(f"deep problems {shapes} M={M}")
+    first = None
+    for rep in range(3):
+        w4.w4a16_gemm_grouped(entries, M, g, ws)
+        torch.cuda.synchronize()
+        outs = [y.view(torch.int16).cpu().numpy().view(np.uint16).copy() for y in ys]
+        assert _handoff_state_clean(ws, M, total)
+        if first is None:
+            first = outs
+            for (x, q, s), yb in zip(data, outs):
+                assert tolerance_ratio(yb, oracle.gemm(x, q, s, g, threads=synth.default_threads())) <= 1.0
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, outs))
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
@@ -125,6 +169,7 @@ def test_streaming_deterministic(M):
     ws = workspace(M, 5120)
     a, b = run_ws(prob, ws), run_ws(prob, ws)
     assert np.array_equal(a, b)
+    assert _handoff_state_clean(ws, M, 5120)
     assert tolerance_ratio(a, oracle.gemm(x, q, s, 128, threads=synth.default_threads())) <= 1.0
 
 

@@ -8,10 +8,12 @@ the invariants its correctness rests on, over many shapes and grid sizes:
   stream, or cut, in which case the waves keep their parts in LDS slots
   (wave, slot) that are distinct, the workgroup's leading wave sums exactly
   the slots written for that super-block, and either stores the result (the
-  workgroup holds it whole) or publishes one part per workgroup in distinct
-  workspace slots (workgroup, slot), with a counter that reaches exactly the
-  number of those parts, so exactly one workgroup finalizes it and it finds
-  every part;
+  workgroup holds it whole) or hands one part per workgroup on: when exactly
+  two workgroups share it, both swap their parts into the super-block's own
+  slots (so each slot sees exactly two exchanges); otherwise it publishes the
+  part in distinct workspace slots (workgroup, slot), with a counter that
+  reaches exactly the number of those parts, so exactly one workgroup
+  finalizes it and it finds every part;
 * every weight, scale, activation, output, partial, counter and LDS index the
   kernel forms lies inside its buffer.
 
@@ -106,7 +108,10 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     part_floats = nbw * Mr * 16
     total_sbs = sum(p["NSB"] for p in table)
     assert total_sbs <= 8 + total_cbs          # counters the host reserves
-    ws_part_floats = max(MAX_WAVES * 2, WIDE_MAX_WAVES * 2 * WIDE) * Mr * 16
+    ws_part_floats = max(MAX_WAVES // WAVES * 2, WIDE_MAX_WAVES // WAVES * 2 * WIDE) * Mr * 16
+    total_cols = sum(N for (N, K) in problems)
+    slot_values = ((total_cols + 15) // 16 + 8 * (1 + WIDE)) * 16 * Mr
+    swaps = {}
 
     def sb_of(u):
         pr = table[problem_of(table, u)]
@@ -199,12 +204,19 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                 if s0 >= W0 and s1 <= W1:
                     emitted[gsb] += 1
                     continue
+                nseg = wg_of(s1 - 1) - wg_of(s0) + 1
+                assert nseg >= 2
+                if nseg == 2:
+                    # swap: this super-block's slots, inside the slot region
+                    assert (gsb + 1) * part_floats <= slot_values
+                    swaps[gsb] = swaps.get(gsb, 0) + 1
+                    if swaps[gsb] == 2:
+                        emitted[gsb] += 1
+                    continue
                 slot = 0 if W0 >= s0 else 1
                 assert (b, slot) not in ws_parts
                 ws_parts[(b, slot)] = gsb
                 assert ((b * 2 + slot) + 1) * part_floats <= ws_part_floats
-                nseg = wg_of(s1 - 1) - wg_of(s0) + 1
-                assert nseg >= 2
                 nseg_of[gsb] = nseg
                 counters[gsb] += 1
                 if counters[gsb] == nseg:
@@ -214,6 +226,7 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                         assert ws_parts.get((c, cs)) == gsb, (c, cs, gsb)
         assert read == set(lds_parts), (b, set(lds_parts) - read)
     assert len(covered) == U and sorted(covered) == list(range(U))
+    assert all(n == 2 for n in swaps.values())
     for gsb in range(total_sbs):
         assert emitted[gsb] == 1, gsb
         if gsb in nseg_of:
@@ -221,7 +234,8 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     # every column block is in exactly one super-block
     for pr in table:
         assert pr["NSB"] * nbw >= pr["NCB"] > (pr["NSB"] - 1) * nbw
-    return dict(U=U, NW=NW, wgs=wgs, lds=lds, xlds=xlds, nbw=nbw)
+    return dict(U=U, NW=NW, wgs=wgs, lds=lds, xlds=xlds, nbw=nbw, swapped=len(swaps),
+                counted=len(nseg_of))
 
 
 LAYER = [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]
@@ -265,3 +279,13 @@ def test_small_and_ragged(case):
 def test_grid_sizes(cus, wg):
     simulate(LAYER[:2], 1, 128, cus=cus, wg_per_cu=wg)
     simulate([(40, 256)], 4, 64, cus=cus, wg_per_cu=wg)
+
+
+def test_both_cross_workgroup_forms_occur():
+    """The layer set takes the two-workgroup swap; a narrow, deep problem (one
+    column block, many groups) has super-blocks spread over three or more
+    workgroups and takes the counted form."""
+    info = simulate(LAYER, 1, 128)
+    assert info["swapped"] > 0 and info["counted"] == 0
+    info = simulate([(16, 8192)], 1, 32)
+    assert info["counted"] > 0

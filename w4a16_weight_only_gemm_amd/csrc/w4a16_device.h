@@ -88,4 +88,43 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// A lane permutation within rows of 16 lanes whose sources all exist.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                     true));
+}
+
+// -136 times the sum of the 8 bf16 values of a 16-byte piece, in fp32: four
+// bf16 dot products against the pair (-136, -136). Each product is exact in
+// fp32 (8-bit by 8-bit significands); only the additions round.
+__device__ __forceinline__ float neg136_sum8(u32x4 d) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 k = __builtin_bit_cast(bf16x2, kBiasPair);
+  // Elements are copied to scalars first: this compiler's __builtin_bit_cast
+  // of a vector-element expression (d[1]) reads the vector's first element.
+  const uint32_t e0 = d[0], e1 = d[1], e2 = d[2], e3 = d[3];
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e0), k, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e1), k, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e2), k, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, e3), k, s, false);
+}
+
+// Sum over the aligned group of LPG consecutive lanes containing this lane,
+// returned in every lane of the group (butterfly within quads, half rows,
+// rows of 16 lanes and pairs of rows). Each step adds two values in an order
+// that does not matter (a + b = b + a), so every lane gets the same bits.
+// All LPG lanes of the group must be active.
+template <int LPG>
+__device__ __forceinline__ float group_lane_sum(float v) {
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16 || LPG == 32, "group of 32, 64, 128 or 256");
+  v += dpp_f32<0xB1>(v);                           // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);                           // quad_perm [2,3,0,1]
+  if constexpr (LPG >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if constexpr (LPG >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if constexpr (LPG >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
 }  // namespace w4a16_internal

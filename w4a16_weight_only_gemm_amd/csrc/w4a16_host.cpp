@@ -124,6 +124,7 @@ size_t w4a16_workspace_bytes(int M, long long total_columns) {
     return w4a16_internal::large_streamk_counter_bytes(M, total_columns) +
            w4a16_internal::large_streamk_part_bytes(M);
   return w4a16_internal::streamk_counter_bytes(total_columns) +
+         w4a16_internal::streamk_slot_bytes(M, total_columns) +
          w4a16_internal::streamk_part_bytes(M);
 }
 
@@ -174,8 +175,10 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
         ws + w4a16_internal::large_streamk_counter_bytes(M, columns));
     err = w4a16_internal::launch_large_streamk(probs, count, M, group, part, counters, stream);
   } else {
-    float* part = reinterpret_cast<float*>(ws + w4a16_internal::streamk_counter_bytes(columns));
-    err = w4a16_internal::launch_streamk(probs, count, M, group, part, counters, stream);
+    char* slots = ws + w4a16_internal::streamk_counter_bytes(columns);
+    float* part = reinterpret_cast<float*>(slots + w4a16_internal::streamk_slot_bytes(M, columns));
+    err = w4a16_internal::launch_streamk(probs, count, M, group, part,
+                                         reinterpret_cast<uint32_t*>(slots), counters, stream);
   }
   return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
@@ -211,11 +214,20 @@ size_t streamk_counter_bytes(long long total_columns) {
   return static_cast<size_t>((ints * 4 + 255) / 256 * 256);
 }
 
+size_t streamk_slot_bytes(int M, long long total_columns) {
+  const int rows = M < 16 ? M : 16;
+  // super-blocks x NBW column blocks <= column blocks + problems x NBW
+  const long long blocks = (total_columns + 15) / 16 + kMaxProblems * (1 + kStreamKWideBlocks);
+  return static_cast<size_t>((blocks * 16 * rows * 4 + 255) / 256 * 256);
+}
+
 size_t streamk_part_bytes(int M) {
   const int rows = M < 16 ? M : 16;
-  // the larger of the two layouts: narrow units (one block) or wide ones
-  const size_t narrow = static_cast<size_t>(kStreamKMaxWaves) * 2;
-  const size_t wide = static_cast<size_t>(kStreamKWideMaxWaves) * 2 * kStreamKWideBlocks;
+  // per workgroup, the larger of the two layouts: narrow units (one block) or
+  // wide ones
+  const size_t narrow = static_cast<size_t>(kStreamKMaxWaves / kStreamKWaves) * 2;
+  const size_t wide =
+      static_cast<size_t>(kStreamKWideMaxWaves / kStreamKWaves) * 2 * kStreamKWideBlocks;
   return (narrow > wide ? narrow : wide) * rows * 16 * sizeof(float);
 }
 

@@ -24,6 +24,7 @@ bool large_supported(int group);
 
 // ---- stream-K (persistent, several problems per launch, M <= 16) ----
 constexpr int kMaxProblems = 8;
+constexpr int kStreamKWaves = 8;                // waves per workgroup
 constexpr int kStreamKMaxWaves = 8192;          // grid never exceeds this many waves
 constexpr size_t kStreamKLdsBudget = 64 * 1024;  // staged activations per workgroup
 
@@ -47,6 +48,7 @@ struct StreamKArgs {
   long long units;          // total units over all problems
   int nwaves;               // waves that own units (<= units)
   float* part;              // [workgroups][2][NBW][min(M,16)][16] fp32 parts
+  uint32_t* slots;          // [super-blocks][NBW][min(M,16)][16] swap slots, zero between calls
   int* counters;            // one per super-block, zero between calls
   int lds_part_off;         // LDS offset (in 4-byte words) of the waves' parts
 };
@@ -57,13 +59,15 @@ struct StreamKArgs {
 constexpr int kStreamKWideBlocks = 4;
 constexpr int kStreamKWideMaxWaves = 4096;      // grid cap with wide units
 
-// Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints,
-// rounded up to 256 bytes), then the parts.
+// Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints),
+// then the swap slots (one value per output of every super-block), then the
+// per-workgroup parts, each region rounded up to 256 bytes.
 size_t streamk_counter_bytes(long long total_columns);
+size_t streamk_slot_bytes(int M, long long total_columns);
 size_t streamk_part_bytes(int M);
 
 hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
-                          int* counters, hipStream_t stream);
+                          uint32_t* slots, int* counters, hipStream_t stream);
 
 // ---- stream-K large-M path (tiles of 32, 64 or 128 rows x 256 columns) ----
 constexpr int kLargeMaxWorkgroups = 320;  // persistent grid never exceeds this

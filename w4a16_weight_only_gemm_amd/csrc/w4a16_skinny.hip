@@ -215,15 +215,22 @@ __device__ __forceinline__ int unit_owner(long long u, long long U, int NW) {
 //     run, 1 for the last); after the stream, one barrier, and the first wave
 //     of the workgroup that overlaps such a super-block sums the parts of the
 //     workgroup's waves in wave order;
-//  2. across workgroups: a super-block that extends past the workgroup's
-//     units is published as one part per workgroup through the workspace and
-//     counted by an atomic counter per super-block; the workgroup whose
-//     increment completes the count sums the parts in workgroup order.
-// Either way the summation order is fixed, so the result does not depend on
-// timing. Level 2 uses no device-wide fences (on this chip a device-scope
-// fence writes back and invalidates the whole L2, which costs more than the
-// GEMM itself). Every access that crosses workgroups is an agent-scope atomic,
-// coherent across the L2s of all XCDs:
+//  2. across workgroups, for a super-block that extends past the workgroup's
+//     units, one part per workgroup:
+//     a. shared by exactly two workgroups (the usual case: a workgroup's run
+//        is longer than a super-block): each swaps its part into the
+//        super-block's slots in the workspace with one atomic exchange per
+//        value; per value, the exchange that returns the other part finishes
+//        it (see swap_part). One memory round trip.
+//     b. shared by three or more: published through the workspace and counted
+//        by an atomic counter per super-block; the workgroup whose increment
+//        completes the count sums the parts in workgroup order.
+// The summation order is fixed (two addends sum the same in either order), so
+// the result does not depend on timing. Level 2 uses no device-wide fences (on
+// this chip a device-scope fence writes back and invalidates the whole L2,
+// which costs more than the GEMM itself). Every access that crosses
+// workgroups is an agent-scope atomic, coherent across the L2s of all XCDs.
+// In 2b:
 //   writer: atomic stores of the part; wait until they complete (vmcnt 0);
 //           atomic increment of the super-block's counter.
 //   reader: the wave whose increment completes the count reads every part
@@ -263,19 +270,60 @@ __device__ __forceinline__ int unit_wg(long long u, long long U, int NW) {
   return unit_owner(u, U, NW) / WAVES;
 }
 
-// Level 2, writer: publish workgroup b's part v of super-block sb (units
-// [s0, s1) of problem pr) and count it. Returns true when it was the last part
-// to arrive; the caller then finalizes the super-block. A workgroup's slot is
-// 0 for the super-block holding its first unit W0, 1 for the one holding its last.
-template <int NBW, int WAVES>
+// A part value as stored in a swap slot: its bit pattern XOR a signalling-NaN
+// pattern. Arithmetic never yields a signalling NaN, so a stored value is
+// never 0, and 0 marks an empty slot.
+constexpr uint32_t kSlotMask = 0x7FA5A5A5u;
+
+// Level 2a: finish super-block sb (shared by exactly two workgroups) with
+// this workgroup's part v. The slots of the super-block hold 0 between calls.
+// For each value, the two workgroups' exchanges are ordered by the atomic:
+// the first gets 0 back and is done; the second gets the first's part, adds
+// its own (the sum of two addends does not depend on their order), stores
+// the bf16 result and empties the slot. Rows at or past Mr are padding: their
+// lanes take no part.
+template <int NBW>
+__device__ __forceinline__ void swap_part(const StreamKArgs& args, const StreamKProblem& pr, int sb,
+                                          int lg, int c16, int M, int Mr, const float (&v)[NBW][4]) {
+  uint32_t* slots = args.slots + static_cast<size_t>(pr.sb_begin + sb) * NBW * Mr * 16;
+  uint32_t old[NBW][4];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      old[j][r] = 0;
+      const int m = 4 * lg + r;
+      if (m < Mr)
+        old[j][r] = __hip_atomic_exchange(slots + (j * Mr + m) * 16 + c16,
+                                          __builtin_bit_cast(uint32_t, v[j][r]) ^ kSlotMask,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int n = (sb * NBW + j) * 16 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r;
+      if (old[j][r] != 0) {
+        const float sum = v[j][r] + __builtin_bit_cast(float, old[j][r] ^ kSlotMask);
+        if (m < M && n < pr.N) to_global(pr.y)[static_cast<size_t>(m) * pr.N + n] = f32_to_bf16_bits(sum);
+        __hip_atomic_store(slots + (j * Mr + m) * 16 + c16, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// Level 2b, writer: publish workgroup b's part v of super-block sb in its
+// slot (0 for the super-block holding the workgroup's first unit, 1 for the
+// one holding its last) and count it; nseg workgroups share the super-block.
+// Returns true when it was the last part to arrive; the caller then finalizes
+// the super-block.
+template <int NBW>
 __device__ __forceinline__ bool publish_wg_part(const StreamKArgs& args, const StreamKProblem& pr,
-                                                int b, long long W0, long long s0, long long s1,
-                                                int sb, int lane, int lg, int c16, int Mr,
-                                                const float (&v)[NBW][4]) {
-  const long long U = args.units;
-  const int NW = args.nwaves;
-  const int nseg = unit_wg<WAVES>(s1 - 1, U, NW) - unit_wg<WAVES>(s0, U, NW) + 1;
-  const int slot = (W0 >= s0) ? 0 : 1;
+                                                int b, int slot, int nseg, int sb, int lane, int lg,
+                                                int c16, int Mr, const float (&v)[NBW][4]) {
   float* mine = args.part + (static_cast<size_t>(b) * 2 + slot) * NBW * Mr * 16;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -297,17 +345,13 @@ __device__ __forceinline__ bool publish_wg_part(const StreamKArgs& args, const S
   return last;
 }
 
-// Level 2, reader: sum the workgroup parts of super-block sb (units [s0, s1)
-// of problem pr) in workgroup order, store the bf16 results and reset its
-// counter for the next call.
-template <int NBW, int WAVES>
+// Level 2b, reader: sum the parts of workgroups bfirst..blast of super-block
+// sb (workgroup c's in slot slot_of(c)) in workgroup order, store the bf16
+// results and reset the super-block's counter for the next call.
+template <int NBW, typename SlotOf>
 __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const StreamKProblem& pr,
-                                               long long s0, long long s1, int sb, int lane,
-                                               int lg, int c16, int M, int Mr) {
-  const long long U = args.units;
-  const int NW = args.nwaves;
-  const int bfirst = unit_wg<WAVES>(s0, U, NW);
-  const int blast = unit_wg<WAVES>(s1 - 1, U, NW);
+                                               int bfirst, int blast, SlotOf slot_of, int sb,
+                                               int lane, int lg, int c16, int M, int Mr) {
   float sum[NBW][4];
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
@@ -315,9 +359,8 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
     for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
   // Two parts at a time, so their loads are all in flight together; the sum
   // runs in workgroup order.
-  auto load_part = [&](float (&v)[NBW][4], int b) {
-    const int slot = (wave_first_unit(b * WAVES, U, NW) >= s0) ? 0 : 1;
-    float* part = args.part + (static_cast<size_t>(b) * 2 + slot) * NBW * Mr * 16;
+  auto load_part = [&](float (&v)[NBW][4], int c) {
+    float* part = args.part + (static_cast<size_t>(c) * 2 + slot_of(c)) * NBW * Mr * 16;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
 #pragma unroll
@@ -326,19 +369,19 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
                                     __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  int b = bfirst;
-  for (; b + 1 <= blast; b += 2) {
+  int c = bfirst;
+  for (; c + 1 <= blast; c += 2) {
     float v0[NBW][4], v1[NBW][4];
-    load_part(v0, b);
-    load_part(v1, b + 1);
+    load_part(v0, c);
+    load_part(v1, c + 1);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sum[j][r] = (sum[j][r] + v0[j][r]) + v1[j][r];
   }
-  if (b <= blast) {
+  if (c <= blast) {
     float v0[NBW][4];
-    load_part(v0, b);
+    load_part(v0, c);
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
@@ -347,6 +390,21 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
   store_block<NBW>(pr, sb, sum, lg, c16, M);
   if (lane == 0)
     __hip_atomic_store(args.counters + pr.sb_begin + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Level 2 for a super-block that extends past workgroup b's part of the
+// sequence: workgroups bfirst..blast share it; slot_of(c) is workgroup c's slot.
+template <int NBW, typename SlotOf>
+__device__ __forceinline__ void hand_off_across(const StreamKArgs& args, const StreamKProblem& pr,
+                                                int b, int bfirst, int blast, SlotOf slot_of, int sb,
+                                                int lane, int lg, int c16, int M, int Mr,
+                                                const float (&v)[NBW][4]) {
+  if (blast - bfirst == 1) {
+    swap_part<NBW>(args, pr, sb, lg, c16, M, Mr, v);  // level 2a
+  } else if (publish_wg_part<NBW>(args, pr, b, slot_of(b), blast - bfirst + 1, sb, lane, lg, c16, Mr,
+                                  v)) {
+    finalize_block<NBW>(args, pr, bfirst, blast, slot_of, sb, lane, lg, c16, M, Mr);  // level 2b
+  }
 }
 
 // Loads of one unit for one lane: for each of its NBW column blocks the packed
@@ -443,7 +501,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   // Activations for the A operand. With XLDS the workgroup stages the x rows
   // (min(M,16) rows) of every problem its units touch into LDS once;
   // otherwise each lane reads them from global memory.
-  extern __shared__ uint32_t xlds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t xlds[];  // 16-byte aligned: read as 128-bit words
   int lds_base[kMaxProblems];
   int lds_stride[kMaxProblems];
 #pragma unroll
@@ -451,27 +509,58 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     lds_base[i] = 0;
     lds_stride[i] = 0;
   }
+  // With XLDS, LDS also holds per problem and group the bias term -136 *
+  // (sum of the group's activations) of each row, as [G][16 rows] fp32 (rows
+  // past Mr repeat row Mr - 1), after the activation rows: an MFMA chain
+  // started from it sums a * q with the codes' bias already removed.
+  int xs_base[kMaxProblems];
+#pragma unroll
+  for (int i = 0; i < kMaxProblems; ++i) xs_base[i] = 0;
+  float* const xsum = reinterpret_cast<float*>(xlds);
   if constexpr (XLDS) {
     const long long wu0 = wave_first_unit(blockIdx.x * WAVES, U, NW);
     const long long wu1 = wave_first_unit(min((blockIdx.x + 1) * WAVES, NW), U, NW);
-    int off = 0;  // in bf16 elements
     if (wu1 > wu0) {
       const int plo = problem_of(wu0), phi = problem_of(wu1 - 1);
+      int off = 0;  // in bf16 elements
+#pragma unroll
+      for (int i = 0; i < kMaxProblems; ++i) {
+        if (i >= plo && i <= phi) {
+          lds_base[i] = off;
+          lds_stride[i] = args.prob[i].K + 8;  // 16 bytes of padding per row against bank conflicts
+          off += Mr * lds_stride[i];
+        }
+      }
+      int xoff = off / 2;  // in 4-byte words; a multiple of 4
+#pragma unroll
+      for (int i = 0; i < kMaxProblems; ++i) {
+        if (i >= plo && i <= phi) {
+          xs_base[i] = xoff;
+          xoff += args.prob[i].G * 16;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < kMaxProblems; ++i) {
         if (i >= plo && i <= phi) {
           const StreamKProblem& pr = args.prob[i];
-          const int stride = pr.K + 8;  // 16 bytes of padding per row against bank conflicts
-          lds_base[i] = off;
-          lds_stride[i] = stride;
+          constexpr int LPG = GS / 8;  // 16-byte pieces per group
           const int chunks = pr.K / 8;
+          // Mr * chunks is a multiple of LPG and each pass starts at a
+          // multiple of 64: a group's pieces are in consecutive lanes of one
+          // pass, all active together.
           for (int e = threadIdx.x; e < Mr * chunks; e += 64 * WAVES) {
             const int row = e / chunks, c8 = e - row * chunks;
             const u32x4 d =
                 *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
-            *reinterpret_cast<u32x4*>(xlds + (off + row * stride + 8 * c8) / 2) = d;
+            *reinterpret_cast<u32x4*>(xlds + (lds_base[i] + row * lds_stride[i] + 8 * c8) / 2) = d;
+            const float bsum = group_lane_sum<LPG>(neg136_sum8(d));  // the group's first lane stores
+            if ((c8 % LPG) == 0) {
+              float* dst = xsum + xs_base[i] + (c8 / LPG) * 16;
+              dst[row] = bsum;
+              if (row == Mr - 1)
+                for (int m = Mr; m < 16; ++m) dst[m] = bsum;
+            }
           }
-          off += Mr * stride;
         }
       }
     }
@@ -497,16 +586,23 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
       const StreamKProblem& pr = args.prob[run.p];
       const int G = run.G;
       const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
+      const float* const xs = xsum + xs_base[run.p] + 4 * lg;  // with XLDS: this lane's rows of group 0
       int sb = uniform(run.v0 / G);
       int g = uniform(run.v0 - sb * G);
       int seg_g0 = g;  // first group of the current super-block segment
 
-      // Compute the units of one chunk (buf holds units v .. v+P-1).
+      // Compute the units of one chunk (buf holds units v .. v+P-1). Units
+      // past the run's end (clamped re-loads of its last unit) are computed
+      // too, with their contribution scaled by zero: every path then consumes
+      // every loaded register, so no load can still be pending when the
+      // buffer is reloaded, and the compiler's waits stay exact (a skipped
+      // unit would make it drain all loads before each reload).
       auto compute_chunk = [&](UnitLoads<WPL, NBW> (&buf)[P], int v) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
           const int vv = v + i;
-          if (vv < run.v1) {
+          const bool live = vv < run.v1;
+          {
             bf16x8 a[WPL];
             if constexpr (XLDS) {
               const uint32_t* xl = xlds + xbase + (g * GS) / 2;
@@ -518,8 +614,12 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
               for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
             }
             if constexpr (NBW == 1) {
-              const f32x4 acc = group_product<WPL>(buf[i].w[0], a, bias);
-              const float sc = fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[0] >> (16 * (c16 & 1))));
+              // from -136 * (row sums): sum of a * q (exact products)
+              f32x4 acc = *reinterpret_cast<const f32x4*>(xs + g * 16);
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[0].w[t]), acc);
+              const float sc =
+                  live ? fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[0] >> (16 * (c16 & 1)))) : 0.f;
 #pragma unroll
               for (int r = 0; r < 4; ++r) yacc[0][r] = __builtin_fmaf(sc, acc[r], yacc[0][r]);
             } else {
@@ -533,13 +633,13 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
 #pragma unroll
                 for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[j].w[t]), acc);
                 const float sc =
-                    fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[j] >> (16 * (c16 & 1))));
+                    live ? fp16_bits_to_f32(static_cast<uint16_t>(buf[i].s2[j] >> (16 * (c16 & 1)))) : 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yacc[j][r] = __builtin_fmaf(sc, acc[r], yacc[j][r]);
               }
             }
 
-            if (g == G - 1 || vv == run.v1 - 1) {
+            if (live && (g == G - 1 || vv == run.v1 - 1)) {
               // End of this wave's segment of super-block sb.
               if (seg_g0 == 0 && g == G - 1) {
                 // The whole super-block was ours: store the results. The wait
@@ -565,7 +665,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
               for (int j = 0; j < NBW; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
               seg_g0 = 0;
             }
-            if (++g == G) {
+            if (live && ++g == G) {
               g = 0;
               ++sb;
             }
@@ -574,12 +674,18 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
       };
 
       // Double-buffered chunks: the next chunk's loads are issued before the
-      // current chunk is computed, so P to 2P units stay in flight.
+      // current chunk is computed, so P to 2P units stay in flight. The
+      // compiled loop routes the early exit through its header, so the exit
+      // waits for the unused loads in flight: otherwise the header would have
+      // to drain every load before each reload.
       for (int v = run.v0; v < run.v1; v += 2 * P) {
 #pragma unroll
         for (int i = 0; i < P; ++i) load_unit(bufB[i], run, v + P + i);
         compute_chunk(bufA, v);
-        if (v + P >= run.v1) break;
+        if (v + P >= run.v1) {
+          wait_vmem_all();
+          break;
+        }
 #pragma unroll
         for (int i = 0; i < P; ++i) load_unit(bufA[i], run, v + 2 * P + i);
         compute_chunk(bufB, v + P);
@@ -628,8 +734,11 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     }
     if (s0 >= W0 && s1 <= W1) {
       store_block<NBW>(pr, sb, sum, lg, c16, M);  // the workgroup owns it whole
-    } else if (publish_wg_part<NBW, WAVES>(args, pr, b, W0, s0, s1, sb, lane, lg, c16, Mr, sum)) {
-      finalize_block<NBW, WAVES>(args, pr, s0, s1, sb, lane, lg, c16, M, Mr);  // level 2
+    } else {
+      // a workgroup's slot: 0 when the super-block holds its first unit
+      auto slot_of = [&](int c) { return wave_first_unit(c * WAVES, U, NW) >= s0 ? 0 : 1; };
+      hand_off_across<NBW>(args, pr, b, unit_wg<WAVES>(s0, U, NW), unit_wg<WAVES>(s1 - 1, U, NW),
+                           slot_of, sb, lane, lg, c16, M, Mr, sum);
     }
   }
 }
@@ -643,9 +752,6 @@ namespace {
 #endif
 #ifndef W4A16_SKINNY_PREFETCH
 #define W4A16_SKINNY_PREFETCH 4
-#endif
-#ifndef W4A16_STREAMK_WAVES
-#define W4A16_STREAMK_WAVES 8
 #endif
 #ifndef W4A16_STREAMK_PREFETCH
 #define W4A16_STREAMK_PREFETCH 4
@@ -702,7 +808,7 @@ constexpr int streamk_prefetch() {
 template <int GS, bool XLDS, int NBW>
 hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(
-      &streamk_kernel<GS, W4A16_STREAMK_WAVES, streamk_prefetch<NBW>(), XLDS, NBW>);
+      &streamk_kernel<GS, kStreamKWaves, streamk_prefetch<NBW>(), XLDS, NBW>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -710,7 +816,7 @@ hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStrea
   }
   StreamKArgs copy = sk;
   void* kargs[] = {&copy};
-  return hipLaunchKernel(fn, dim3(wgs), dim3(64 * W4A16_STREAMK_WAVES), kargs, lds, stream);
+  return hipLaunchKernel(fn, dim3(wgs), dim3(64 * kStreamKWaves), kargs, lds, stream);
 }
 
 // Activations staged in LDS: one column block per unit. Read by each wave:
@@ -729,7 +835,7 @@ hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t ld
 
 // LDS for the waves' parts of cut super-blocks: [waves][2][nbw][min(M,16)][16] fp32.
 size_t streamk_lds_part_bytes(int M, int nbw) {
-  return static_cast<size_t>(W4A16_STREAMK_WAVES) * 2 * nbw * (M < 16 ? M : 16) * 16 * sizeof(float);
+  return static_cast<size_t>(kStreamKWaves) * 2 * nbw * (M < 16 ? M : 16) * 16 * sizeof(float);
 }
 
 // Units of the problems with NBW column blocks per super-block, and the grid:
@@ -748,13 +854,13 @@ int plan_streamk(StreamKArgs& sk, int nbw) {
   sk.units = units;
   int wgs = device_cus() * (nbw == 1 ? W4A16_STREAMK_WG_PER_CU : W4A16_STREAMK_WIDE_WG_PER_CU);
   const int max_waves = nbw == 1 ? kStreamKMaxWaves : kStreamKWideMaxWaves;
-  if (wgs * W4A16_STREAMK_WAVES > max_waves) wgs = max_waves / W4A16_STREAMK_WAVES;
+  if (wgs * kStreamKWaves > max_waves) wgs = max_waves / kStreamKWaves;
   // Every counted wave must own at least one unit (NW <= units): the parts of
   // a super-block are then produced by consecutive non-empty waves.
-  long long nw = static_cast<long long>(wgs) * W4A16_STREAMK_WAVES;
+  long long nw = static_cast<long long>(wgs) * kStreamKWaves;
   if (nw > units) nw = units;
   sk.nwaves = static_cast<int>(nw);
-  return static_cast<int>((nw + W4A16_STREAMK_WAVES - 1) / W4A16_STREAMK_WAVES);
+  return static_cast<int>((nw + kStreamKWaves - 1) / kStreamKWaves);
 }
 
 }  // namespace
@@ -785,7 +891,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
-                          int* counters, hipStream_t stream) {
+                          uint32_t* slots, int* counters, hipStream_t stream) {
   if (count < 1 || count > kMaxProblems || M < 1 || M > 16) return hipErrorInvalidValue;
   StreamKArgs sk = {};
   for (int i = 0; i < count; ++i) {
@@ -797,32 +903,34 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
   sk.nprob = count;
   sk.M = M;
   sk.part = part;
+  sk.slots = slots;
   sk.counters = counters;
   // LDS for staged activations (one column block per unit): the most any
-  // workgroup needs (Mr rows of K + 8 of each problem its units touch).
-  // Beyond the budget, each wave reads activations itself and takes
-  // kStreamKWideBlocks column blocks per unit instead.
+  // workgroup needs (Mr rows of K + 8 and G x 16 group sums of each problem
+  // its units touch). Beyond the budget, each wave reads activations itself
+  // and takes kStreamKWideBlocks column blocks per unit instead.
   int wgs = plan_streamk(sk, 1);
   const long long units = sk.units;
   const long long nw = sk.nwaves;
   const int Mr = M < 16 ? M : 16;
   long long need = 0;
   for (int b = 0; b < wgs; ++b) {
-    const long long wb0 = static_cast<long long>(b) * W4A16_STREAMK_WAVES;
-    const long long wb1 = wb0 + W4A16_STREAMK_WAVES < nw ? wb0 + W4A16_STREAMK_WAVES : nw;
+    const long long wb0 = static_cast<long long>(b) * kStreamKWaves;
+    const long long wb1 = wb0 + kStreamKWaves < nw ? wb0 + kStreamKWaves : nw;
     const long long wu0 = units * wb0 / nw;
     const long long wu1 = units * wb1 / nw;
     if (wu1 <= wu0) continue;
-    long long elems = 0;
+    long long bytes = 0;  // activation rows and their group sums
     for (int i = 0; i < count; ++i) {
       const long long pb = sk.prob[i].u_begin;
       const long long pe = pb + static_cast<long long>(sk.prob[i].NSB) * sk.prob[i].G;
-      if (pe > wu0 && pb < wu1) elems += static_cast<long long>(Mr) * (sk.prob[i].K + 8);
+      if (pe > wu0 && pb < wu1)
+        bytes += static_cast<long long>(Mr) * (sk.prob[i].K + 8) * 2 + static_cast<long long>(sk.prob[i].G) * 16 * 4;
     }
-    if (elems > need) need = elems;
+    if (bytes > need) need = bytes;
   }
   // The waves' parts (level 1 of the hand-off) follow the staged activations.
-  const size_t x_bytes = (static_cast<size_t>(need) * 2 + 15) / 16 * 16;
+  const size_t x_bytes = (static_cast<size_t>(need) + 15) / 16 * 16;
   const size_t lds = x_bytes + streamk_lds_part_bytes(M, 1);
   if (lds <= kStreamKLdsBudget) {
     sk.lds_part_off = static_cast<int>(x_bytes / 4);
