@@ -114,12 +114,14 @@ int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* 
 /*
  * Workspace of the streaming entry points below, for M activation rows and
  * `total_columns` output columns (the sum of N over the problems of a call):
- * per-block (M <= 16) or per-tile (M > 16) counters followed by fp32 partial
- * sums: 2 MB at M = 1, 34 MB at M = 16, up to 84 MB for M > 64. Device memory owned
- * by the caller, 256-byte aligned, zero-filled once before its first use;
- * every call leaves the counters at zero again, so it is reused without
- * clearing. One workspace must not serve two calls that can run at the same
- * time. Returns 0 for M < 0 or total_columns < 0.
+ * for M <= 16, per-block counters, one swap slot per output value and fp32
+ * partial sums per workgroup; for M > 16, per-tile counters and partial sums.
+ * For 52,224 columns (one layer's four projections): 0.6 MB at M = 1, 10 MB
+ * at M = 16, 21 to 84 MB for M > 16. Device memory owned by the caller,
+ * 256-byte aligned, zero-filled once before its first use; every call leaves
+ * the counters and slots at zero again, so it is reused without clearing.
+ * One workspace must not serve two calls that can run at the same time.
+ * Returns 0 for M < 0 or total_columns < 0.
  */
 size_t w4a16_workspace_bytes(int M, long long total_columns);
 

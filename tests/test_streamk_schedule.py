@@ -38,7 +38,12 @@ def owner(u, U, NW):
     return ((u + 1) * NW - 1) // U
 
 
-WIDE = 4
+WIDE_MAX = 6
+
+
+def wide(group):
+    """Column blocks per unit when each wave reads its activations."""
+    return 3 if group == 256 else 6
 
 
 WIDE_WG_PER_CU = 1
@@ -53,7 +58,7 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     """The launcher's grid: (problem table, units, NW, workgroups, staged
     activation bytes, column blocks, nbw). With nbw None, the launcher's
     choice: 1 when the staged activations and the LDS parts fit the LDS
-    budget, WIDE otherwise (with WIDE_WG_PER_CU workgroups per compute unit)."""
+    budget, wide(group) otherwise (with WIDE_WG_PER_CU workgroups per compute unit)."""
     def grid(nbw):
         table, units, sbs, cbs = [], 0, 0, 0
         for (N, K) in problems:
@@ -78,12 +83,13 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
         wu0, wu1 = units * wb0 // nw, units * wb1 // nw
         if wu1 <= wu0:
             continue
-        e = sum(Mr * (p["K"] + 8) for p in table
+        # activation rows and their group sums (G x 16 fp32)
+        e = sum(Mr * (p["K"] + 8) * 2 + p["G"] * 64 for p in table
                 if p["u_begin"] + p["NSB"] * p["G"] > wu0 and p["u_begin"] < wu1)
         need = max(need, e)
-    x_bytes = (need * 2 + 15) // 16 * 16
+    x_bytes = (need + 15) // 16 * 16
     if nbw is None:
-        nbw = 1 if x_bytes + lds_part_bytes(M, 1) <= LDS_BUDGET else WIDE
+        nbw = 1 if x_bytes + lds_part_bytes(M, 1) <= LDS_BUDGET else wide(group)
     if nbw != 1:
         table, units, nw, wgs, cbs = grid(nbw)
     return table, units, nw, wgs, x_bytes, cbs, nbw
@@ -108,9 +114,9 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     part_floats = nbw * Mr * 16
     total_sbs = sum(p["NSB"] for p in table)
     assert total_sbs <= 8 + total_cbs          # counters the host reserves
-    ws_part_floats = max(MAX_WAVES // WAVES * 2, WIDE_MAX_WAVES // WAVES * 2 * WIDE) * Mr * 16
+    ws_part_floats = max(MAX_WAVES // WAVES * 2, WIDE_MAX_WAVES // WAVES * 2 * WIDE_MAX) * Mr * 16
     total_cols = sum(N for (N, K) in problems)
-    slot_values = ((total_cols + 15) // 16 + 8 * (1 + WIDE)) * 16 * Mr
+    slot_values = ((total_cols + 15) // 16 + 8 * (1 + WIDE_MAX)) * 16 * Mr
     swaps = {}
 
     def sb_of(u):
@@ -130,16 +136,24 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
     for b in range(wgs):
         W0 = first_unit(min(b * WAVES, NW), U, NW)
         W1 = first_unit(min((b + 1) * WAVES, NW), U, NW)
-        # LDS staging of the workgroup (problems touched by its waves)
+        # LDS staging of the workgroup (problems touched by its waves): the
+        # activation rows, then the group sums of each touched problem
+        xs_base = {}
         if xlds:
             off = 0
             if W1 > W0:
-                for i in range(problem_of(table, W0), problem_of(table, W1 - 1) + 1):
+                touched = range(problem_of(table, W0), problem_of(table, W1 - 1) + 1)
+                for i in touched:
                     stride = table[i]["K"] + 8
                     # last 16-byte write: row Mr-1, chunk K/8-1
                     last = off + (Mr - 1) * stride + 8 * (table[i]["K"] // 8 - 1) + 8
                     assert last * 2 <= x_bytes, (b, i)
                     off += Mr * stride
+                xoff = off // 2
+                for i in touched:
+                    xs_base[i] = xoff
+                    xoff += table[i]["G"] * 16
+                assert xoff * 4 <= x_bytes
         lds_parts = {}                      # (local wave, slot) -> super-block
         for wave in range(WAVES):
             wg = b * WAVES + wave
@@ -163,6 +177,8 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                     assert tile * 16 + 15 < pr["NCB"] * 16 * pr["G"]
                 row = min(15, M - 1)
                 assert row * pr["K"] + g * group + 3 * wpl * 8 + 8 * (wpl - 1) + 7 < M * pr["K"]
+                if xlds:  # this unit's group sums (rows 4 * lg .. + 3, lg <= 3)
+                    assert (xs_base[p] + g * 16 + 12 + 4) * 4 <= part_off
                 if seg_g0 is None:
                     seg_g0 = g
                 if g == pr["G"] - 1 or u == u1 - 1:
@@ -248,10 +264,10 @@ def test_layer_set_grouped(M):
     if M == 1:
         assert info["xlds"] and info["lds"] <= LDS_BUDGET and info["nbw"] == 1
     if M == 16:
-        assert not info["xlds"] and info["nbw"] == WIDE
+        assert not info["xlds"] and info["nbw"] == wide(128)
 
 
-@pytest.mark.parametrize("nbw", [1, WIDE])
+@pytest.mark.parametrize("nbw", [1, 3, 6])
 @pytest.mark.parametrize("case", [([(200, 384)], 16, 64), ([(33, 512)], 7, 128),
                                   ([(100, 64), (300, 128), (17, 96)], 9, 32), (LAYER[:2], 16, 128)])
 def test_forced_block_widths(case, nbw):

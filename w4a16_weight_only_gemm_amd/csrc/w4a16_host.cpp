@@ -217,7 +217,7 @@ size_t streamk_counter_bytes(long long total_columns) {
 size_t streamk_slot_bytes(int M, long long total_columns) {
   const int rows = M < 16 ? M : 16;
   // super-blocks x NBW column blocks <= column blocks + problems x NBW
-  const long long blocks = (total_columns + 15) / 16 + kMaxProblems * (1 + kStreamKWideBlocks);
+  const long long blocks = (total_columns + 15) / 16 + kMaxProblems * (1 + kStreamKWideMaxBlocks);
   return static_cast<size_t>((blocks * 16 * rows * 4 + 255) / 256 * 256);
 }
 
@@ -227,7 +227,7 @@ size_t streamk_part_bytes(int M) {
   // wide ones
   const size_t narrow = static_cast<size_t>(kStreamKMaxWaves / kStreamKWaves) * 2;
   const size_t wide =
-      static_cast<size_t>(kStreamKWideMaxWaves / kStreamKWaves) * 2 * kStreamKWideBlocks;
+      static_cast<size_t>(kStreamKWideMaxWaves / kStreamKWaves) * 2 * kStreamKWideMaxBlocks;
   return (narrow > wide ? narrow : wide) * rows * 16 * sizeof(float);
 }
 

@@ -54,9 +54,12 @@ struct StreamKArgs {
 };
 
 // Column blocks per stream-K unit: 1 when the activations are staged in LDS,
-// kStreamKWideBlocks when each wave reads them itself (then one activation
-// fragment serves that many weight tiles).
-constexpr int kStreamKWideBlocks = 4;
+// streamk_wide_blocks(group) when each wave reads them itself (then one
+// activation fragment serves that many weight tiles: the wider, the less
+// activation traffic per weight byte, up to what the registers hold without
+// spilling at two waves per SIMD).
+constexpr int streamk_wide_blocks(int group) { return group == 256 ? 3 : 6; }
+constexpr int kStreamKWideMaxBlocks = 6;
 constexpr int kStreamKWideMaxWaves = 4096;      // grid cap with wide units
 
 // Workspace layout: counters first (kMaxProblems + ceil(columns/16) ints),

@@ -820,15 +820,14 @@ hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStrea
 }
 
 // Activations staged in LDS: one column block per unit. Read by each wave:
-// kStreamKWideBlocks column blocks per unit.
+// streamk_wide_blocks(group) column blocks per unit.
 template <bool XLDS>
 hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t lds, hipStream_t s) {
-  constexpr int NBW = XLDS ? 1 : kStreamKWideBlocks;
   switch (group) {
-    case 32: return launch_streamk_t<32, XLDS, NBW>(sk, wgs, lds, s);
-    case 64: return launch_streamk_t<64, XLDS, NBW>(sk, wgs, lds, s);
-    case 128: return launch_streamk_t<128, XLDS, NBW>(sk, wgs, lds, s);
-    case 256: return launch_streamk_t<256, XLDS, NBW>(sk, wgs, lds, s);
+    case 32: return launch_streamk_t<32, XLDS, XLDS ? 1 : streamk_wide_blocks(32)>(sk, wgs, lds, s);
+    case 64: return launch_streamk_t<64, XLDS, XLDS ? 1 : streamk_wide_blocks(64)>(sk, wgs, lds, s);
+    case 128: return launch_streamk_t<128, XLDS, XLDS ? 1 : streamk_wide_blocks(128)>(sk, wgs, lds, s);
+    case 256: return launch_streamk_t<256, XLDS, XLDS ? 1 : streamk_wide_blocks(256)>(sk, wgs, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -908,7 +907,7 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
   // LDS for staged activations (one column block per unit): the most any
   // workgroup needs (Mr rows of K + 8 and G x 16 group sums of each problem
   // its units touch). Beyond the budget, each wave reads activations itself
-  // and takes kStreamKWideBlocks column blocks per unit instead.
+  // and takes streamk_wide_blocks(group) column blocks per unit instead.
   int wgs = plan_streamk(sk, 1);
   const long long units = sk.units;
   const long long nw = sk.nwaves;
@@ -936,9 +935,10 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
     sk.lds_part_off = static_cast<int>(x_bytes / 4);
     return launch_streamk_x<true>(sk, group, wgs, lds, stream);
   }
-  wgs = plan_streamk(sk, kStreamKWideBlocks);
+  const int nbw = streamk_wide_blocks(group);
+  wgs = plan_streamk(sk, nbw);
   sk.lds_part_off = 0;
-  return launch_streamk_x<false>(sk, group, wgs, streamk_lds_part_bytes(M, kStreamKWideBlocks), stream);
+  return launch_streamk_x<false>(sk, group, wgs, streamk_lds_part_bytes(M, nbw), stream);
 }
 
 int choose_path(int M, int N, int K, int group) {
