@@ -455,8 +455,15 @@ def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
                         if rc != 0:
                             raise RuntimeError(f"w4a16_gemm failed with status {rc}")
 
-        one_pass()
-        torch.cuda.synchronize()
+        # warm up for 300 ms (at least two passes): clocks reach their
+        # sustained level only after a few thousand launches
+        import time
+        t_end = time.time() + 0.3
+        n_warm = 0
+        while n_warm < 2 or time.time() < t_end:
+            one_pass()
+            n_warm += 1
+            torch.cuda.synchronize()
 
         def timed_passes():
             for _ in range(passes):
