@@ -50,6 +50,12 @@ def _load():
         lib.oracle_pack.argtypes = [vp, vp, vp, vp, c_int, c_int, c_int]
         lib.oracle_unpack.restype = c_int
         lib.oracle_unpack.argtypes = [vp, vp, c_int, c_int, c_int]
+        lib.oracle_quantize_rows.restype = c_int
+        lib.oracle_quantize_rows.argtypes = [vp, vp, vp, c_int, c_int]
+        lib.oracle_gemm_w4a8.restype = c_int
+        lib.oracle_gemm_w4a8.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int]
+        lib.oracle_arrange_xq.restype = c_int
+        lib.oracle_arrange_xq.argtypes = [vp, vp, vp, c_int, c_int, c_int]
         _lib = lib
     return _lib
 
@@ -118,3 +124,48 @@ def unpack(qweight: np.ndarray, N: int, K: int, group: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_unpack rejected the input")
     return q
+
+
+def quantize_rows(x_bf16: np.ndarray):
+    """W4A8 activation quantization (oracle.c): (xq int8 [M][K], sx float32 [M])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    xq = np.empty((M, K), dtype=np.int8)
+    sx = np.empty(M, dtype=np.float32)
+    rc = _load().oracle_quantize_rows(x.ctypes.data, xq.ctypes.data, sx.ctypes.data, M, K)
+    if rc != 0:
+        raise ValueError("oracle_quantize_rows rejected the input")
+    return xq, sx
+
+
+def gemm_w4a8(xq: np.ndarray, sx: np.ndarray, q: np.ndarray, s_fp16: np.ndarray,
+              group: int) -> np.ndarray:
+    """y[M][N] (float64) of the W4A8 product (oracle.c): exact integer sums per
+    group, scaled in double."""
+    xq = _c(xq, np.int8)
+    sx = _c(sx, np.float32)
+    q = _c(q, np.int8)
+    s = _c(s_fp16, np.uint16)
+    M, K = xq.shape
+    N = q.shape[0]
+    if q.shape != (N, K) or sx.shape != (M,) or s.shape != (N, K // group):
+        raise ValueError("shape mismatch")
+    y = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_w4a8(xq.ctypes.data, sx.ctypes.data, q.ctypes.data, s.ctypes.data,
+                                  y.ctypes.data, M, N, K, group)
+    if rc != 0:
+        raise ValueError("oracle_gemm_w4a8 rejected the input")
+    return y
+
+
+def arrange_xq(xq: np.ndarray, group: int):
+    """Device arrangement of quantized activations and their group sums
+    (oracle.c): (int8 [M][K], int32 [M][K/group])."""
+    xq = _c(xq, np.int8)
+    M, K = xq.shape
+    out = np.empty((M, K), dtype=np.int8)
+    xs = np.empty((M, K // group), dtype=np.int32)
+    rc = _load().oracle_arrange_xq(xq.ctypes.data, out.ctypes.data, xs.ctypes.data, M, K, group)
+    if rc != 0:
+        raise ValueError("oracle_arrange_xq rejected the input")
+    return out, xs

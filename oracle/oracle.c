@@ -212,3 +212,116 @@ int oracle_unpack(const uint32_t* qweight, int8_t* q, int N, int K, int group) {
   }
   return 0;
 }
+
+/* ---- W4A8: int8 activations (per-row scale) times int4 weights ---- */
+/*
+ * The step past the bend: once the rows' arithmetic is the bottleneck, only
+ * cheaper arithmetic raises the rate (ai.satyajit.si page, section "What one
+ * more stream costs on this model"). Here the activations are quantized to
+ * int8 with one scale per row, so that the products of codes are integers.
+ *
+ * Quantization of row m (a reading: the pages give no formula). All steps in
+ * IEEE binary32 with round to nearest even, in this order:
+ *   a      = max_k |x[m][k]|                       (exact: bf16 values)
+ *   a == 0: sx[m] = 0 and every xq[m][k] = 0
+ *   inv    = 127 / a                               (one rounding)
+ *   t      = x[m][k] * inv                         (one rounding)
+ *   xq     = nearest integer to t, ties to even, clamped to [-127, 127]
+ *   sx[m]  = a / 127                               (one rounding)
+ * GEMM: the integer sum per group is exact, the scaling is done in double:
+ *   acc[m][n][t] = sum_{k in group t} xq[m][k] * q[n][k]        (exact)
+ *   y[m][n]      = sx[m] * sum_t s[n][t] * acc[m][n][t]         (double, increasing t)
+ */
+
+/* Round a binary32 value to the nearest integer, ties to even. */
+static float oracle_rne_int(float t) {
+  const float f = floorf(t);
+  const float d = t - f; /* exact: t and f are close binary32 values */
+  if (d > 0.5f) return f + 1.0f;
+  if (d < 0.5f) return f;
+  return fmodf(f, 2.0f) == 0.0f ? f : f + 1.0f;
+}
+
+/*
+ * Quantize x[M][K] (bf16 bits) row by row: xq[M][K] int8 (natural k order)
+ * and sx[M] (binary32). Returns 0; 1 on invalid arguments (nothing written).
+ */
+int oracle_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, int M, int K) {
+  if (M < 0 || K < 0 || (M > 0 && K > 0 && (!x || !xq)) || (M > 0 && !sx)) return 1;
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* xm = x + (size_t)m * K;
+    float a = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const float v = fabsf((float)oracle_bf16_to_f64(xm[k]));
+      if (v > a) a = v;
+    }
+    if (a == 0.0f) {
+      sx[m] = 0.0f;
+      for (int k = 0; k < K; ++k) xq[(size_t)m * K + k] = 0;
+      continue;
+    }
+    volatile float inv = 127.0f / a;
+    for (int k = 0; k < K; ++k) {
+      volatile float t = (float)oracle_bf16_to_f64(xm[k]) * inv;
+      float r = oracle_rne_int(t);
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      xq[(size_t)m * K + k] = (int8_t)r;
+    }
+    volatile float s = a / 127.0f;
+    sx[m] = s;
+  }
+  return 0;
+}
+
+/*
+ * y[M][N] (double) = W4A8 product of xq[M][K] (int8), sx[M] (binary32),
+ * q[N][K] (int8 in -8..7) and s[N][K/group] (fp16 bits), as above.
+ * Returns 0; 1 on invalid arguments.
+ */
+int oracle_gemm_w4a8(const int8_t* xq, const float* sx, const int8_t* q, const uint16_t* s,
+                     double* y, int M, int N, int K, int group) {
+  if (M < 0 || N < 0 || K < 0 || group <= 0 || K % group != 0) return 1;
+  if (M == 0 || N == 0) return 0;
+  if (!y || !sx || (K > 0 && (!xq || !q || !s))) return 1;
+  const int G = K / group;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      double sum = 0.0;
+      for (int t = 0; t < G; ++t) {
+        long long acc = 0;
+        for (int k = t * group; k < (t + 1) * group; ++k)
+          acc += (long long)xq[(size_t)m * K + k] * (long long)q[(size_t)n * K + k];
+        sum += oracle_fp16_to_f64(s[(size_t)n * G + t]) * (double)acc;
+      }
+      y[(size_t)m * N + n] = (double)sx[m] * sum;
+    }
+  return 0;
+}
+
+/*
+ * Device arrangement of quantized activations (a reading, chosen to match
+ * the weights' stored words): row-major [M][K] int8, with each aligned block
+ * of 16 consecutive k stored in the order of the codes of two stored words,
+ * low nibbles then high nibbles: k offsets 0,4,1,5,2,6,3,7, 8,12,9,13,
+ * 10,14,11,15. Group sums xsum[M][K/group] (int32) of the codes.
+ */
+static int oracle_xq_offset(int j) {
+  static const int order[16] = {0, 4, 1, 5, 2, 6, 3, 7, 8, 12, 9, 13, 10, 14, 11, 15};
+  return order[j];
+}
+
+int oracle_arrange_xq(const int8_t* xq, int8_t* out, int* xsum, int M, int K, int group) {
+  if (M < 0 || K < 0 || K % 16 != 0 || group <= 0 || K % group != 0) return 1;
+  for (int m = 0; m < M; ++m) {
+    for (int b = 0; b < K / 16; ++b)
+      for (int j = 0; j < 16; ++j)
+        out[(size_t)m * K + 16 * b + j] = xq[(size_t)m * K + 16 * b + oracle_xq_offset(j)];
+    for (int t = 0; t < K / group; ++t) {
+      int acc = 0;
+      for (int k = t * group; k < (t + 1) * group; ++k) acc += xq[(size_t)m * K + k];
+      xsum[(size_t)m * (K / group) + t] = acc;
+    }
+  }
+  return 0;
+}
