@@ -165,6 +165,41 @@ typedef struct w4a16_problem {
 int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int group,
                        void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
 
+/*
+ * W4A8: the activations quantized to int8 with one scale per row, times the
+ * same packed 4-bit weights, on the int8 MFMA. Once the rows' arithmetic
+ * rather than the weight stream bounds a step, cheaper arithmetic is what
+ * raises the rate (ai.satyajit.si page, section "What one more stream costs
+ * on this model"); the int8 product does twice the multiply-adds per cycle
+ * of the bf16 one. Intended for large M (hundreds of rows and more); any
+ * M >= 1 is computed correctly.
+ *
+ * w4a8_quantize: x (device bf16 [M][K]) -> xq (device int8 [M][K]) and sx
+ * (device fp32 [M]). For row m, in fp32 with round to nearest even:
+ *   a = max_k |x[m][k]|,  sx[m] = a / 127,
+ *   xq[m][k] = x[m][k] * (127 / a) rounded to the nearest integer (ties to
+ *              even) and clamped to [-127, 127];  a row of zeros gives codes 0
+ *              and sx[m] = 0. Inputs must be finite.
+ * Arrangement of xq: row-major, each aligned block of 16 k stored in the
+ * order in which the MFMA consumes two packed weight words: byte j of block
+ * b holds the code of k = 16b + o[j], o = 0,4,1,5,2,6,3,7,8,12,9,13,10,14,11,15.
+ * Requires M >= 0, K >= 16, K % 16 == 0; every pointer a 16-byte aligned
+ * device address. M == 0 returns W4A16_OK and launches nothing.
+ */
+int w4a8_quantize(const void* x, void* xq, void* sx, int M, int K, struct ihipStream_t* stream);
+
+/*
+ * w4a8_gemm: y[m][n] = sx[m] * sum_t s[n][t] * sum_{k in group t} xq[m][k] * q[n][k],
+ * with xq and sx as w4a8_quantize writes them, qweight and scales as
+ * w4a16_pack writes them, the integer sums exact (int32), the scaling in fp32
+ * and y (device bf16 [M][N]) rounded to nearest even. group 64 or 128,
+ * K % group == 0, N >= 1; other shapes return W4A16_ERR_UNSUPPORTED. Every
+ * pointer a 16-byte aligned device address; y overlaps no input. Errors and
+ * asynchrony as for w4a16_gemm; no workspace.
+ */
+int w4a8_gemm(const void* xq, const void* sx, const void* qweight, const void* scales, void* y,
+              int M, int N, int K, int group, struct ihipStream_t* stream);
+
 /* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
  * host integers), or -1 for an unsupported shape. */
 int w4a16_select_path(int M, int N, int K, int group);

@@ -19,12 +19,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "w4a16.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w4a(?:16|8)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert len(names) >= 8, names
+    assert "w4a8_quantize" in names and "w4a8_gemm" in names
     lib = ctypes.CDLL(w4.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
@@ -166,3 +167,32 @@ def test_grouped_argument_checks_without_launch():
     assert st([ok], 4, 64, None, nb) == w4.W4A16_ERR_INVALID_ARG              # no workspace
     assert st([ok], 4, 64, A * 16, nb - 1) == w4.W4A16_ERR_INVALID_ARG        # too small
     assert st([ok], 4, 64, A * 16 + 16, nb) == w4.W4A16_ERR_MISALIGNED        # not 256-aligned
+
+
+def test_w4a8_argument_checks_without_launch():
+    q = w4.w4a8_quantize_status
+    assert q(A, A, A, 0, 256) == w4.W4A16_OK                                  # M == 0: no-op
+    assert q(None, None, None, 0, 256) == w4.W4A16_OK
+    assert q(A, A, A, -1, 256) == w4.W4A16_ERR_INVALID_ARG
+    assert q(A, A, A, 1, -16) == w4.W4A16_ERR_INVALID_ARG
+    assert q(None, A, A, 1, 256) == w4.W4A16_ERR_INVALID_ARG
+    assert q(A, A, None, 1, 256) == w4.W4A16_ERR_INVALID_ARG
+    assert q(A, A, A, 1, 200) == w4.W4A16_ERR_UNSUPPORTED                     # K % 16
+    assert q(A, A, A, 1, 0) == w4.W4A16_ERR_UNSUPPORTED
+    assert q(A + 2, A, A, 1, 256) == w4.W4A16_ERR_MISALIGNED
+    assert q(A, A + 8, A, 1, 256) == w4.W4A16_ERR_MISALIGNED
+    assert q(A, A, A + 4, 1, 256) == w4.W4A16_ERR_MISALIGNED
+    g = w4.w4a8_gemm_status
+    assert g(A, A, A, A, A, 0, 512, 256, 64) == w4.W4A16_OK                   # M == 0
+    assert g(A, A, A, A, A, -1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert g(A, None, A, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG   # null sx
+    assert g(A, A, A, A, None, 1, 512, 256, 64) == w4.W4A16_ERR_INVALID_ARG   # null y
+    for group in (32, 256, 48):
+        assert g(A, A, A, A, A, 1, 512, 1024, group) == w4.W4A16_ERR_UNSUPPORTED
+    assert g(A, A, A, A, A, 1, 512, 320, 128) == w4.W4A16_ERR_UNSUPPORTED     # K % group
+    assert g(A, A, A, A, A, 1, 0, 256, 64) == w4.W4A16_ERR_UNSUPPORTED
+    assert g(A, A, A, A, A, 1, 1 << 20, 1 << 14, 128) == w4.W4A16_ERR_UNSUPPORTED  # 8 GB of weights
+    for i in range(5):
+        args = [A] * 5
+        args[i] = A + 4
+        assert g(*args, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED, i

@@ -57,6 +57,8 @@ SIGNATURES = {
     "w4a16_gemm_ws": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
+    "w4a8_quantize": (_int, [_vp, _vp, _vp, _int, _int, _vp]),
+    "w4a8_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_version": (_int, []),
 }
@@ -230,3 +232,49 @@ def grouped_status(problems, M, group, workspace, workspace_bytes, stream=None) 
     arr = problems if isinstance(problems, ctypes.Array) else make_problems(problems)
     return int(_lib.w4a16_gemm_grouped(ctypes.cast(arr, ctypes.c_void_p), len(arr), M, group,
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def _check_sizes(**need):
+    """name=(tensor or address, bytes needed): size checks for torch tensors."""
+    if _torch is None:
+        return
+    for name, (t, nbytes) in need.items():
+        if isinstance(t, _torch.Tensor):
+            have = t.numel() * t.element_size()
+            if have < nbytes:
+                raise ValueError(f"{name} holds {have} bytes, needs {nbytes}")
+
+
+def w4a8_quantize(x, xq, sx, M: int, K: int, stream=None) -> None:
+    """Row-wise int8 quantization of bf16 x[M][K] on the GPU: codes xq[M][K]
+    (int8, arranged for the int8 MFMA) and row scales sx[M] (fp32)."""
+    if _torch is not None and isinstance(x, _torch.Tensor) and x.dtype != _torch.bfloat16:
+        raise TypeError("x must be torch.bfloat16")
+    _check_sizes(x=(x, 2 * M * K), xq=(xq, M * K), sx=(sx, 4 * M))
+    rc = _lib.w4a8_quantize(_ptr(x), _ptr(xq), _ptr(sx), M, K, _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a8_quantize")
+
+
+def w4a8_gemm(xq, sx, qweight, scales, y, M: int, N: int, K: int, group: int,
+              stream=None) -> None:
+    """y[M][N] (bf16) = W4A8 product of the codes and row scales written by
+    w4a8_quantize and the packed weights written by w4a16_pack."""
+    if group > 0 and K % group == 0:
+        _check_sizes(xq=(xq, M * K), sx=(sx, 4 * M), y=(y, 2 * M * N),
+                     qweight=(qweight, N * K // 2), scales=(scales, 2 * N * (K // group)))
+    rc = _lib.w4a8_gemm(_ptr(xq), _ptr(sx), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
+                        _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a8_gemm")
+
+
+def w4a8_quantize_status(x, xq, sx, M, K, stream=None) -> int:
+    """Raw status of w4a8_quantize, without raising (for tests of the error paths)."""
+    return int(_lib.w4a8_quantize(_ptr(x), _ptr(xq), _ptr(sx), M, K, _stream(stream)))
+
+
+def w4a8_gemm_status(xq, sx, qweight, scales, y, M, N, K, group, stream=None) -> int:
+    """Raw status of w4a8_gemm, without raising (for tests of the error paths)."""
+    return int(_lib.w4a8_gemm(_ptr(xq), _ptr(sx), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K,
+                              group, _stream(stream)))

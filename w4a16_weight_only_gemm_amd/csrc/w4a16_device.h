@@ -127,4 +127,19 @@ __device__ __forceinline__ float group_lane_sum(float v) {
   return v;
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets at or beyond
+// `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Workgroup b of `total` in XCD-grouped order: XCD x (= b % 8) owns a
+// contiguous range of the indices.
+__device__ __forceinline__ int xcd_grouped(int b, int total) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
 }  // namespace w4a16_internal

@@ -8,6 +8,7 @@
 
 #include "../../include/w4a16.h"
 #include "w4a16_launch.h"
+#include "w4a8_launch.h"
 
 namespace {
 
@@ -190,6 +191,44 @@ int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* 
   if (M == 0) return W4A16_OK;
   if (!x || !qweight || !scales || !y) return W4A16_ERR_INVALID_ARG;
   return w4a16_gemm_grouped(&p, 1, M, group, workspace, workspace_bytes, stream);
+}
+
+int w4a8_quantize(const void* x, void* xq, void* sx, int M, int K, hipStream_t stream) {
+  if (M < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
+  if (M == 0) return W4A16_OK;
+  if (!x || !xq || !sx) return W4A16_ERR_INVALID_ARG;
+  if (K < 16 || K % 16 != 0) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return W4A16_ERR_MISALIGNED;
+  const hipError_t err = w4a16_internal::launch_w4a8_quantize(
+      static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), static_cast<float*>(sx), M, K,
+      stream);
+  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+int w4a8_gemm(const void* xq, const void* sx, const void* qweight, const void* scales, void* y,
+              int M, int N, int K, int group, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
+  if (M == 0) return W4A16_OK;
+  if (!xq || !sx || !qweight || !scales || !y) return W4A16_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || (group != 64 && group != 128) || K % group != 0)
+    return W4A16_ERR_UNSUPPORTED;
+  // packed weights and scales are addressed with 32-bit buffer offsets
+  if (w4a16_qweight_bytes(N, K) > 0xFFFFFFF0u) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned16(xq) || !aligned16(sx) || !aligned16(qweight) || !aligned16(scales) ||
+      !aligned16(y))
+    return W4A16_ERR_MISALIGNED;
+  w4a16_internal::W4A8Args a;
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.sx = static_cast<const float*>(sx);
+  a.qweight = static_cast<const uint32_t*>(qweight);
+  a.scales = static_cast<const uint16_t*>(scales);
+  a.y = static_cast<uint16_t*>(y);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  const hipError_t err = w4a16_internal::launch_w4a8_gemm(a, stream);
+  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
 const char* w4a16_status_string(int status) {
