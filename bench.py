@@ -15,8 +15,10 @@ their sustained level before timing.
 
 The headline line reports the decode layer set (M = 1) in HBM TB/s over
 algorithmic bytes (packed weights + scales + activations + outputs, counted once
-per call). Extra entries report the verify block (M = 16, TB/s) and the batched
-step (M = 1024, TFLOP/s).
+per call). Extra entries report the verify block (M = 16, TB/s), the batched
+step (M = 1024, TFLOP/s) and the same batched step through the W4A8 entry
+points (each projection's activations quantized to int8, then the int8 MFMA
+GEMM; TOP/s against the int8 MFMA peak).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--graph]
 """
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, vendor figure
+INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, vendor figure
 GROUP = 128
 
 
@@ -318,6 +321,67 @@ def check_parity(wl: Workload, layer: int, cols: int = 64):
     return worst
 
 
+def time_w4a8(wl: Workload, steps: int, warmup: int):
+    """The W4A8 step at wl.M rows: for each projection, w4a8_quantize of its
+    activations, then w4a8_gemm. Returns (ms per step, ms per gate_up GEMM
+    launch alone, sampled parity ratio against the oracle's W4A8 chain)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    cur = torch.cuda.current_stream()
+    stream = cur.cuda_stream
+    M = wl.M
+    L = len(wl.args)
+    q8 = []
+    for layer in range(L):
+        la = []
+        for pi, p in enumerate(wl.store.projs):
+            xq = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
+            sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+            x, qw, sp, y = wl.args[layer][pi][:4]
+            la.append(((x, xq.data_ptr(), sx.data_ptr(), M, p.K),
+                       (xq.data_ptr(), sx.data_ptr(), qw, sp, y, M, p.N, p.K, GROUP), xq, sx))
+        q8.append(la)
+
+    def run(first, count, only=None):
+        for s_ in range(first, first + count):
+            for pi, (qa, ga, _, _) in enumerate(q8[s_ % L]):
+                if only is not None and pi != only:
+                    continue
+                if only is None:
+                    rc = lib.w4a8_quantize(*qa, stream)
+                    if rc != 0:
+                        raise RuntimeError(f"w4a8_quantize failed with status {rc}")
+                rc = lib.w4a8_gemm(*ga, stream)
+                if rc != 0:
+                    raise RuntimeError(f"w4a8_gemm failed with status {rc}")
+
+    run(0, warmup)
+    torch.cuda.synchronize()
+    step_ms = timed(lambda: run(0, steps), cur) / steps
+    dom_ms = timed(lambda: run(0, steps, only=2), cur) / steps
+    run(0, L)  # every layer's outputs from the full chain
+    torch.cuda.synchronize()
+    worst = 0.0
+    for pi, p in enumerate(wl.store.projs):
+        rng = np.random.default_rng(10 + pi)
+        c = np.sort(rng.choice(p.N, 64, replace=False))
+        rows = min(M, 16)
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, pi), p.N, p.K)[c]
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, pi), p.N, p.K // GROUP)[c]
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 0, pi, M), M, p.K, rows=(0, rows))
+        xq, sx = oracle.quantize_rows(x)
+        ref = oracle.gemm_w4a8(xq, sx, q, s, GROUP)
+        y = wl.y[0][pi][:rows].view(torch.int16).cpu().numpy().view(np.uint16)[:, c]
+        yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(yv - ref) / (1e-2 * (1 + np.abs(ref))))))
+    return step_ms, dom_ms, worst
+
+
 def cpu_baseline(seconds_target: float = 15.0):
     """The oracle, as it stands, on the host cores: decode layer sets (M = 1),
     projection after projection, layer after layer, until about
@@ -550,6 +614,8 @@ def main(argv=None):
                     help="replay the steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--m-list", default="1,16,1024")
+    ap.add_argument("--w4a8-m-list", default="1024",
+                    help="row counts of the W4A8 batched step (empty: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC byte calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -636,6 +702,25 @@ def main(argv=None):
             e["roofline"] = {"bound": "hbm", "achieved": e["tbps"] * 1e3, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": e["tbps"] * 1e3 / HBM_PEAK_GBS}
         extra.append(e)
+    for M in [int(v) for v in args.w4a8_m_list.split(",") if v]:
+        wl8 = Workload(store, M, grouped=False)
+        ms8, dom8, par8 = time_w4a8(wl8, args.steps, min(args.warmup, 1000))
+        f = wl8.step_flops()
+        e = {"path": "w4a8", "M": M, "ms_per_step": ms8, "tops": f / (ms8 * 1e-3) / 1e12,
+             "positions_per_s": M / (ms8 * 1e-3), "parity_ratio": par8,
+             "note": "per projection: w4a8_quantize of bf16 activations, then w4a8_gemm; "
+                     "parity against the oracle's quantize + W4A8 GEMM"}
+        gflops = flops(M, gu.N, gu.K)
+        e["roofline"] = {"bound": "mfma", "achieved": gflops / (dom8 * 1e-3) / 1e12,
+                         "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                         "frac": gflops / (dom8 * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                         "kernel": "w4a8_gemm, gate_up projection (5120x34816) at M=%d" % M}
+        if M in results:
+            e["speedup_vs_w4a16_step"] = results[M][1] / ms8
+        print(f"# W4A8 M={M}: {ms8 * 1e3:.2f} us/step, {e['tops']:.1f} TOP/s, gate_up GEMM "
+              f"{dom8 * 1e3:.2f} us, parity ratio {par8:.3f}", file=sys.stderr, flush=True)
+        extra.append(e)
+        del wl8
 
     line = {
         "metric": "W4A16 GEMM achieved HBM TB/s (M=1,16) and TFLOP/s (M>=256) vs MI355X peak",

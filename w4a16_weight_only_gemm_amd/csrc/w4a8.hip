@@ -19,18 +19,18 @@
 //  * w4a8_gemm_kernel: one workgroup per 128 x 256 output tile, in
 //    XCD-grouped order. K advances in k-tiles of 128: the workgroup stages the
 //    128 x 128-byte code tile in LDS (double-buffered, 16-byte pieces
-//    XOR-swizzled by row) and, while staging, each group's code sums per row
-//    (v_dot4 against ones, then a DPP reduction over the group's lanes).
-//    Eight waves in a 2 x 4 arrangement each own a 64 x 64 sub-tile: 4 x 4
-//    blocks of 16 x 16, so every activation fragment read from LDS feeds four
-//    MFMAs and every weight operand four. A packed word turns into int8
-//    operand bytes with one and-xor (low nibbles) or one shift and and-xor
-//    (high nibbles): (c & 0xF) ^ 8 is the offset code q + 8 in 0..15. The
-//    offset is removed by starting each group's integer accumulation from
-//    -8 times the group's code sum of the row. At the end of a group the
-//    exact int32 sum is converted to fp32, multiplied by the group's fp16
-//    scale and added to the fp32 result; the epilogue multiplies by the row
-//    scale and rounds to bf16.
+//    XOR-swizzled by row). Eight waves side by side along N each own a
+//    128 x 32 sub-tile: 8 x 2 blocks of 16 x 16, so every weight operand feeds
+//    eight MFMAs and no two waves load or convert the same weights. Loads run
+//    two k-tiles ahead of the math (three rotating weight register sets, two
+//    staging sets). A packed 4-bit code moved into the high nibble of a byte
+//    (low nibble zero) is the signed byte 16 q, so a packed word becomes two
+//    int8 operand registers with one and (odd nibbles, in place) and one
+//    shift and and (even nibbles): the int32 MFMA sums are 16 times the exact
+//    sums of products, with no offset to remove. At the end of a group the
+//    int32 sum is converted to fp32 and multiplied by the group's fp16 scale
+//    times 1/16 (exact), then added to the fp32 result; the epilogue
+//    multiplies by the row scale and rounds to bf16.
 //
 // Group sizes 64 and 128 (a k-tile holds two or one whole groups; a group
 // fills whole 64-deep MFMA steps in every lane group). Rows beyond M read as
@@ -142,11 +142,8 @@ struct Q8Cfg {
   static constexpr int T = kQ8KT / GS;                    // groups per k-tile
   static constexpr int WPL = GS / 32;                     // words per lane per group
   static constexpr int Steps = GS / 64;                   // MFMA steps per group
-  static constexpr int LPG = GS / 16;                     // staging lanes per group
   static constexpr int ABytes = Rows * kQ8KT;
-  static constexpr int SBytes = T * Rows * 4;
-  static constexpr int BufBytes = ABytes + SBytes;
-  static constexpr size_t Lds = 2 * static_cast<size_t>(BufBytes);
+  static constexpr size_t Lds = 2 * static_cast<size_t>(ABytes);
 };
 
 // LDS slot of 16-byte piece p of a row: p ^ (r & 7) ^ ((r >> 3) & 1), r the
@@ -158,25 +155,16 @@ __device__ __forceinline__ int q8_slot(int piece, int row) {
   return piece ^ (row & 7) ^ ((row >> 3) & 1);
 }
 
-// Sum over the aligned group of LPG (4 or 8) consecutive lanes, in every lane
-// of the group.
-template <int LPG>
-__device__ __forceinline__ int group_lane_sum_i32(int v) {
-  static_assert(LPG == 4 || LPG == 8, "group of 64 or 128 codes");
-  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);                   // quad_perm [1,0,3,2]
-  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);                   // quad_perm [2,3,0,1]
-  if constexpr (LPG == 8) v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // half mirror
-  return v;
-}
-
-// Offset codes (q + 8, 0..15) of two packed words as one int8 operand: bytes
-// in the order low nibbles of w0, high nibbles of w0, low of w1, high of w1.
-__device__ __forceinline__ i32x4 dequant_i8(uint32_t w0, uint32_t w1) {
+// The codes of two packed words as one int8 operand, each byte 16 q: a 4-bit
+// two's-complement code moved into the high nibble of a byte, low nibble
+// zero, is the signed byte 16 q. Bytes in the order even nibbles of w0
+// (shifted up), odd nibbles of w0 (in place), then the same for w1.
+__device__ __forceinline__ i32x4 dequant_i8x16(uint32_t w0, uint32_t w1) {
   i32x4 r;
-  r[0] = static_cast<int>((w0 & 0x0F0F0F0Fu) ^ 0x08080808u);
-  r[1] = static_cast<int>(((w0 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u);
-  r[2] = static_cast<int>((w1 & 0x0F0F0F0Fu) ^ 0x08080808u);
-  r[3] = static_cast<int>(((w1 >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u);
+  r[0] = static_cast<int>((w0 << 4) & 0xF0F0F0F0u);
+  r[1] = static_cast<int>(w0 & 0xF0F0F0F0u);
+  r[2] = static_cast<int>((w1 << 4) & 0xF0F0F0F0u);
+  r[3] = static_cast<int>(w1 & 0xF0F0F0F0u);
   return r;
 }
 
@@ -250,18 +238,11 @@ struct Q8Engine {
     }
   }
   __device__ __forceinline__ void stage_store(const Q8Stage<GS, WM, MB, NB>& r, int buf) const {
-    unsigned char* base = lds + buf * C::BufBytes;
-    int* sums = reinterpret_cast<int*>(base + C::ABytes);
+    unsigned char* base = lds + buf * C::ABytes;
     const int spiece = tid % kQ8Pieces, srow0 = tid / kQ8Pieces;
 #pragma unroll
     for (int i = 0; i < C::Loads; ++i) {
       const int row = srow0 + i * C::RowStep;
-      int s = __builtin_amdgcn_sdot4(static_cast<int>(r.d[i][0]), 0x01010101, 0, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(r.d[i][1]), 0x01010101, s, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(r.d[i][2]), 0x01010101, s, false);
-      s = __builtin_amdgcn_sdot4(static_cast<int>(r.d[i][3]), 0x01010101, s, false);
-      s = group_lane_sum_i32<C::LPG>(s);
-      sums[(spiece / C::LPG) * C::Rows + row] = -8 * s;  // same value from every lane of the group
       *reinterpret_cast<u32x4*>(base + row * kQ8KT + q8_slot(spiece, row) * 16) = r.d[i];
     }
   }
@@ -293,80 +274,89 @@ struct Q8Engine {
     }
   }
 
-  // One k-tile: for each group, Steps MFMA steps of 64 k from the group's
-  // -8 x code-sum start, then the scaled add into acc_out.
+  // One k-tile: for each group, Steps MFMA steps of 64 k per 16 x 16 block
+  // (one column block at a time, its MB row blocks side by side), then the
+  // block's scaled add into acc_out. The integer sums are 16 times the
+  // products of codes; the 1/16 goes into the scale.
   __device__ __forceinline__ void compute(Q8Acc<MB, NB>& acc_out, const Q8B<NB>& b, int t,
                                           int buf) const {
-    const unsigned char* base = lds + buf * C::BufBytes;
-    const int* sums = reinterpret_cast<const int*>(base + C::ABytes);
+    const unsigned char* base = lds + buf * C::ABytes;
     const int arow = lane & 15, lg = lane >> 4;
     const int shalf = (lane & 1) * 16;
     const int rbase = wm * MB * 16;
 #pragma unroll
     for (int gi = 0; gi < C::T; ++gi) {
       if (C::T > 1 && t * C::T + gi >= G) break;  // ragged last k-tile (uniform)
-      i32x4 acc[NB][MB];
+      i32x4 af[C::Steps][MB];
 #pragma unroll
       for (int s = 0; s < C::Steps; ++s) {
         const int piece = gi * (GS / 16) + lg * (GS / 64) + s;
-        i32x4 af[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int row = rbase + mb * 16 + arow;
-          af[mb] = *reinterpret_cast<const i32x4*>(base + row * kQ8KT + q8_slot(piece, arow) * 16);
-        }
-        if (s == 0) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const i32x4 bias =
-                *reinterpret_cast<const i32x4*>(sums + gi * C::Rows + rbase + mb * 16 + 4 * lg);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb][mb] = bias;
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int w0 = gi * C::WPL + 2 * s;
-          const i32x4 bq = dequant_i8(b.w[nb][w0], b.w[nb][w0 + 1]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma_i8(af[mb], bq, acc[nb][mb]);
+          af[s][mb] =
+              *reinterpret_cast<const i32x4*>(base + row * kQ8KT + q8_slot(piece, arow) * 16);
         }
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float sc = fp16_bits_to_f32(static_cast<uint16_t>(b.s[nb][gi] >> shalf));
+        i32x4 acc[MB];
+#pragma unroll
+        for (int s = 0; s < C::Steps; ++s) {
+          const int w0 = gi * C::WPL + 2 * s;
+          const i32x4 bq = dequant_i8x16(b.w[nb][w0], b.w[nb][w0 + 1]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb] = mfma_i8(af[s][mb], bq, s == 0 ? i32x4{0, 0, 0, 0} : acc[mb]);
+        }
+        const float sc =
+            fp16_bits_to_f32(static_cast<uint16_t>(b.s[nb][gi] >> shalf)) * 0.0625f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc_out.v[mb][nb][r] += sc * static_cast<float>(acc[nb][mb][r]);
+            acc_out.v[mb][nb][r] += sc * static_cast<float>(acc[mb][r]);
       }
     }
   }
 
-  // k-tiles [0, kt), pipelined as in the bf16 tile engine: k-tile t computes
-  // from LDS buffer t & 1 while k-tile t + 1 is loaded into registers and then
-  // staged into the other buffer; one workgroup barrier per k-tile.
+  // k-tiles [0, kt), two k-tiles ahead: while k-tile t computes from LDS
+  // buffer t & 1, the codes and weights of k-tile t + 2 are loaded into
+  // registers and the codes of k-tile t + 1 (loaded one iteration earlier)
+  // are staged into the other buffer; one workgroup barrier per k-tile.
+  // Three weight sets and two staging sets rotate through six unrolled
+  // iterations (no register copies). Loads past the last k-tile repeat it.
   __device__ __forceinline__ void kloop(Q8Acc<MB, NB>& acc, int kt) const {
-    Q8Stage<GS, WM, MB, NB> sr;
-    Q8B<NB> b0, b1;
-    stage_load(sr, 0);
+    Q8Stage<GS, WM, MB, NB> sa, sb;
+    Q8B<NB> b0, b1, b2;
+    const int t1 = kt > 1 ? 1 : 0;
+    stage_load(sa, 0);
     load_b(b0, 0);
-    stage_store(sr, 0);
+    stage_load(sb, t1);
+    load_b(b1, t1);
+    stage_store(sa, 0);
     lds_barrier();
-    auto iter = [&](int t, const Q8B<NB>& cur, Q8B<NB>& nxt) {
-      const int tn = t + 1 < kt ? t + 1 : t;  // the last iteration reloads (unused)
-      stage_load(sr, tn);
-      load_b(nxt, tn);
-      __builtin_amdgcn_sched_barrier(0);      // issue the loads before the math
+    // s_next holds k-tile t + 1; s_next2 and nxt2 receive k-tile t + 2
+    auto iter = [&](int t, const Q8B<NB>& cur, Q8B<NB>& nxt2, const Q8Stage<GS, WM, MB, NB>& s_next,
+                    Q8Stage<GS, WM, MB, NB>& s_next2) {
+      const int t2 = t + 2 < kt ? t + 2 : kt - 1;
+      stage_load(s_next2, t2);
+      load_b(nxt2, t2);
+      __builtin_amdgcn_sched_barrier(0);  // issue the loads before the math
       compute(acc, cur, t, t & 1);
-      stage_store(sr, (t & 1) ^ 1);
+      stage_store(s_next, (t + 1) & 1);
       lds_barrier();
     };
-    for (int t = 0; t < kt; t += 2) {
-      iter(t, b0, b1);
-      if (t + 1 >= kt) break;
-      iter(t + 1, b1, b0);
+    // A single exit, at the top: an iteration past the last k-tile is
+    // skipped rather than left through a break (exits from the middle of the
+    // unrolled body make the compiler copy the accumulators at every exit).
+    for (int t = 0; t < kt; t += 6) {
+      iter(t, b0, b2, sb, sa);
+      if (t + 1 < kt) iter(t + 1, b1, b0, sa, sb);
+      if (t + 2 < kt) iter(t + 2, b2, b1, sb, sa);
+      if (t + 3 < kt) iter(t + 3, b0, b2, sa, sb);
+      if (t + 4 < kt) iter(t + 4, b1, b0, sb, sa);
+      if (t + 5 < kt) iter(t + 5, b2, b1, sa, sb);
     }
   }
 
@@ -421,7 +411,7 @@ __global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Args
 
 template <int GS>
 hipError_t launch_w4a8_t(const W4A8Args& a, hipStream_t stream) {
-  constexpr int WM = 2, MB = 4, NB = 4;
+  constexpr int WM = 1, MB = 8, NB = 2;
   using C = Q8Cfg<GS, WM, MB, NB>;
   const int NCB = (a.N + 15) / 16;
   const int NT = (NCB + C::Blocks - 1) / C::Blocks;
