@@ -322,9 +322,12 @@ def check_parity(wl: Workload, layer: int, cols: int = 64):
 
 
 def time_w4a8(wl: Workload, steps: int, warmup: int):
-    """The W4A8 step at wl.M rows: for each projection, w4a8_quantize of its
-    activations, then w4a8_gemm. Returns (ms per step, ms per gate_up GEMM
-    launch alone, sampled parity ratio against the oracle's W4A8 chain)."""
+    """The W4A8 step at wl.M rows: one w4a8_quantize_grouped launch over the
+    four projections' activations, then one w4a8_gemm_grouped launch. Returns
+    (ms per step, ms per grouped GEMM launch alone, sampled parity ratio
+    against the oracle's W4A8 chain)."""
+    import ctypes
+
     import numpy as np
     import torch
 
@@ -336,34 +339,37 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
     stream = cur.cuda_stream
     M = wl.M
     L = len(wl.args)
-    q8 = []
+    steps_args, keep = [], []
     for layer in range(L):
-        la = []
+        qents, gents = [], []
         for pi, p in enumerate(wl.store.projs):
             xq = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
             sx = torch.empty((M,), dtype=torch.float32, device="cuda")
             x, qw, sp, y = wl.args[layer][pi][:4]
-            la.append(((x, xq.data_ptr(), sx.data_ptr(), M, p.K),
-                       (xq.data_ptr(), sx.data_ptr(), qw, sp, y, M, p.N, p.K, GROUP), xq, sx))
-        q8.append(la)
+            qents.append((x, xq.data_ptr(), sx.data_ptr(), p.K))
+            gents.append((xq.data_ptr(), sx.data_ptr(), qw, sp, y, p.N, p.K))
+            keep += [xq, sx]
+        qa = w4.make_w4a8_quantize_problems(qents)
+        ga = w4.make_w4a8_problems(gents)
+        keep += [qa, ga]
+        steps_args.append((ctypes.cast(qa, ctypes.c_void_p).value, len(qents),
+                           ctypes.cast(ga, ctypes.c_void_p).value, len(gents)))
 
-    def run(first, count, only=None):
+    def run(first, count, gemm_only=False):
         for s_ in range(first, first + count):
-            for pi, (qa, ga, _, _) in enumerate(q8[s_ % L]):
-                if only is not None and pi != only:
-                    continue
-                if only is None:
-                    rc = lib.w4a8_quantize(*qa, stream)
-                    if rc != 0:
-                        raise RuntimeError(f"w4a8_quantize failed with status {rc}")
-                rc = lib.w4a8_gemm(*ga, stream)
+            qa, nq, ga, ng = steps_args[s_ % L]
+            if not gemm_only:
+                rc = lib.w4a8_quantize_grouped(qa, nq, M, stream)
                 if rc != 0:
-                    raise RuntimeError(f"w4a8_gemm failed with status {rc}")
+                    raise RuntimeError(f"w4a8_quantize_grouped failed with status {rc}")
+            rc = lib.w4a8_gemm_grouped(ga, ng, M, GROUP, stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a8_gemm_grouped failed with status {rc}")
 
     run(0, warmup)
     torch.cuda.synchronize()
     step_ms = timed(lambda: run(0, steps), cur) / steps
-    dom_ms = timed(lambda: run(0, steps, only=2), cur) / steps
+    dom_ms = timed(lambda: run(0, steps, gemm_only=True), cur) / steps
     run(0, L)  # every layer's outputs from the full chain
     torch.cuda.synchronize()
     worst = 0.0
@@ -708,16 +714,16 @@ def main(argv=None):
         f = wl8.step_flops()
         e = {"path": "w4a8", "M": M, "ms_per_step": ms8, "tops": f / (ms8 * 1e-3) / 1e12,
              "positions_per_s": M / (ms8 * 1e-3), "parity_ratio": par8,
-             "note": "per projection: w4a8_quantize of bf16 activations, then w4a8_gemm; "
-                     "parity against the oracle's quantize + W4A8 GEMM"}
-        gflops = flops(M, gu.N, gu.K)
-        e["roofline"] = {"bound": "mfma", "achieved": gflops / (dom8 * 1e-3) / 1e12,
+             "note": "one w4a8_quantize_grouped launch (bf16 activations of the four "
+                     "projections to int8) and one w4a8_gemm_grouped launch; parity against "
+                     "the oracle's quantize + W4A8 GEMM"}
+        e["roofline"] = {"bound": "mfma", "achieved": f / (dom8 * 1e-3) / 1e12,
                          "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                         "frac": gflops / (dom8 * 1e-3) / 1e12 / INT8_PEAK_TOPS,
-                         "kernel": "w4a8_gemm, gate_up projection (5120x34816) at M=%d" % M}
+                         "frac": f / (dom8 * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                         "kernel": "w4a8_gemm_grouped launch (qkv+o+gate_up+down) at M=%d" % M}
         if M in results:
             e["speedup_vs_w4a16_step"] = results[M][1] / ms8
-        print(f"# W4A8 M={M}: {ms8 * 1e3:.2f} us/step, {e['tops']:.1f} TOP/s, gate_up GEMM "
+        print(f"# W4A8 M={M}: {ms8 * 1e3:.2f} us/step, {e['tops']:.1f} TOP/s, grouped GEMM "
               f"{dom8 * 1e3:.2f} us, parity ratio {par8:.3f}", file=sys.stderr, flush=True)
         extra.append(e)
         del wl8

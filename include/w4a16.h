@@ -200,6 +200,45 @@ int w4a8_quantize(const void* x, void* xq, void* sx, int M, int K, struct ihipSt
 int w4a8_gemm(const void* xq, const void* sx, const void* qweight, const void* scales, void* y,
               int M, int N, int K, int group, struct ihipStream_t* stream);
 
+/* One quantization of a grouped call: x (bf16 [M][K]) -> xq, sx, as w4a8_quantize. */
+typedef struct w4a8_quantize_problem {
+  const void* x;
+  void* xq;
+  void* sx;
+  int K;
+} w4a8_quantize_problem;
+
+/*
+ * Several quantizations sharing M in one launch (for example the inputs of a
+ * layer's projections). `problems` is host memory read during the call;
+ * count is 1..W4A16_MAX_PROBLEMS; each problem is validated as in
+ * w4a8_quantize, and every result equals that of w4a8_quantize.
+ */
+int w4a8_quantize_grouped(const w4a8_quantize_problem* problems, int count, int M,
+                          struct ihipStream_t* stream);
+
+/* One GEMM of a grouped W4A8 call: y[M][N] from xq, sx ([M][K], [M]) and the
+ * packed weights, as w4a8_gemm. */
+typedef struct w4a8_problem {
+  const void* xq;
+  const void* sx;
+  const void* qweight;
+  const void* scales;
+  void* y;
+  int N;
+  int K;
+} w4a8_problem;
+
+/*
+ * Several W4A8 GEMMs sharing M and the group size in one launch, so that the
+ * small projections of a layer do not leave compute units idle and the
+ * deepest-K problems start first. `problems` is host memory read during the
+ * call; count is 1..W4A16_MAX_PROBLEMS; each problem is validated as in
+ * w4a8_gemm, and every result equals that of w4a8_gemm. No workspace.
+ */
+int w4a8_gemm_grouped(const w4a8_problem* problems, int count, int M, int group,
+                      struct ihipStream_t* stream);
+
 /* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
  * host integers), or -1 for an unsupported shape. */
 int w4a16_select_path(int M, int N, int K, int group);

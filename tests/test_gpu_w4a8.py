@@ -252,3 +252,86 @@ def test_gemm_deterministic_and_stream():
     st.synchronize()
     b = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------- grouped
+
+def test_grouped_quantize_matches_oracle():
+    """One launch over three inputs of different K, bit-exact against the oracle."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = _torch()
+    M = 37
+    entries, xs, outs = [], [], []
+    for i, K in enumerate((5120, 272, 1024)):
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 320 + i, 0, M), M, K)
+        xd = dev_u16(x).view(torch.bfloat16)
+        xq = torch.full((M, K), 99, dtype=torch.int8, device="cuda")
+        sx = torch.full((M,), -1.0, dtype=torch.float32, device="cuda")
+        entries.append((xd, xq, sx, K))
+        xs.append(x)
+        outs.append((xq, sx))
+    log("w4a8 grouped quantize")
+    w4.w4a8_quantize_grouped(entries, M)
+    torch.cuda.synchronize()
+    for x, (xq, sx) in zip(xs, outs):
+        eq, es = oracle.quantize_rows(x)
+        assert np.array_equal(sx.cpu().numpy().view(np.uint32), es.view(np.uint32))
+        assert np.array_equal(xq.cpu().numpy(), arranged(eq))
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_grouped_gemm_parity_and_identity(g):
+    """One launch over problems of different N and K (the deepest K is
+    dispatched first, whatever its position in the list): each result within
+    tolerance of the oracle and bit-identical to its single-problem call."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = _torch()
+    M = 130
+    shapes = [(300, 640), (1000, 1152), (48, 2048), (520, 256)]
+    probs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x, q, s = _random_inputs(50 + i, M, N, K, g)
+        xq, sx = oracle.quantize_rows(x)
+        probs.append(Q8Problem(arranged(xq), sx, q, s, g))
+        refs.append(oracle.gemm_w4a8(xq, sx, q, s, g))
+    ys = [torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda") for N, _ in shapes]
+    log(f"w4a8 grouped gemm g={g}")
+    w4.w4a8_gemm_grouped([(p.xq, p.sx, p.qw, p.sp, y, p.N, p.K) for p, y in zip(probs, ys)], M, g)
+    torch.cuda.synchronize()
+    for p, y, ref in zip(probs, ys, refs):
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert tolerance_ratio(yb, ref) <= 1.0
+        assert np.array_equal(yb, p.run())
+
+
+def test_grouped_layer_set_m256_sampled():
+    """The four projections of a layer at M = 256 (group 128) through the
+    grouped quantize and grouped GEMM, as the benchmark runs them; the oracle
+    recomputes sampled rows and columns of every projection."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = _torch()
+    M, g = 256, 128
+    rng = np.random.default_rng(24)
+    qents, gents, keep = [], [], []
+    for proj, p in enumerate(synth.LAYER_PROJECTIONS):
+        x, q, s = synth.layer_inputs(1, proj, M, group=g)
+        qw, sp = w4.w4a16_pack(q, s, g)
+        xd = dev_u16(x).view(torch.bfloat16)
+        xq = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
+        sx = torch.empty((M,), dtype=torch.float32, device="cuda")
+        y = torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda")
+        qwd, spd = dev_u32(qw), dev_u16(sp)
+        qents.append((xd, xq, sx, p.K))
+        gents.append((xq, sx, qwd, spd, y, p.N, p.K))
+        keep.append((x, q, s, y, p, xd, qwd, spd))
+    log("w4a8 grouped layer set M=256")
+    w4.w4a8_quantize_grouped(qents, M)
+    w4.w4a8_gemm_grouped(gents, M, g)
+    torch.cuda.synchronize()
+    for x, q, s, y, p, *_ in keep:
+        rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 10)]))
+        cols = np.unique(np.concatenate([[0, p.N - 1], rng.integers(0, p.N, 24)]))
+        eq, es = oracle.quantize_rows(x[rows])
+        ref = oracle.gemm_w4a8(eq, es, q[cols], s[cols], g)
+        yb = y.view(torch.int16).cpu().numpy().view(np.uint16)[np.ix_(rows, cols)]
+        assert tolerance_ratio(yb, ref) <= 1.0

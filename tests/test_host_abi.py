@@ -25,7 +25,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert len(names) >= 8, names
-    assert "w4a8_quantize" in names and "w4a8_gemm" in names
+    for name in ("w4a8_quantize", "w4a8_gemm", "w4a8_quantize_grouped", "w4a8_gemm_grouped"):
+        assert name in names, name
     lib = ctypes.CDLL(w4.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
@@ -196,3 +197,25 @@ def test_w4a8_argument_checks_without_launch():
         args = [A] * 5
         args[i] = A + 4
         assert g(*args, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED, i
+
+
+def test_w4a8_grouped_argument_checks_without_launch():
+    q = w4.w4a8_quantize_grouped_status
+    ok = (A, A, A, 256)
+    assert q([ok], 0) == w4.W4A16_OK                                          # M == 0
+    assert q([ok] * 9, 4) == w4.W4A16_ERR_INVALID_ARG                         # too many
+    assert q([ok], -1) == w4.W4A16_ERR_INVALID_ARG
+    assert q([ok, (A, A, A, -16)], 4) == w4.W4A16_ERR_INVALID_ARG
+    assert q([ok, (A, None, A, 256)], 4) == w4.W4A16_ERR_INVALID_ARG
+    assert q([ok, (A, A, A, 40)], 4) == w4.W4A16_ERR_UNSUPPORTED
+    assert q([ok, (A, A, A + 4, 256)], 4) == w4.W4A16_ERR_MISALIGNED
+    g = w4.w4a8_gemm_grouped_status
+    ok = (A, A, A, A, A, 512, 256)
+    assert g([ok], 0, 64) == w4.W4A16_OK
+    assert g([ok] * 9, 4, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert g([ok], -1, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert g([ok, (A, A, A, A, A, -1, 256)], 4, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert g([ok, (A, A, None, A, A, 512, 256)], 4, 64) == w4.W4A16_ERR_INVALID_ARG
+    assert g([ok], 4, 32) == w4.W4A16_ERR_UNSUPPORTED
+    assert g([ok, (A, A, A, A, A, 512, 352)], 4, 64) == w4.W4A16_ERR_UNSUPPORTED
+    assert g([ok, (A, A, A, A, A + 2, 512, 256)], 4, 64) == w4.W4A16_ERR_MISALIGNED

@@ -45,6 +45,16 @@ class w4a16_problem(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("N", ctypes.c_int), ("K", ctypes.c_int)]
 
+class w4a8_quantize_problem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("xq", ctypes.c_void_p), ("sx", ctypes.c_void_p),
+                ("K", ctypes.c_int)]
+
+
+class w4a8_problem(ctypes.Structure):
+    _fields_ = [("xq", ctypes.c_void_p), ("sx", ctypes.c_void_p), ("qweight", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int),
+                ("K", ctypes.c_int)]
+
 # Every symbol include/w4a16.h declares, with its ctypes signature.
 _vp, _int, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 SIGNATURES = {
@@ -59,6 +69,8 @@ SIGNATURES = {
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
     "w4a8_quantize": (_int, [_vp, _vp, _vp, _int, _int, _vp]),
     "w4a8_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "w4a8_quantize_grouped": (_int, [_vp, _int, _int, _vp]),
+    "w4a8_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_version": (_int, []),
 }
@@ -278,3 +290,56 @@ def w4a8_gemm_status(xq, sx, qweight, scales, y, M, N, K, group, stream=None) ->
     """Raw status of w4a8_gemm, without raising (for tests of the error paths)."""
     return int(_lib.w4a8_gemm(_ptr(xq), _ptr(sx), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K,
                               group, _stream(stream)))
+
+
+def make_w4a8_quantize_problems(entries):
+    """ctypes array of w4a8_quantize_problem from (x, xq, sx, K) tuples."""
+    arr = (w4a8_quantize_problem * len(entries))()
+    for i, (x, xq, sx, K) in enumerate(entries):
+        arr[i] = w4a8_quantize_problem(_ptr(x), _ptr(xq), _ptr(sx), K)
+    return arr
+
+
+def make_w4a8_problems(entries):
+    """ctypes array of w4a8_problem from (xq, sx, qweight, scales, y, N, K) tuples."""
+    arr = (w4a8_problem * len(entries))()
+    for i, (xq, sx, qw, sp, y, N, K) in enumerate(entries):
+        arr[i] = w4a8_problem(_ptr(xq), _ptr(sx), _ptr(qw), _ptr(sp), _ptr(y), N, K)
+    return arr
+
+
+def w4a8_quantize_grouped_status(problems, M, stream=None) -> int:
+    arr = problems if isinstance(problems, ctypes.Array) else make_w4a8_quantize_problems(problems)
+    return int(_lib.w4a8_quantize_grouped(ctypes.cast(arr, ctypes.c_void_p), len(arr), M,
+                                          _stream(stream)))
+
+
+def w4a8_quantize_grouped(problems, M: int, stream=None) -> None:
+    """Several row-wise quantizations sharing M in one launch; `problems` is a
+    list of (x, xq, sx, K) tuples or a make_w4a8_quantize_problems() array."""
+    if not isinstance(problems, ctypes.Array):
+        for (x, xq, sx, K) in problems:
+            _check_sizes(x=(x, 2 * M * K), xq=(xq, M * K), sx=(sx, 4 * M))
+    rc = w4a8_quantize_grouped_status(problems, M, stream)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a8_quantize_grouped")
+
+
+def w4a8_gemm_grouped_status(problems, M, group, stream=None) -> int:
+    arr = problems if isinstance(problems, ctypes.Array) else make_w4a8_problems(problems)
+    return int(_lib.w4a8_gemm_grouped(ctypes.cast(arr, ctypes.c_void_p), len(arr), M, group,
+                                      _stream(stream)))
+
+
+def w4a8_gemm_grouped(problems, M: int, group: int, stream=None) -> None:
+    """Several W4A8 GEMMs sharing M and the group size in one launch; `problems`
+    is a list of (xq, sx, qweight, scales, y, N, K) tuples or a
+    make_w4a8_problems() array."""
+    if not isinstance(problems, ctypes.Array):
+        for (xq, sx, qw, sp, y, N, K) in problems:
+            if group > 0 and K % group == 0:
+                _check_sizes(xq=(xq, M * K), sx=(sx, 4 * M), y=(y, 2 * M * N),
+                             qweight=(qw, N * K // 2), scales=(sp, 2 * N * (K // group)))
+    rc = w4a8_gemm_grouped_status(problems, M, group, stream)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a8_gemm_grouped")

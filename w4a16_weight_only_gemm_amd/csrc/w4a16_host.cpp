@@ -193,15 +193,64 @@ int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* 
   return w4a16_gemm_grouped(&p, 1, M, group, workspace, workspace_bytes, stream);
 }
 
+int w4a8_quantize_grouped(const w4a8_quantize_problem* problems, int count, int M,
+                          hipStream_t stream) {
+  if (!problems || count < 1 || count > W4A16_MAX_PROBLEMS || M < 0) return W4A16_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (problems[i].K < 0) return W4A16_ERR_INVALID_ARG;
+  if (M == 0) return W4A16_OK;
+  w4a16_internal::W4A8QuantProblem probs[W4A16_MAX_PROBLEMS] = {};
+  for (int i = 0; i < count; ++i) {
+    const w4a8_quantize_problem& p = problems[i];
+    if (!p.x || !p.xq || !p.sx) return W4A16_ERR_INVALID_ARG;
+    if (p.K < 16 || p.K % 16 != 0) return W4A16_ERR_UNSUPPORTED;
+    if (!aligned16(p.x) || !aligned16(p.xq) || !aligned16(p.sx)) return W4A16_ERR_MISALIGNED;
+    probs[i].x = static_cast<const uint16_t*>(p.x);
+    probs[i].xq = static_cast<uint8_t*>(p.xq);
+    probs[i].sx = static_cast<float*>(p.sx);
+    probs[i].K = p.K;
+  }
+  if (static_cast<long long>(M) * count > 0x7FFFFFFFLL) return W4A16_ERR_UNSUPPORTED;
+  const hipError_t err = w4a16_internal::launch_w4a8_quantize(probs, count, M, stream);
+  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
 int w4a8_quantize(const void* x, void* xq, void* sx, int M, int K, hipStream_t stream) {
   if (M < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
   if (M == 0) return W4A16_OK;
-  if (!x || !xq || !sx) return W4A16_ERR_INVALID_ARG;
-  if (K < 16 || K % 16 != 0) return W4A16_ERR_UNSUPPORTED;
-  if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return W4A16_ERR_MISALIGNED;
-  const hipError_t err = w4a16_internal::launch_w4a8_quantize(
-      static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), static_cast<float*>(sx), M, K,
-      stream);
+  const w4a8_quantize_problem p = {x, xq, sx, K};
+  return w4a8_quantize_grouped(&p, 1, M, stream);
+}
+
+int w4a8_gemm_grouped(const w4a8_problem* problems, int count, int M, int group,
+                      hipStream_t stream) {
+  if (!problems || count < 1 || count > W4A16_MAX_PROBLEMS || M < 0) return W4A16_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (problems[i].N < 0 || problems[i].K < 0) return W4A16_ERR_INVALID_ARG;
+  if (M == 0) return W4A16_OK;
+  w4a16_internal::W4A8Args probs[W4A16_MAX_PROBLEMS] = {};
+  for (int i = 0; i < count; ++i) {
+    const w4a8_problem& p = problems[i];
+    if (!p.xq || !p.sx || !p.qweight || !p.scales || !p.y) return W4A16_ERR_INVALID_ARG;
+    if (p.N < 1 || p.K < 1 || (group != 64 && group != 128) || p.K % group != 0)
+      return W4A16_ERR_UNSUPPORTED;
+    // packed weights and scales are addressed with 32-bit buffer offsets
+    if (w4a16_qweight_bytes(p.N, p.K) > 0xFFFFFFF0u) return W4A16_ERR_UNSUPPORTED;
+    if (!aligned16(p.xq) || !aligned16(p.sx) || !aligned16(p.qweight) || !aligned16(p.scales) ||
+        !aligned16(p.y))
+      return W4A16_ERR_MISALIGNED;
+    w4a16_internal::W4A8Args& a = probs[i];
+    a.xq = static_cast<const uint8_t*>(p.xq);
+    a.sx = static_cast<const float*>(p.sx);
+    a.qweight = static_cast<const uint32_t*>(p.qweight);
+    a.scales = static_cast<const uint16_t*>(p.scales);
+    a.y = static_cast<uint16_t*>(p.y);
+    a.M = M;
+    a.N = p.N;
+    a.K = p.K;
+    a.group = group;
+  }
+  const hipError_t err = w4a16_internal::launch_w4a8_gemm(probs, count, stream);
   return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -209,26 +258,8 @@ int w4a8_gemm(const void* xq, const void* sx, const void* qweight, const void* s
               int M, int N, int K, int group, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;
   if (M == 0) return W4A16_OK;
-  if (!xq || !sx || !qweight || !scales || !y) return W4A16_ERR_INVALID_ARG;
-  if (N < 1 || K < 1 || (group != 64 && group != 128) || K % group != 0)
-    return W4A16_ERR_UNSUPPORTED;
-  // packed weights and scales are addressed with 32-bit buffer offsets
-  if (w4a16_qweight_bytes(N, K) > 0xFFFFFFF0u) return W4A16_ERR_UNSUPPORTED;
-  if (!aligned16(xq) || !aligned16(sx) || !aligned16(qweight) || !aligned16(scales) ||
-      !aligned16(y))
-    return W4A16_ERR_MISALIGNED;
-  w4a16_internal::W4A8Args a;
-  a.xq = static_cast<const uint8_t*>(xq);
-  a.sx = static_cast<const float*>(sx);
-  a.qweight = static_cast<const uint32_t*>(qweight);
-  a.scales = static_cast<const uint16_t*>(scales);
-  a.y = static_cast<uint16_t*>(y);
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.group = group;
-  const hipError_t err = w4a16_internal::launch_w4a8_gemm(a, stream);
-  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+  const w4a8_problem p = {xq, sx, qweight, scales, y, N, K};
+  return w4a8_gemm_grouped(&p, 1, M, group, stream);
 }
 
 const char* w4a16_status_string(int status) {

@@ -71,10 +71,15 @@ __device__ __forceinline__ uint32_t code_byte(uint32_t bf16_bits, float inv) {
   return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
 }
 
-__global__ __launch_bounds__(kQThreads) void w4a8_quantize_kernel(const uint16_t* x, uint32_t* xq,
-                                                                  float* sx, int K) {
+__global__ __launch_bounds__(kQThreads) void w4a8_quantize_kernel(const W4A8QuantBatch bt) {
+  const int p = uniform(static_cast<int>(blockIdx.x) / bt.M);
+  const W4A8QuantProblem& pr = bt.prob[p];
+  const uint16_t* x = pr.x;
+  uint32_t* xq = reinterpret_cast<uint32_t*>(pr.xq);
+  float* sx = pr.sx;
+  const int K = pr.K;
   __shared__ uint32_t wmax[kQThreads / 64];
-  const int m = blockIdx.x;
+  const int m = static_cast<int>(blockIdx.x) - p * bt.M;
   const int tid = threadIdx.x;
   const int nblk = K / 16;
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(m) * K);
@@ -391,13 +396,26 @@ struct Q8Engine {
   }
 };
 
+// Workgroups of problem p are blocks [begin[p], begin[p] + tiles[p]) of the
+// grid; begin[p] is a multiple of 8, so the hardware's round-robin XCD of a
+// block is also its XCD within the problem, and each XCD owns a contiguous
+// range of the problem's tiles (row tiles of a column tile together). Blocks
+// past a problem's tiles (padding to the next multiple of 8) exit at once.
 template <int GS, int WM, int MB, int NB>
-__global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Args a, int MT,
-                                                                  int NT) {
+__global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Batch bt) {
   using C = Q8Cfg<GS, WM, MB, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char q8_lds[];
-  const int tile = xcd_grouped(blockIdx.x, MT * NT);
+  const int b = blockIdx.x;
+  int p = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProblems; ++i)
+    if (i < bt.nprob && b >= bt.begin[i]) p = i;
+  const int local = b - bt.begin[p];
+  if (local >= bt.tiles[p]) return;
+  const int tile = xcd_grouped(local, bt.tiles[p]);
+  const int MT = bt.MT;
   const int mt = tile % MT, nt = tile / MT;
+  const W4A8Args& a = bt.prob[p];
   Q8Engine<GS, WM, MB, NB> e;
   e.setup(q8_lds, a, mt * C::Rows, nt);
   Q8Acc<MB, NB> acc;
@@ -409,53 +427,98 @@ __global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Args
   e.store(acc, a.sx, a.y);
 }
 
+constexpr int kQ8WM = 1, kQ8MB = 8, kQ8NB = 2;
+
+// One launch over bt.prob[0 .. nprob), all with M rows; fills MT, tiles and
+// begin. Problems are dispatched in the order given.
 template <int GS>
-hipError_t launch_w4a8_t(const W4A8Args& a, hipStream_t stream) {
-  constexpr int WM = 1, MB = 8, NB = 2;
-  using C = Q8Cfg<GS, WM, MB, NB>;
-  const int NCB = (a.N + 15) / 16;
-  const int NT = (NCB + C::Blocks - 1) / C::Blocks;
-  const void* fn = reinterpret_cast<const void*>(&w4a8_gemm_kernel<GS, WM, MB, NB>);
+hipError_t launch_w4a8_batch(W4A8Batch& bt, hipStream_t stream) {
+  using C = Q8Cfg<GS, kQ8WM, kQ8MB, kQ8NB>;
+  const void* fn = reinterpret_cast<const void*>(&w4a8_gemm_kernel<GS, kQ8WM, kQ8MB, kQ8NB>);
   const size_t lds = C::Lds;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  // Code offsets are 32-bit: each launch covers at most rows_per_launch rows.
-  long long rows_per_launch = (0xFFFFFFFFLL - 256) / a.K;
-  rows_per_launch -= rows_per_launch % C::Rows;
-  if (rows_per_launch < C::Rows) return hipErrorInvalidValue;
-  for (long long r0 = 0; r0 < a.M; r0 += rows_per_launch) {
-    W4A8Args part = a;
-    part.M = static_cast<int>(a.M - r0 < rows_per_launch ? a.M - r0 : rows_per_launch);
-    part.xq = a.xq + r0 * a.K;
-    part.sx = a.sx + r0;
-    part.y = a.y + r0 * a.N;
-    int MT = (part.M + C::Rows - 1) / C::Rows;
-    const long long total = static_cast<long long>(MT) * NT;
-    if (total < 1 || total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    int ntc = NT;
-    void* kargs[] = {&part, &MT, &ntc};
-    e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(total)), dim3(kQ8Threads), kargs, lds,
-                        stream);
-    if (e != hipSuccess) return e;
+  bt.MT = (bt.prob[0].M + C::Rows - 1) / C::Rows;
+  long long blocks = 0;
+  for (int i = 0; i < bt.nprob; ++i) {
+    const int NCB = (bt.prob[i].N + 15) / 16;
+    const long long tiles = static_cast<long long>(bt.MT) * ((NCB + C::Blocks - 1) / C::Blocks);
+    if (tiles < 1 || blocks + tiles > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+    bt.begin[i] = static_cast<int>(blocks);
+    bt.tiles[i] = static_cast<int>(tiles);
+    blocks += (tiles + 7) / 8 * 8;
+  }
+  void* kargs[] = {&bt};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kQ8Threads), kargs, lds,
+                         stream);
+}
+
+template <int GS>
+hipError_t launch_w4a8_t(const W4A8Args* probs, int count, hipStream_t stream) {
+  using C = Q8Cfg<GS, kQ8WM, kQ8MB, kQ8NB>;
+  // Code offsets are 32-bit: a problem with M * K beyond that runs by itself,
+  // in row chunks of at most rows_per_launch rows.
+  bool fits = true;
+  for (int i = 0; i < count; ++i)
+    fits = fits && static_cast<long long>(probs[i].M) * probs[i].K <= 0xFFFFFF00LL;
+  if (fits) {
+    W4A8Batch bt = {};
+    // longest tiles first: the K-deepest problems start before the rest
+    int order[kMaxProblems];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    for (int i = 1; i < count; ++i)
+      for (int j = i; j > 0 && probs[order[j]].K > probs[order[j - 1]].K; --j) {
+        const int t = order[j];
+        order[j] = order[j - 1];
+        order[j - 1] = t;
+      }
+    for (int i = 0; i < count; ++i) bt.prob[i] = probs[order[i]];
+    bt.nprob = count;
+    return launch_w4a8_batch<GS>(bt, stream);
+  }
+  for (int i = 0; i < count; ++i) {
+    const W4A8Args& a = probs[i];
+    long long rows_per_launch = (0xFFFFFF00LL) / a.K;
+    rows_per_launch -= rows_per_launch % C::Rows;
+    if (rows_per_launch < C::Rows) return hipErrorInvalidValue;
+    for (long long r0 = 0; r0 < a.M; r0 += rows_per_launch) {
+      W4A8Batch bt = {};
+      W4A8Args& part = bt.prob[0];
+      part = a;
+      part.M = static_cast<int>(a.M - r0 < rows_per_launch ? a.M - r0 : rows_per_launch);
+      part.xq = a.xq + r0 * a.K;
+      part.sx = a.sx + r0;
+      part.y = a.y + r0 * a.N;
+      bt.nprob = 1;
+      const hipError_t e = launch_w4a8_batch<GS>(bt, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_w4a8_quantize(const uint16_t* x, uint8_t* xq, float* sx, int M, int K,
+hipError_t launch_w4a8_quantize(const W4A8QuantProblem* probs, int count, int M,
                                 hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems || M < 1 ||
+      static_cast<long long>(M) * count > 0x7FFFFFFFLL)
+    return hipErrorInvalidValue;
+  W4A8QuantBatch bt = {};
+  for (int i = 0; i < count; ++i) bt.prob[i] = probs[i];
+  bt.M = M;
   const void* fn = reinterpret_cast<const void*>(&w4a8_quantize_kernel);
-  uint32_t* xq32 = reinterpret_cast<uint32_t*>(xq);
-  void* kargs[] = {&x, &xq32, &sx, &K};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(M)), dim3(kQThreads), kargs, 0, stream);
+  void* kargs[] = {&bt};
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(M * count)), dim3(kQThreads), kargs, 0,
+                         stream);
 }
 
-hipError_t launch_w4a8_gemm(const W4A8Args& a, hipStream_t stream) {
-  switch (a.group) {
-    case 64: return launch_w4a8_t<64>(a, stream);
-    case 128: return launch_w4a8_t<128>(a, stream);
+hipError_t launch_w4a8_gemm(const W4A8Args* probs, int count, hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
+  switch (probs[0].group) {
+    case 64: return launch_w4a8_t<64>(probs, count, stream);
+    case 128: return launch_w4a8_t<128>(probs, count, stream);
     default: return hipErrorInvalidValue;
   }
 }
