@@ -68,7 +68,14 @@ def test_w4a16_large_path_activations_over_4gb():
     ref = oracle.gemm(_rows_bits(x, rows), q, s, g)
     yb = y[rows].view(torch.int16).cpu().numpy().view(np.uint16)
     assert tolerance_ratio(yb, ref) <= 1.0
-    del x, y
+    # the workspace entry point falls back to the same per-problem kernels here
+    nb = w4.w4a16_workspace_bytes(M, N)
+    ws = torch.zeros((nb + 3) // 4, dtype=torch.int32, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm_ws(x, dev_u32(qw), dev_u16(sp), y2, M, N, K, g, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    del x, y, y2, ws
 
 
 def test_w4a8_activations_over_4gb():
