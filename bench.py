@@ -16,9 +16,9 @@ their sustained level before timing.
 The headline line reports the decode layer set (M = 1) in HBM TB/s over
 algorithmic bytes (packed weights + scales + activations + outputs, counted once
 per call). Extra entries report the verify block (M = 16, TB/s), the batched
-step (M = 1024, TFLOP/s) and the same batched step through the W4A8 entry
-points (each projection's activations quantized to int8, then the int8 MFMA
-GEMM; TOP/s against the int8 MFMA peak).
+step (M = 1024, TFLOP/s) and the W4A8 step at M = 256 and 1024 (each
+projection's activations quantized to int8, then the int8 MFMA GEMM; TOP/s
+against the int8 MFMA peak).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--graph]
 """
@@ -620,7 +620,7 @@ def main(argv=None):
                     help="replay the steps from a captured HIP graph (no host launch cost)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--m-list", default="1,16,1024")
-    ap.add_argument("--w4a8-m-list", default="1024",
+    ap.add_argument("--w4a8-m-list", default="256,1024",
                     help="row counts of the W4A8 batched step (empty: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC byte calibration)")

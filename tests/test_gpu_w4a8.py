@@ -128,7 +128,7 @@ def test_gemm_one_hot_bit_exact():
     """Row m holds the code 1 at k = (37 m) mod K and zeros elsewhere, unit
     scales: y[m][n] = q[n][(37 m) mod K] exactly. Every k position of every
     lane group and k-tile is hit, so a wrong byte order or piece index fails."""
-    for (M, N, K, g) in [(256, 48, 1024, 128), (200, 40, 640, 64)]:
+    for (M, N, K, g) in [(256, 48, 1024, 128), (200, 40, 640, 64), (700, 264, 512, 128)]:
         log(f"w4a8 one-hot {(M, N, K, g)}")
         rng = np.random.default_rng(22)
         q = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
@@ -143,7 +143,7 @@ def test_gemm_one_hot_bit_exact():
 def test_gemm_group_index_bit_exact():
     """Codes 1 everywhere, unit weights, scale t + 1 on group t, row scale 2^-e:
     y = 2^-e * g * G (G + 1) / 2, exact."""
-    for (M, N, K, g) in [(130, 32, 1024, 128), (70, 24, 1472, 64)]:
+    for (M, N, K, g) in [(130, 32, 1024, 128), (70, 24, 1472, 64), (600, 272, 1472, 64)]:
         G = K // g
         log(f"w4a8 group-index {(M, N, K, g)}")
         s = pins.fp16_bits(np.tile(1.0 + np.arange(G), (N, 1)))
@@ -166,8 +166,10 @@ def test_gemm_extreme_codes_bit_exact():
     assert np.all(bf16_bits_to_f64(y) == 127 * 8 * K * 2.0 ** -10)
 
 
+# M <= 256 runs 4-wave workgroups (128 x 128 tiles), larger M 8-wave ones (128 x 256)
 GEMM_SHAPES = [(1, 16, 64, 64), (5, 40, 320, 64), (128, 256, 1024, 128), (130, 300, 640, 64),
-               (257, 520, 2048, 128), (300, 1000, 1088, 64), (64, 7168, 512, 128)]
+               (257, 520, 2048, 128), (300, 1000, 1088, 64), (64, 7168, 512, 128),
+               (512, 136, 384, 128), (513, 300, 640, 64), (700, 520, 1152, 128)]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda s: "x".join(map(str, s)))

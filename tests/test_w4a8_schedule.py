@@ -6,9 +6,13 @@ and checked for coverage, bounds and agreement with the packed format."""
 import numpy as np
 import pytest
 
-ROWS, KT, PIECES, THREADS = 128, 128, 8, 512
-MB, NB, WAVES = 8, 2, 8
-BLOCKS = WAVES * NB                      # 16-column blocks per tile
+ROWS, KT, PIECES = 128, 128, 8
+MB, NB = 8, 2
+SMALL_TILE_MAX_M = 256                   # 4-wave workgroups (128 x 128 tiles) up to this M
+
+
+def waves_for(M):
+    return 4 if M <= SMALL_TILE_MAX_M else 8
 
 
 def xcd_grouped(b, total):
@@ -21,12 +25,13 @@ def plan(problems, M):
     """Kernel-side view of a grouped launch: problems sorted by K (deepest
     first, stable), each a range of blocks starting at a multiple of 8."""
     order = sorted(range(len(problems)), key=lambda i: -problems[i][1])
+    blocks_per_tile = waves_for(M) * NB
     mt = (M + ROWS - 1) // ROWS
     begin, tiles, blocks = [], [], 0
     for i in order:
         N, K = problems[i]
         ncb = (N + 15) // 16
-        t = mt * ((ncb + BLOCKS - 1) // BLOCKS)
+        t = mt * ((ncb + blocks_per_tile - 1) // blocks_per_tile)
         begin.append(blocks)
         tiles.append(t)
         blocks += (t + 7) // 8 * 8
@@ -52,6 +57,7 @@ def test_xcd_grouped_is_a_bijection(total):
 
 @pytest.mark.parametrize("M,problems", [
     (1024, [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]),
+    (256, [(7168, 5120), (5120, 6144), (34816, 5120), (5120, 17408)]),
     (130, [(300, 640), (1000, 1152), (48, 2048), (520, 256)]),
     (1, [(16, 64)]),
     (4096, [(5120, 17408)] * 8),
@@ -78,9 +84,11 @@ def slot(piece, row):
     return piece ^ (row & 7) ^ ((row >> 3) & 1)
 
 
-def test_staging_writes_fill_the_tile_and_reads_find_them():
+@pytest.mark.parametrize("waves", [4, 8])
+def test_staging_writes_fill_the_tile_and_reads_find_them(waves):
     """Every (row, piece) of a k-tile is staged exactly once, at a distinct
     16-byte slot inside the buffer; a fragment read of (row, piece) finds it."""
+    THREADS = 64 * waves
     written = {}
     for tid in range(THREADS):
         spiece, srow0 = tid % PIECES, tid // PIECES

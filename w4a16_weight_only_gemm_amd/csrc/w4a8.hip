@@ -16,12 +16,14 @@
 //    MFMA step consumes the weight codes of two packed words:
 //    0,4,1,5,2,6,3,7, 8,12,9,13,10,14,11,15.
 //
-//  * w4a8_gemm_kernel: one workgroup per 128 x 256 output tile, in
-//    XCD-grouped order. K advances in k-tiles of 128: the workgroup stages the
-//    128 x 128-byte code tile in LDS (double-buffered, 16-byte pieces
-//    XOR-swizzled by row). Eight waves side by side along N each own a
-//    128 x 32 sub-tile: 8 x 2 blocks of 16 x 16, so every weight operand feeds
-//    eight MFMAs and no two waves load or convert the same weights. Loads run
+//  * w4a8_gemm_kernel: one workgroup per 128 x 256 output tile (8 waves), or
+//    128 x 128 (4 waves, two workgroups per CU) for M <= 256, where the wider
+//    tiles leave compute units idle; tiles in XCD-grouped order. K advances
+//    in k-tiles of 128: the workgroup stages the 128 x 128-byte code tile in
+//    LDS (double-buffered, 16-byte pieces XOR-swizzled by row). The waves sit
+//    side by side along N, each owning a 128 x 32 sub-tile: 8 x 2 blocks of
+//    16 x 16, so every weight operand feeds eight MFMAs and no two waves load
+//    or convert the same weights. Loads run
 //    two k-tiles ahead of the math (three rotating weight register sets, two
 //    staging sets). A packed 4-bit code moved into the high nibble of a byte
 //    (low nibble zero) is the signed byte 16 q, so a packed word becomes two
@@ -129,21 +131,21 @@ __global__ __launch_bounds__(kQThreads) void w4a8_quantize_kernel(const W4A8Quan
 
 // -------------------------------------------------------------------- GEMM
 
-constexpr int kQ8Threads = 512;  // 8 waves
 constexpr int kQ8KT = 128;       // k per k-tile (bytes of a row's codes)
 constexpr int kQ8Pieces = kQ8KT / 16;
 
-// Tile geometry: WM x WN waves, each MB x NB blocks of 16 x 16.
-template <int GS, int WM, int MB, int NB>
+// Tile geometry: WAVES = WM x WN waves, each MB x NB blocks of 16 x 16.
+template <int GS, int WAVES, int WM, int MB, int NB>
 struct Q8Cfg {
   static_assert(GS == 64 || GS == 128, "group 64 or 128");
-  static_assert(WM * (8 / WM) == 8, "eight waves");
-  static constexpr int WN = 8 / WM;
+  static_assert(WAVES % WM == 0, "whole wave rows");
+  static constexpr int Threads = 64 * WAVES;
+  static constexpr int WN = WAVES / WM;
   static constexpr int Rows = WM * MB * 16;
   static constexpr int Blocks = WN * NB;                  // 16-column blocks per tile
-  static constexpr int Loads = Rows * kQ8Pieces / kQ8Threads;
-  static_assert(Loads >= 1 && Rows * kQ8Pieces % kQ8Threads == 0, "whole staging passes");
-  static constexpr int RowStep = kQ8Threads / kQ8Pieces;  // rows staged per pass
+  static constexpr int Loads = Rows * kQ8Pieces / Threads;
+  static_assert(Loads >= 1 && Rows * kQ8Pieces % Threads == 0, "whole staging passes");
+  static constexpr int RowStep = Threads / kQ8Pieces;  // rows staged per pass
   static constexpr int T = kQ8KT / GS;                    // groups per k-tile
   static constexpr int WPL = GS / 32;                     // words per lane per group
   static constexpr int Steps = GS / 64;                   // MFMA steps per group
@@ -177,9 +179,9 @@ __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-template <int GS, int WM, int MB, int NB>
+template <int GS, int WAVES, int WM, int MB, int NB>
 struct Q8Stage {
-  u32x4 d[Q8Cfg<GS, WM, MB, NB>::Loads];
+  u32x4 d[Q8Cfg<GS, WAVES, WM, MB, NB>::Loads];
 };
 
 template <int NB>
@@ -193,9 +195,9 @@ struct Q8Acc {
   f32x4 v[MB][NB];
 };
 
-template <int GS, int WM, int MB, int NB>
+template <int GS, int WAVES, int WM, int MB, int NB>
 struct Q8Engine {
-  using C = Q8Cfg<GS, WM, MB, NB>;
+  using C = Q8Cfg<GS, WAVES, WM, MB, NB>;
   unsigned char* lds;
   int tid, lane, wave, wm, wn;
   int M, N, K, G, NCB, m0, nt;
@@ -232,7 +234,7 @@ struct Q8Engine {
 
   // Thread stages piece tid % 8 of rows tid / 8 + 64 i, through a buffer
   // resource based at (row m0, k-tile t) that ends at the end of xq.
-  __device__ __forceinline__ void stage_load(Q8Stage<GS, WM, MB, NB>& r, int t) const {
+  __device__ __forceinline__ void stage_load(Q8Stage<GS, WAVES, WM, MB, NB>& r, int t) const {
     const __amdgpu_buffer_rsrc_t rx =
         make_rsrc(xrow0 + t * kQ8KT, xbytes - static_cast<uint32_t>(t) * kQ8KT);
     const int spiece = tid % kQ8Pieces, srow0 = tid / kQ8Pieces;
@@ -242,7 +244,7 @@ struct Q8Engine {
       r.d[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0);
     }
   }
-  __device__ __forceinline__ void stage_store(const Q8Stage<GS, WM, MB, NB>& r, int buf) const {
+  __device__ __forceinline__ void stage_store(const Q8Stage<GS, WAVES, WM, MB, NB>& r, int buf) const {
     unsigned char* base = lds + buf * C::ABytes;
     const int spiece = tid % kQ8Pieces, srow0 = tid / kQ8Pieces;
 #pragma unroll
@@ -332,7 +334,7 @@ struct Q8Engine {
   // Three weight sets and two staging sets rotate through six unrolled
   // iterations (no register copies). Loads past the last k-tile repeat it.
   __device__ __forceinline__ void kloop(Q8Acc<MB, NB>& acc, int kt) const {
-    Q8Stage<GS, WM, MB, NB> sa, sb;
+    Q8Stage<GS, WAVES, WM, MB, NB> sa, sb;
     Q8B<NB> b0, b1, b2;
     const int t1 = kt > 1 ? 1 : 0;
     stage_load(sa, 0);
@@ -342,8 +344,8 @@ struct Q8Engine {
     stage_store(sa, 0);
     lds_barrier();
     // s_next holds k-tile t + 1; s_next2 and nxt2 receive k-tile t + 2
-    auto iter = [&](int t, const Q8B<NB>& cur, Q8B<NB>& nxt2, const Q8Stage<GS, WM, MB, NB>& s_next,
-                    Q8Stage<GS, WM, MB, NB>& s_next2) {
+    auto iter = [&](int t, const Q8B<NB>& cur, Q8B<NB>& nxt2, const Q8Stage<GS, WAVES, WM, MB, NB>& s_next,
+                    Q8Stage<GS, WAVES, WM, MB, NB>& s_next2) {
       const int t2 = t + 2 < kt ? t + 2 : kt - 1;
       stage_load(s_next2, t2);
       load_b(nxt2, t2);
@@ -401,9 +403,9 @@ struct Q8Engine {
 // block is also its XCD within the problem, and each XCD owns a contiguous
 // range of the problem's tiles (row tiles of a column tile together). Blocks
 // past a problem's tiles (padding to the next multiple of 8) exit at once.
-template <int GS, int WM, int MB, int NB>
-__global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Batch bt) {
-  using C = Q8Cfg<GS, WM, MB, NB>;
+template <int GS, int WAVES, int WM, int MB, int NB>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4a8_gemm_kernel(const W4A8Batch bt) {
+  using C = Q8Cfg<GS, WAVES, WM, MB, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char q8_lds[];
   const int b = blockIdx.x;
   int p = 0;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Batc
   const int MT = bt.MT;
   const int mt = tile % MT, nt = tile / MT;
   const W4A8Args& a = bt.prob[p];
-  Q8Engine<GS, WM, MB, NB> e;
+  Q8Engine<GS, WAVES, WM, MB, NB> e;
   e.setup(q8_lds, a, mt * C::Rows, nt);
   Q8Acc<MB, NB> acc;
 #pragma unroll
@@ -427,14 +429,22 @@ __global__ __launch_bounds__(kQ8Threads, 1) void w4a8_gemm_kernel(const W4A8Batc
   e.store(acc, a.sx, a.y);
 }
 
+// Wave tiles of 128 x 32 (8 x 2 MFMA blocks), all waves along N: 8 waves
+// (128 x 256 workgroup tiles, one workgroup per CU) or, for small M where
+// 256-column tiles leave compute units idle, 4 waves (128 x 128 tiles, two
+// workgroups per CU).
 constexpr int kQ8WM = 1, kQ8MB = 8, kQ8NB = 2;
+#ifndef W4A8_SMALL_TILE_MAX_M
+#define W4A8_SMALL_TILE_MAX_M 256
+#endif
 
 // One launch over bt.prob[0 .. nprob), all with M rows; fills MT, tiles and
 // begin. Problems are dispatched in the order given.
-template <int GS>
+template <int GS, int WAVES>
 hipError_t launch_w4a8_batch(W4A8Batch& bt, hipStream_t stream) {
-  using C = Q8Cfg<GS, kQ8WM, kQ8MB, kQ8NB>;
-  const void* fn = reinterpret_cast<const void*>(&w4a8_gemm_kernel<GS, kQ8WM, kQ8MB, kQ8NB>);
+  using C = Q8Cfg<GS, WAVES, kQ8WM, kQ8MB, kQ8NB>;
+  const void* fn =
+      reinterpret_cast<const void*>(&w4a8_gemm_kernel<GS, WAVES, kQ8WM, kQ8MB, kQ8NB>);
   const size_t lds = C::Lds;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
@@ -450,13 +460,19 @@ hipError_t launch_w4a8_batch(W4A8Batch& bt, hipStream_t stream) {
     blocks += (tiles + 7) / 8 * 8;
   }
   void* kargs[] = {&bt};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kQ8Threads), kargs, lds,
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(C::Threads), kargs, lds,
                          stream);
 }
 
 template <int GS>
+hipError_t launch_w4a8_batch_m(W4A8Batch& bt, hipStream_t stream) {
+  return bt.prob[0].M <= W4A8_SMALL_TILE_MAX_M ? launch_w4a8_batch<GS, 4>(bt, stream)
+                                               : launch_w4a8_batch<GS, 8>(bt, stream);
+}
+
+template <int GS>
 hipError_t launch_w4a8_t(const W4A8Args* probs, int count, hipStream_t stream) {
-  using C = Q8Cfg<GS, kQ8WM, kQ8MB, kQ8NB>;
+  constexpr int kRows = kQ8WM * kQ8MB * 16;  // tile rows (both wave counts)
   // Code offsets are 32-bit: a problem with M * K beyond that runs by itself,
   // in row chunks of at most rows_per_launch rows.
   bool fits = true;
@@ -475,13 +491,13 @@ hipError_t launch_w4a8_t(const W4A8Args* probs, int count, hipStream_t stream) {
       }
     for (int i = 0; i < count; ++i) bt.prob[i] = probs[order[i]];
     bt.nprob = count;
-    return launch_w4a8_batch<GS>(bt, stream);
+    return launch_w4a8_batch_m<GS>(bt, stream);
   }
   for (int i = 0; i < count; ++i) {
     const W4A8Args& a = probs[i];
     long long rows_per_launch = (0xFFFFFF00LL) / a.K;
-    rows_per_launch -= rows_per_launch % C::Rows;
-    if (rows_per_launch < C::Rows) return hipErrorInvalidValue;
+    rows_per_launch -= rows_per_launch % kRows;
+    if (rows_per_launch < kRows) return hipErrorInvalidValue;
     for (long long r0 = 0; r0 < a.M; r0 += rows_per_launch) {
       W4A8Batch bt = {};
       W4A8Args& part = bt.prob[0];
@@ -491,7 +507,7 @@ hipError_t launch_w4a8_t(const W4A8Args* probs, int count, hipStream_t stream) {
       part.sx = a.sx + r0;
       part.y = a.y + r0 * a.N;
       bt.nprob = 1;
-      const hipError_t e = launch_w4a8_batch<GS>(bt, stream);
+      const hipError_t e = launch_w4a8_batch_m<GS>(bt, stream);
       if (e != hipSuccess) return e;
     }
   }
