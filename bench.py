@@ -388,6 +388,36 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
     return step_ms, dom_ms, worst
 
 
+def read_ceiling(nbytes: int, buffers: int = 8, steps: int = 500, warmup: int = 1000):
+    """Practical read ceiling: GB/s of w4a16_read_probe reading `nbytes` once per
+    launch (the weight-stream access pattern and nothing else), cycling through
+    `buffers` distinct buffers so that no launch finds its bytes in the
+    last-level cache. Mean over `steps` back-to-back launches between events
+    on the launch stream."""
+    import torch
+
+    import w4a16_weight_only_gemm_amd as w4
+    nbytes -= nbytes % 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(buffers)]
+    sink = torch.zeros(w4.READ_PROBE_SINK_BYTES // 4, dtype=torch.int32, device="cuda")
+    cur = torch.cuda.current_stream()
+    lib, stream = w4._lib, cur.cuda_stream
+    ptrs = [b.data_ptr() for b in bufs]
+
+    def run(count):
+        for i in range(count):
+            rc = lib.w4a16_read_probe(ptrs[i % buffers], nbytes, sink.data_ptr(),
+                                      w4.READ_PROBE_SINK_BYTES, stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_read_probe failed with status {rc}")
+
+    run(warmup)
+    torch.cuda.synchronize()
+    ms = timed(lambda: run(steps), cur) / steps
+    del bufs
+    return nbytes / (ms * 1e-3) / 1e9, ms
+
+
 def cpu_baseline(seconds_target: float = 15.0):
     """The oracle, as it stands, on the host cores: decode layer sets (M = 1),
     projection after projection, layer after layer, until about
@@ -749,6 +779,16 @@ def main(argv=None):
                      "kernel": dom_name},
         "extra": extra,
     }
+    ceil_gbs, ceil_ms = read_ceiling(step_bytes)
+    line["practical_ceiling"] = {
+        "value": ceil_gbs, "unit": "GB/s", "frac_of_peak": ceil_gbs / HBM_PEAK_GBS,
+        "m1_frac_of_ceiling": achieved / ceil_gbs,
+        "kernel": "w4a16_read_probe: one read of the layer set's %d bytes per launch in the "
+                  "weight-stream access pattern, 8 rotating buffers, %.2f us per launch"
+                  % (step_bytes - step_bytes % 16, ceil_ms * 1e3)}
+    print(f"# practical read ceiling: {ceil_gbs:.0f} GB/s ({ceil_ms * 1e3:.2f} us per "
+          f"{step_bytes / 1e6:.2f} MB); the M={M0} launch reaches {achieved / ceil_gbs:.1%} of it",
+          file=sys.stderr, flush=True)
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu:

@@ -246,6 +246,25 @@ int w4a16_select_path(int M, int N, int K, int group);
 /* Static text for a status code; never NULL. */
 const char* w4a16_status_string(int status);
 
+/*
+ * Measurement aid, not part of the GEMM: reads `bytes` of device memory at
+ * `buf` once, in the access pattern of the small-M weight stream (a persistent
+ * grid of two 8-wave workgroups per compute unit, each wave one contiguous run
+ * of non-temporal 16-byte loads), and nothing else. Its rate over the packed
+ * weights of a step is the practical ceiling of the bandwidth-ceiling equation
+ * (ai.satyajit.si page, section "One weight read, shared by every stream") on
+ * this chip, against which the streaming kernels are judged.
+ *   buf  : device, 16-byte aligned, bytes % 16 == 0 (bytes == 0: no launch)
+ *   sink : device, 4-byte aligned, at least 8,192 bytes (2,048 uint32); the
+ *          probe writes one 32-bit wrapping sum per workgroup into its first
+ *          words, so over a zero-filled sink the wrapping sum of all sink words
+ *          equals that of every 32-bit word of the buffer.
+ * Asynchronous on `stream`; allocates nothing. Returns W4A16_OK,
+ * W4A16_ERR_INVALID_ARG, W4A16_ERR_MISALIGNED or W4A16_ERR_LAUNCH.
+ */
+int w4a16_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
+                     struct ihipStream_t* stream);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int w4a16_version(void);
 

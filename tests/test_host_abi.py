@@ -219,3 +219,17 @@ def test_w4a8_grouped_argument_checks_without_launch():
     assert g([ok], 4, 32) == w4.W4A16_ERR_UNSUPPORTED
     assert g([ok, (A, A, A, A, A, 512, 352)], 4, 64) == w4.W4A16_ERR_UNSUPPORTED
     assert g([ok, (A, A, A, A, A + 2, 512, 256)], 4, 64) == w4.W4A16_ERR_MISALIGNED
+
+
+def test_read_probe_rejects_bad_arguments_before_launch():
+    """The read-bandwidth probe checks its arguments on the host; none of these
+    calls reaches a kernel (bytes == 0 returns before any launch)."""
+    ok, bad, mis = w4.W4A16_OK, w4.W4A16_ERR_INVALID_ARG, w4.W4A16_ERR_MISALIGNED
+    buf, sink = 0x10000, 0x20000  # never dereferenced on these paths
+    assert w4.read_probe_status(buf, 24, sink) == bad            # not a multiple of 16
+    assert w4.read_probe_status(buf, 0, None) == bad             # no sink
+    assert w4.read_probe_status(buf, 0, sink, 8188) == bad       # sink below 2,048 words
+    assert w4.read_probe_status(buf, 0, sink + 2) == mis         # sink not 4-byte aligned
+    assert w4.read_probe_status(0, 0, sink) == ok                # empty read: nothing launched
+    assert w4.read_probe_status(None, 32, sink) == bad           # null buffer
+    assert w4.read_probe_status(buf + 8, 32, sink) == mis        # buffer not 16-byte aligned

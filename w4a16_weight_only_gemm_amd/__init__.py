@@ -73,6 +73,7 @@ SIGNATURES = {
     "w4a8_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp]),
     "w4a16_status_string": (ctypes.c_char_p, [_int]),
     "w4a16_version": (_int, []),
+    "w4a16_read_probe": (_int, [_vp, _sz, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -343,3 +344,21 @@ def w4a8_gemm_grouped(problems, M: int, group: int, stream=None) -> None:
     rc = w4a8_gemm_grouped_status(problems, M, group, stream)
     if rc != W4A16_OK:
         raise W4A16Error(rc, "w4a8_gemm_grouped")
+
+
+READ_PROBE_SINK_BYTES = 8192
+
+
+def read_probe_status(buf, nbytes: int, sink, sink_bytes: int = READ_PROBE_SINK_BYTES,
+                      stream=None) -> int:
+    return int(_lib.w4a16_read_probe(_ptr(buf), nbytes, _ptr(sink), sink_bytes, _stream(stream)))
+
+
+def w4a16_read_probe(buf, nbytes: int, sink, sink_bytes: int = READ_PROBE_SINK_BYTES,
+                     stream=None) -> None:
+    """Read `nbytes` of device memory at `buf` once in the weight-stream access
+    pattern (a measurement aid: the practical read-bandwidth ceiling); one
+    32-bit wrapping sum per workgroup goes into the zero-filled `sink`."""
+    rc = read_probe_status(buf, nbytes, sink, sink_bytes, stream)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_read_probe")

@@ -275,6 +275,23 @@ const char* w4a16_status_string(int status) {
 
 int w4a16_version(void) { return 100; }
 
+int w4a16_read_probe(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
+                     hipStream_t stream) {
+  if (bytes % 16 != 0) return W4A16_ERR_INVALID_ARG;
+  if (sink == nullptr ||
+      sink_bytes < static_cast<size_t>(w4a16_internal::kReadProbeMaxWorkgroups) * 4)
+    return W4A16_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return W4A16_ERR_MISALIGNED;
+  if (bytes == 0) return W4A16_OK;
+  if (buf == nullptr) return W4A16_ERR_INVALID_ARG;
+  if (!aligned16(buf)) return W4A16_ERR_MISALIGNED;
+  const long long words = static_cast<long long>(bytes / 16);
+  return w4a16_internal::launch_read_probe(buf, words, static_cast<uint32_t*>(sink), stream) ==
+                 hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_LAUNCH;
+}
+
 }  // extern "C"
 
 namespace w4a16_internal {

@@ -112,6 +112,11 @@ hipError_t launch_large_streamk(const StreamKProblem* probs, int count, int M, i
 // Compute units of the current device (cached per device).
 int device_cus();
 
+// ---- read-bandwidth probe (w4a16_probe.hip) ----
+constexpr int kReadProbeMaxWorkgroups = 2048;  // sink words the probe may write
+int read_probe_workgroups();
+hipError_t launch_read_probe(const void* buf, long long words, uint32_t* sink, hipStream_t stream);
+
 // M-dispatch: W4A16_PATH_SKINNY or W4A16_PATH_LARGE for a supported shape.
 int choose_path(int M, int N, int K, int group);
 
