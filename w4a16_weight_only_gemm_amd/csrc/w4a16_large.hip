@@ -87,7 +87,7 @@ struct LgCfg {
 // SQ_LDS_BANK_CONFLICT over address patterns on gfx950). A fragment read
 // puts rows 0..15 in lanes 0..15 and pieces p + WPL j in lane group j; with
 // the plain p ^ r' two rows of one pass share a slot at group 128 (four
-// conflict cycles per read, half the kernel's LDS time). With the extra bit
+// conflict cycles per 128-bit read, as counted). With the extra bit
 // every pass reads 16 distinct slots at groups 128, 64 and 32, and the
 // staging writes (four rows of 16 pieces per wave) stay conflict-free.
 __device__ __forceinline__ int lg_slot(int piece, int row) {
