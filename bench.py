@@ -418,28 +418,37 @@ def read_ceiling(nbytes: int, buffers: int = 8, steps: int = 500, warmup: int = 
     return nbytes / (ms * 1e-3) / 1e9, ms
 
 
-def cpu_baseline(seconds_target: float = 15.0):
+def cpu_baseline(seconds_target: float = 15.0, single_seconds: float = 5.0):
     """The oracle, as it stands, on the host cores: decode layer sets (M = 1),
     projection after projection, layer after layer, until about
-    `seconds_target` seconds of CPU work; throughput in the metric's unit."""
+    `seconds_target` seconds of CPU work on all host threads, then about
+    `single_seconds` on one thread; throughput in the metric's unit."""
     import synth
     import oracle
+
+    def run(threads, seconds):
+        done_bytes, t_total, count, layer = 0, 0.0, 0, 0
+        while t_total < seconds:
+            for pi, p in enumerate(synth.LAYER_PROJECTIONS):
+                x, q, s = synth.layer_inputs(layer % 64, pi, 1)
+                t0 = time.perf_counter()
+                oracle.gemm(x, q, s, GROUP, threads=threads)
+                t_total += time.perf_counter() - t0
+                done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
+                count += 1
+                if threads == 1 and t_total >= seconds:
+                    break
+            layer += 1
+        return done_bytes / t_total / 1e12, count, layer, t_total
+
     threads = synth.default_threads()
-    done_bytes, t_total, count = 0, 0.0, 0
-    layer = 0
-    while t_total < seconds_target:
-        for pi, p in enumerate(synth.LAYER_PROJECTIONS):
-            x, q, s = synth.layer_inputs(layer % 64, pi, 1)
-            t0 = time.perf_counter()
-            oracle.gemm(x, q, s, GROUP, threads=threads)
-            t_total += time.perf_counter() - t0
-            done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
-            count += 1
-        layer += 1
-    return {"value": done_bytes / t_total / 1e12, "unit": "TB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{count} projection GEMMs (decode layer sets M=1, {layer} layers), "
-                      f"group {GROUP}), fp64 oracle, {t_total:.1f} s of CPU time"}
+    value, count, layers, t_total = run(threads, seconds_target)
+    single, count1, _, t1 = run(1, single_seconds)
+    return {"value": value, "unit": "TB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": single,
+            "sample": f"{count} projection GEMMs (decode layer sets M=1, {layers} layers, "
+                      f"group {GROUP}), fp64 oracle, {t_total:.1f} s on {threads} threads; "
+                      f"single thread: {count1} projection GEMMs, {t1:.1f} s"}
 
 
 COPY_BYTES = 512 << 20  # calibration kernels: 512 MiB written (fill), 512 MiB read (sum)
