@@ -203,8 +203,9 @@ def test_empty_n_tail_and_single_column():
 
 
 # Every kernel instantiation: group sizes 32..256 against row-block counts
-# 1, 2, 4 (M = 3, 24, 50) and two row tiles (M = 90), at K = 8 and 20 groups.
-MATRIX = [(M, g, kg) for g in (32, 64, 128, 256) for M in (3, 24, 50, 90) for kg in (8, 20)]
+# 1 (M = 3 and 12, the two one-row-block split-K shapes), 2 and 4 (M = 24, 50)
+# and two row tiles (M = 90), at K = 8 and 20 groups.
+MATRIX = [(M, g, kg) for g in (32, 64, 128, 256) for M in (3, 12, 24, 50, 90) for kg in (8, 20)]
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)

@@ -747,12 +747,6 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
 
 namespace {
 
-#ifndef W4A16_SKINNY_WAVES
-#define W4A16_SKINNY_WAVES 8
-#endif
-#ifndef W4A16_SKINNY_PREFETCH
-#define W4A16_SKINNY_PREFETCH 4
-#endif
 #ifndef W4A16_STREAMK_PREFETCH
 #define W4A16_STREAMK_PREFETCH 4
 #endif
@@ -760,36 +754,34 @@ namespace {
 #define W4A16_STREAMK_WG_PER_CU 2
 #endif
 
-constexpr int kSplitWaves = W4A16_SKINNY_WAVES;  // waves per workgroup (split-K ways)
-// groups in flight per wave; fewer at larger row-block counts, whose
-// activation fragments take RB times the registers
-template <int RB>
-constexpr int split_prefetch() {
-  return RB == 1 ? W4A16_SKINNY_PREFETCH : (RB == 2 ? 2 : 1);
-}
-
-template <int GS, int RB>
+// Split-K shape (waves per workgroup = split-K ways, groups in flight per
+// wave), by row-block count RB and, for one row block, by M. Measured on the
+// four projections of a decoder layer as separate calls: at M <= 7 eight waves
+// with one group in flight were fastest, at M = 8..16 four waves with two in
+// flight, where the activation loads (one 16-byte fragment per row and MFMA
+// step) grow with M and fewer, deeper-pipelined waves hide them better. Larger RB keeps eight waves and fewer groups in
+// flight, since its activation fragments take RB times the registers.
+template <int GS, int RB, int WAVES, int P>
 hipError_t launch_splitk_t(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 15) / 16, (a.M + 16 * RB - 1) / (16 * RB));
-  dim3 block(64 * kSplitWaves);
+  dim3 block(64 * WAVES);
   const uint16_t* x = a.x;
   const uint32_t* qw = a.qweight;
   const uint16_t* sp = a.scales;
   uint16_t* y = a.y;
   int M = a.M, N = a.N, K = a.K;
   void* kargs[] = {&x, &qw, &sp, &y, &M, &N, &K};
-  return hipLaunchKernel(
-      reinterpret_cast<const void*>(&splitk_kernel<GS, RB, kSplitWaves, split_prefetch<RB>()>),
-      grid, block, kargs, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&splitk_kernel<GS, RB, WAVES, P>), grid,
+                         block, kargs, 0, stream);
 }
 
 template <int GS>
 hipError_t launch_splitk_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_splitk_t<GS, 1>(a, stream);
-  if (a.M <= 32) return launch_splitk_t<GS, 2>(a, stream);
-  return launch_splitk_t<GS, 4>(a, stream);
+  if (a.M <= 7) return launch_splitk_t<GS, 1, 8, 1>(a, stream);
+  if (a.M <= 16) return launch_splitk_t<GS, 1, 4, 2>(a, stream);
+  if (a.M <= 32) return launch_splitk_t<GS, 2, 8, 2>(a, stream);
+  return launch_splitk_t<GS, 4, 8, 1>(a, stream);
 }
-
 
 #ifndef W4A16_STREAMK_WIDE_PREFETCH
 #define W4A16_STREAMK_WIDE_PREFETCH 1
