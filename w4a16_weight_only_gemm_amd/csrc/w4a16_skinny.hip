@@ -755,12 +755,11 @@ namespace {
 #endif
 
 // Split-K shape (waves per workgroup = split-K ways, groups in flight per
-// wave), by row-block count RB and, for one row block, by M. Measured on the
-// four projections of a decoder layer as separate calls: at M <= 7 eight waves
-// with one group in flight were fastest, at M = 8..16 four waves with two in
-// flight, where the activation loads (one 16-byte fragment per row and MFMA
-// step) grow with M and fewer, deeper-pipelined waves hide them better. Larger RB keeps eight waves and fewer groups in
-// flight, since its activation fragments take RB times the registers.
+// wave), by M. Measured on the four projections of a decoder layer as separate
+// calls: at M <= 7 eight waves with one group in flight were fastest; from
+// M = 8 on (one, two or four row blocks) four waves with two groups in flight,
+// as the activation loads (one 16-byte fragment per row and MFMA step) grow
+// with M and fewer, deeper-pipelined waves hide them better.
 template <int GS, int RB, int WAVES, int P>
 hipError_t launch_splitk_t(const GemmArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 15) / 16, (a.M + 16 * RB - 1) / (16 * RB));
@@ -779,8 +778,10 @@ template <int GS>
 hipError_t launch_splitk_g(const GemmArgs& a, hipStream_t stream) {
   if (a.M <= 7) return launch_splitk_t<GS, 1, 8, 1>(a, stream);
   if (a.M <= 16) return launch_splitk_t<GS, 1, 4, 2>(a, stream);
-  if (a.M <= 32) return launch_splitk_t<GS, 2, 8, 2>(a, stream);
-  return launch_splitk_t<GS, 4, 8, 1>(a, stream);
+  if (a.M <= 32) return launch_splitk_t<GS, 2, 4, 2>(a, stream);
+  // at 256-wide groups two groups in flight of four row blocks take every
+  // register of the SIMD; one in flight there
+  return launch_splitk_t<GS, 4, 4, (GS >= 256 ? 1 : 2)>(a, stream);
 }
 
 #ifndef W4A16_STREAMK_WIDE_PREFETCH
