@@ -115,8 +115,9 @@ def fit_step_model(rows, step_s, W: float, per_row_bytes: float, flops_per_row: 
     GEMM sweep (rows[i] activation rows take step_s[i] seconds): eta is the
     best bandwidth fraction seen on the memory line (W + rows * per_row_bytes
     per step), P the best arithmetic rate seen (rows * flops_per_row per step).
-    Both are envelopes, so the fitted model never predicts a time below a
-    measured one. Returns (eta, P, bend rows)."""
+    Both are the best values seen, so the fitted t_step is an optimistic
+    envelope: it is at most every measured time (a lower bound on the step
+    time), never above one. Returns (eta, P, bend rows)."""
     eta = max((W + m * per_row_bytes) / (BW * t) for m, t in zip(rows, step_s))
     P = max(m * flops_per_row / t for m, t in zip(rows, step_s))
     bend = crossover_streams(W, BW, flops_per_row, P, eta=eta, S=per_row_bytes / 2.0)

@@ -71,14 +71,20 @@ typedef enum {
 } w4a16_path;
 
 /* Bytes of the packed weights, ceil(N/16)*16*K/2, and of the packed scales,
- * ceil(N/16)*16*(K/group)*2. Return 0 for negative sizes, K not a multiple of
- * 32, or a group that is not a multiple of 32 or does not divide K. */
+ * ceil(N/16)*16*(K/group)*2. The pages fix no format; these sizes are the
+ * library's own: N is padded up to whole 16-column blocks (the width of one
+ * MFMA tile), so for N % 16 != 0 they exceed the unpadded N*K/2 and
+ * N*(K/group)*2, and every buffer handed to a GEMM call must hold the padded
+ * size. Return 0 for negative sizes, K not a multiple of 32, or a group that is
+ * not a multiple of 32 or does not divide K. */
 size_t w4a16_qweight_bytes(int N, int K);
 size_t w4a16_scales_bytes(int N, int K, int group);
 
 /*
- * Host-side packing into the packed format above. Pure and deterministic; no
- * device involvement.
+ * Host-side packing into the packed format above (the library's own format:
+ * the pages name 4-bit weights with group-wise scales, kongchang.com page,
+ * section "What Exactly Is This Stack", but no layout). Pure and
+ * deterministic; no device involvement.
  *   q          : host int8 [N][K], each code in -8..7 (read only)
  *   scales_in  : host fp16 bit patterns [N][K/group], row n = output column n
  *   qweight_out: host, w4a16_qweight_bytes(N, K) bytes, device arrangement above
@@ -92,7 +98,12 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
                uint16_t* scales_out, int N, int K, int group);
 
 /*
- * y = x . dequant(qweight, scales) on the GPU, overwriting y (no bias, no beta).
+ * y = x . dequant(qweight, scales) on the GPU, overwriting y (no bias, no beta):
+ * the W4A16 product of kongchang.com, section "What Exactly Is This Stack"
+ * (4-bit weights, 16-bit activations), with the weights read once and shared
+ * by all M rows (ai.satyajit.si, section "One weight read, shared by every
+ * stream"). Needs no workspace: every kernel behind it reduces within a
+ * workgroup, so calls on different streams may overlap.
  *   x       : device bf16 [M][K]
  *   qweight, scales : device copies of what w4a16_pack wrote for (N, K, group)
  *   y       : device bf16 [M][N]
@@ -106,13 +117,15 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
 int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
                int K, int group, struct ihipStream_t* stream);
 
-/* As w4a16_gemm, with the kernel path forced (W4A16_PATH_*); every path gives
- * a result within the same tolerance of the exact product. */
+/* As w4a16_gemm, with the kernel path forced (W4A16_PATH_*; the M-dispatch
+ * choice is the library's own, the pages give none); every path gives a result
+ * within the same tolerance of the exact product. */
 int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* y, int M,
                   int N, int K, int group, int path, struct ihipStream_t* stream);
 
 /*
- * Workspace of the streaming entry points below, for M activation rows and
+ * Workspace of the streaming entry points below (the library's own; the pages
+ * describe the product, not its scheduling), for M activation rows and
  * `total_columns` output columns (the sum of N over the problems of a call):
  * for M <= 16, per-block counters, one swap slot per output value and fp32
  * partial sums per workgroup; for M > 16, per-tile counters and partial sums.
@@ -126,7 +139,8 @@ int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* 
 size_t w4a16_workspace_bytes(int M, long long total_columns);
 
 /*
- * As w4a16_gemm, using a workspace (see w4a16_workspace_bytes(M, N)). For
+ * As w4a16_gemm (same operation, same citations), using a workspace (see
+ * w4a16_workspace_bytes(M, N)). For
  * M <= 16 this runs the streaming kernel: a persistent grid whose waves split
  * the packed weights into equal contiguous runs, combining the column blocks
  * cut between waves through the workspace. For larger M (group 32, 64 or
@@ -155,7 +169,8 @@ typedef struct w4a16_problem {
 /*
  * Several GEMMs that share M and the group size, in one launch (for example
  * the four projections of one layer: one weight stream and one launch instead
- * of four). `problems` is host memory read during the call; count is
+ * of four; the step time of ai.satyajit.si, section "One weight read, shared
+ * by every stream", is per step, not per matrix). `problems` is host memory read during the call; count is
  * 1..W4A16_MAX_PROBLEMS. The workspace is sized by
  * w4a16_workspace_bytes(M, sum of N). Each problem is validated as in
  * w4a16_gemm; with group 256 at M > 16 the problems run one after another on

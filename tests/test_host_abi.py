@@ -233,3 +233,36 @@ def test_read_probe_rejects_bad_arguments_before_launch():
     assert w4.read_probe_status(0, 0, sink) == ok                # empty read: nothing launched
     assert w4.read_probe_status(None, 32, sink) == bad           # null buffer
     assert w4.read_probe_status(buf + 8, 32, sink) == mis        # buffer not 16-byte aligned
+
+
+def test_binding_requires_padded_packed_sizes():
+    """With N % 16 != 0 the kernels read whole 16-column blocks of the packed
+    weights and scales: tensors sized to the unpadded N*K/2 and N*(K/group)*2
+    must be rejected by the binding before anything reaches the library."""
+    torch = pytest.importorskip("torch")
+    M, N, K, g = 3, 20, 256, 64
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    y = torch.zeros((M, N), dtype=torch.bfloat16)
+    qw_short = torch.zeros(N * K // 8, dtype=torch.int32)            # N*K/2 bytes
+    sp_short = torch.zeros(N * (K // g), dtype=torch.int16)          # N*(K/g)*2 bytes
+    qw_full = torch.zeros(w4.w4a16_qweight_bytes(N, K) // 4, dtype=torch.int32)
+    sp_full = torch.zeros(w4.w4a16_scales_bytes(N, K, g) // 2, dtype=torch.int16)
+    assert qw_full.numel() * 4 > qw_short.numel() * 4
+    for qw, sp, what in ((qw_short, sp_full, "qweight"), (qw_full, sp_short, "scales")):
+        with pytest.raises(ValueError, match=what):
+            w4.w4a16_gemm(x, qw, sp, y, M, N, K, g)
+        with pytest.raises(ValueError, match=what):
+            w4.w4a16_gemm_ex(x, qw, sp, y, M, N, K, g, w4.W4A16_PATH_SKINNY)
+        with pytest.raises(ValueError, match=what):
+            w4.w4a16_gemm_ws(x, qw, sp, y, M, N, K, g, torch.zeros(64, dtype=torch.int32))
+        with pytest.raises(ValueError, match=what):
+            w4.w4a16_gemm_grouped([(x, qw, sp, y, N, K)], M, g, torch.zeros(64, dtype=torch.int32))
+        xq = torch.zeros((M, K), dtype=torch.int8)
+        sx = torch.zeros((M,), dtype=torch.float32)
+        with pytest.raises(ValueError, match=what):
+            w4.w4a8_gemm(xq, sx, qw, sp, y, M, N, K, g)
+        with pytest.raises(ValueError, match=what):
+            w4.w4a8_gemm_grouped([(xq, sx, qw, sp, y, N, K)], M, g)
+    # padded sizes pass the size check and only then meet the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        w4.w4a16_gemm(x, qw_full, sp_full, y, M, N, K, g)

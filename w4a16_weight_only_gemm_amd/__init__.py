@@ -154,12 +154,22 @@ def _stream(stream):
     return stream.cuda_stream  # torch.cuda.Stream
 
 
+def _packed_bytes(N: int, K: int, group: int):
+    """Bytes the kernels read of the packed weights and scales: the device
+    arrangement pads N up to whole 16-column blocks (w4a16_qweight_bytes and
+    w4a16_scales_bytes), so a buffer of N * K / 2 bytes is too short when
+    N % 16 != 0."""
+    return int(_lib.w4a16_qweight_bytes(N, K)), int(_lib.w4a16_scales_bytes(N, K, group))
+
+
 def _check_tensors(x, qweight, scales, y, M, N, K, group):
-    """Size and dtype checks for torch tensors (raw addresses are the caller's business)."""
+    """Size and dtype checks for torch tensors (raw addresses are the caller's business).
+    Raises before anything reaches the library."""
     if _torch is None:
         return
+    qbytes, sbytes = _packed_bytes(N, K, group)
     need = {"x": (x, 2 * M * K, True), "y": (y, 2 * M * N, True),
-            "qweight": (qweight, N * K // 2, False), "scales": (scales, 2 * N * (K // group), False)}
+            "qweight": (qweight, qbytes, False), "scales": (scales, sbytes, False)}
     for name, (t, nbytes, bf16) in need.items():
         if isinstance(t, _torch.Tensor):
             if bf16 and t.dtype != _torch.bfloat16:
@@ -232,6 +242,10 @@ def w4a16_gemm_grouped(problems, M: int, group: int, workspace, workspace_bytes:
                        stream=None) -> None:
     """Several GEMMs sharing M and the group size; `problems` is a list of
     (x, qweight, scales, y, N, K) tuples or a make_problems() array."""
+    if not isinstance(problems, ctypes.Array):
+        for (x, qw, sp, y, N, K) in problems:
+            if group > 0 and K % group == 0:
+                _check_tensors(x, qw, sp, y, M, N, K, group)
     arr = problems if isinstance(problems, ctypes.Array) else make_problems(problems)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
@@ -274,8 +288,9 @@ def w4a8_gemm(xq, sx, qweight, scales, y, M: int, N: int, K: int, group: int,
     """y[M][N] (bf16) = W4A8 product of the codes and row scales written by
     w4a8_quantize and the packed weights written by w4a16_pack."""
     if group > 0 and K % group == 0:
+        qbytes, sbytes = _packed_bytes(N, K, group)
         _check_sizes(xq=(xq, M * K), sx=(sx, 4 * M), y=(y, 2 * M * N),
-                     qweight=(qweight, N * K // 2), scales=(scales, 2 * N * (K // group)))
+                     qweight=(qweight, qbytes), scales=(scales, sbytes))
     rc = _lib.w4a8_gemm(_ptr(xq), _ptr(sx), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
                         _stream(stream))
     if rc != W4A16_OK:
@@ -339,8 +354,9 @@ def w4a8_gemm_grouped(problems, M: int, group: int, stream=None) -> None:
     if not isinstance(problems, ctypes.Array):
         for (xq, sx, qw, sp, y, N, K) in problems:
             if group > 0 and K % group == 0:
+                qbytes, sbytes = _packed_bytes(N, K, group)
                 _check_sizes(xq=(xq, M * K), sx=(sx, 4 * M), y=(y, 2 * M * N),
-                             qweight=(qw, N * K // 2), scales=(sp, 2 * N * (K // group)))
+                             qweight=(qw, qbytes), scales=(sp, sbytes))
     rc = w4a8_gemm_grouped_status(problems, M, group, stream)
     if rc != W4A16_OK:
         raise W4A16Error(rc, "w4a8_gemm_grouped")

@@ -8,10 +8,10 @@
 namespace w4a16_internal {
 
 struct GemmArgs {
-  const uint16_t* x;        // bf16 [M][K]
-  const uint32_t* qweight;  // [N][K/8]
-  const uint16_t* scales;   // fp16 [K/group][N]
-  uint16_t* y;              // bf16 [M][N]
+  const uint16_t* x;        // bf16 [M][K], row-major
+  const uint32_t* qweight;  // packed tiles [ceil(N/16)][K/group][64 lanes][group/32 words]
+  const uint16_t* scales;   // fp16 [ceil(N/16)][K/group][16]
+  uint16_t* y;              // bf16 [M][N], row-major
   int M, N, K, group;
 };
 
