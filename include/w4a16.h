@@ -60,7 +60,8 @@ typedef enum {
   W4A16_ERR_INVALID_ARG = 1, /* null pointer, negative size, size mismatch, code out of -8..7 */
   W4A16_ERR_UNSUPPORTED = 2, /* shape outside the supported set (see w4a16_gemm) */
   W4A16_ERR_MISALIGNED = 3,  /* a device pointer is not 16-byte aligned */
-  W4A16_ERR_LAUNCH = 4       /* the HIP runtime refused the kernel launch */
+  W4A16_ERR_LAUNCH = 4,      /* the HIP runtime refused the kernel launch */
+  W4A16_ERR_TOO_LARGE = 5    /* needs more scratch than w4a16_gemm_noalloc's static array */
 } w4a16_status;
 
 /* Kernel paths; W4A16_PATH_AUTO lets the M-dispatch heuristic choose. */
@@ -155,6 +156,26 @@ size_t w4a16_workspace_bytes(int M, long long total_columns);
 int w4a16_gemm_ws(const void* x, const void* qweight, const void* scales, void* y, int M, int N,
                   int K, int group, void* workspace, size_t workspace_bytes,
                   struct ihipStream_t* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * GEMM and kernels as w4a16_gemm_ws, with the library's own static device
+ * array of W4A16_NOALLOC_SCRATCH_BYTES (96 MiB; each GPU the library runs on
+ * holds one until the process ends) in place of the caller's workspace. It
+ * allocates nothing and frees nothing. Arguments, validation and results as
+ * for w4a16_gemm; a shape whose workspace w4a16_workspace_bytes(M, N) exceeds
+ * the array returns W4A16_ERR_TOO_LARGE before anything runs (for example
+ * M <= 16 with N above about 1.4 million columns). The first call on a device
+ * clears the array once, with one fill kernel on `stream`; every call leaves
+ * its counters and slots at zero for the next. All calls on one GPU share
+ * that GPU's array: calls that can overlap on one GPU (different streams or
+ * host threads without ordering between them) race and give wrong results,
+ * so the caller orders them.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int w4a16_gemm_noalloc(const void* x, const void* qweight, const void* scales, void* y, int M,
+                       int N, int K, int group, struct ihipStream_t* stream);
 
 /* One GEMM of a grouped call: y[M][N] = x[M][K] . dequant(qweight, scales). */
 typedef struct w4a16_problem {

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert w4.w4a16_version() >= 100
-    for st in range(5):
+    for st in range(6):
         assert w4.w4a16_status_string(st).startswith("W4A16_")
     assert "unknown" in w4.w4a16_status_string(99)
 

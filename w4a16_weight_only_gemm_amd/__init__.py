@@ -33,6 +33,8 @@ W4A16_ERR_INVALID_ARG = 1
 W4A16_ERR_UNSUPPORTED = 2
 W4A16_ERR_MISALIGNED = 3
 W4A16_ERR_LAUNCH = 4
+W4A16_ERR_TOO_LARGE = 5
+W4A16_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 W4A16_PATH_AUTO = 0
 W4A16_PATH_SKINNY = 1
@@ -66,6 +68,7 @@ SIGNATURES = {
     "w4a16_workspace_bytes": (_sz, [_int, ctypes.c_longlong]),
     "w4a16_gemm_ws": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp, _sz, _vp]),
+    "w4a16_gemm_noalloc": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
     "w4a8_quantize": (_int, [_vp, _vp, _vp, _int, _int, _vp]),
     "w4a8_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
@@ -228,6 +231,24 @@ def w4a16_gemm_ws(x, qweight, scales, y, M: int, N: int, K: int, group: int, wor
                             _ptr(workspace), workspace_bytes, _stream(stream))
     if rc != W4A16_OK:
         raise W4A16Error(rc, "w4a16_gemm_ws")
+
+
+def w4a16_gemm_noalloc(x, qweight, scales, y, M: int, N: int, K: int, group: int,
+                       stream=None) -> None:
+    """As w4a16_gemm_ws, with the library's static device scratch in place of a
+    workspace (allocates nothing). Calls that can overlap on one GPU race."""
+    if group > 0 and K % group == 0:
+        _check_tensors(x, qweight, scales, y, M, N, K, group)
+    rc = _lib.w4a16_gemm_noalloc(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K, group,
+                                 _stream(stream))
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm_noalloc")
+
+
+def noalloc_status(x, qweight, scales, y, M, N, K, group, stream=None) -> int:
+    """Raw status of w4a16_gemm_noalloc, without raising (for tests of the error paths)."""
+    return int(_lib.w4a16_gemm_noalloc(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(y), M, N, K,
+                                       group, _stream(stream)))
 
 
 def make_problems(entries):

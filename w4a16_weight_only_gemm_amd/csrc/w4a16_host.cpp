@@ -269,6 +269,8 @@ const char* w4a16_status_string(int status) {
     case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED: shape or group size not supported";
     case W4A16_ERR_MISALIGNED: return "W4A16_ERR_MISALIGNED: device pointer not 16-byte aligned";
     case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH: kernel launch failed";
+    case W4A16_ERR_TOO_LARGE:
+      return "W4A16_ERR_TOO_LARGE: shape needs more scratch than the static array holds";
     default: return "unknown w4a16 status";
   }
 }
