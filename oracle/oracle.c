@@ -45,16 +45,20 @@
 
 /* ---- number decoding (bf16 and fp16 bit patterns to double) ---- */
 
-/* bf16 is the top half of an IEEE binary32. */
-double oracle_bf16_to_f64(uint16_t b) {
+/* bf16 is the top half of an IEEE binary32. (Internal copies of the two
+ * decoders are static, so that the compiler can inline them into the GEMM's
+ * loops; the exported names below only forward to them.) */
+static double bf16_to_f64(uint16_t b) {
   uint32_t u = (uint32_t)b << 16;
   float f;
   memcpy(&f, &u, sizeof f);
   return (double)f;
 }
 
+double oracle_bf16_to_f64(uint16_t b) { return bf16_to_f64(b); }
+
 /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
-double oracle_fp16_to_f64(uint16_t h) {
+static double fp16_to_f64(uint16_t h) {
   int sign = (h >> 15) & 1;
   int expo = (h >> 10) & 0x1F;
   int frac = h & 0x3FF;
@@ -68,6 +72,8 @@ double oracle_fp16_to_f64(uint16_t h) {
   }
   return sign ? -v : v;
 }
+
+double oracle_fp16_to_f64(uint16_t h) { return fp16_to_f64(h); }
 
 /* ---- the GEMM ---- */
 
@@ -89,12 +95,12 @@ static int oracle_columns(const oracle_job* j) {
     /* dequantize column n: w[k] = q[n][k] * s[n][floor(k / g)] */
     const int8_t* qn = j->q + (size_t)n * K;
     const uint16_t* sn = j->s + (size_t)n * G;
-    for (int k = 0; k < K; ++k) w[k] = (double)qn[k] * oracle_fp16_to_f64(sn[k / j->group]);
+    for (int k = 0; k < K; ++k) w[k] = (double)qn[k] * fp16_to_f64(sn[k / j->group]);
     /* accumulate: y[m][n] = sum_k x[m][k] * w[k], increasing k */
     for (int m = 0; m < j->M; ++m) {
       const uint16_t* xm = j->x + (size_t)m * K;
       double acc = 0.0;
-      for (int k = 0; k < K; ++k) acc += oracle_bf16_to_f64(xm[k]) * w[k];
+      for (int k = 0; k < K; ++k) acc += bf16_to_f64(xm[k]) * w[k];
       j->y[(size_t)m * j->N + n] = acc;
     }
   }
