@@ -202,6 +202,51 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
                        void* workspace, size_t workspace_bytes, struct ihipStream_t* stream);
 
 /*
+ * Planned calls: many GEMMs sharing M and the group size in ONE launch, with
+ * their descriptors in device memory, so that a whole step (for example the
+ * four projections of every layer of a stack: 256 GEMMs) pays one launch ramp
+ * and one tail instead of one per layer; the step time of ai.satyajit.si,
+ * section "One weight read, shared by every stream", is per step. The GEMMs of
+ * one plan are independent of each other (no output feeds an input). The
+ * planning is the library's own; the pages give none.
+ *
+ * w4a16_plan_bytes: bytes of the plan of `count` problems (1..4096), or 0.
+ *
+ * w4a16_plan_build: writes the plan of `count` problems (host memory,
+ *   read during the call; each validated as in w4a16_gemm) at M >= 1 rows and
+ *   `group` into `plan` (host memory, plan_bytes >= w4a16_plan_bytes(count)):
+ *   each problem's descriptor and place in one persistent stream-K launch,
+ *   sized for the current device's compute units, with a checksum. Pure host
+ *   code. M <= 16 takes the streaming kernel (any supported group); M > 16 the
+ *   MFMA tile engine, which needs group 32, 64 or 128 and packed weights and
+ *   activations of each problem below 4 GB (else W4A16_ERR_UNSUPPORTED).
+ *   Returns W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED or
+ *   W4A16_ERR_MISALIGNED; on an error the plan holds nothing usable.
+ *
+ * w4a16_plan_workspace_bytes: workspace bytes of a built plan (0 if `plan` is
+ *   not one). The workspace follows the rules of w4a16_workspace_bytes:
+ *   caller-owned device memory, 256-byte aligned, zero-filled once before its
+ *   first use, left with zero counters by every call, one call at a time.
+ *
+ * w4a16_gemm_planned: runs every GEMM of the plan in one launch on `stream`.
+ *   `plan` is the host plan, `plan_dev` a byte copy of it in device memory
+ *   (16-byte aligned) that the caller made (for example once, when the
+ *   buffers of the plan are allocated); the kernels read the descriptors from
+ *   plan_dev. A device copy whose checksum differs from the host plan's makes
+ *   the launch do nothing. The buffers the plan names must stay valid while
+ *   calls run. Asynchronous; allocates nothing. Returns W4A16_OK,
+ *   W4A16_ERR_INVALID_ARG (not a plan, null or too small workspace),
+ *   W4A16_ERR_MISALIGNED or W4A16_ERR_LAUNCH.
+ */
+#define W4A16_PLAN_MAX_PROBLEMS 4096
+size_t w4a16_plan_bytes(int count);
+int w4a16_plan_build(const w4a16_problem* problems, int count, int M, int group, void* plan,
+                     size_t plan_bytes);
+size_t w4a16_plan_workspace_bytes(const void* plan);
+int w4a16_gemm_planned(const void* plan, const void* plan_dev, void* workspace,
+                       size_t workspace_bytes, struct ihipStream_t* stream);
+
+/*
  * W4A8: the activations quantized to int8 with one scale per row, times the
  * same packed 4-bit weights, on the int8 MFMA. Once the rows' arithmetic
  * rather than the weight stream bounds a step, cheaper arithmetic is what

@@ -41,6 +41,7 @@ W4A16_PATH_SKINNY = 1
 W4A16_PATH_LARGE = 2
 
 W4A16_MAX_PROBLEMS = 8
+W4A16_PLAN_MAX_PROBLEMS = 4096
 
 
 class w4a16_problem(ctypes.Structure):
@@ -69,6 +70,10 @@ SIGNATURES = {
     "w4a16_gemm_ws": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_gemm_grouped": (_int, [_vp, _int, _int, _int, _vp, _sz, _vp]),
     "w4a16_gemm_noalloc": (_int, [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
+    "w4a16_plan_bytes": (_sz, [_int]),
+    "w4a16_plan_build": (_int, [_vp, _int, _int, _int, _vp, _sz]),
+    "w4a16_plan_workspace_bytes": (_sz, [_vp]),
+    "w4a16_gemm_planned": (_int, [_vp, _vp, _vp, _sz, _vp]),
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
     "w4a8_quantize": (_int, [_vp, _vp, _vp, _int, _int, _vp]),
     "w4a8_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
@@ -274,6 +279,55 @@ def w4a16_gemm_grouped(problems, M: int, group: int, workspace, workspace_bytes:
                                  _ptr(workspace), workspace_bytes, _stream(stream))
     if rc != W4A16_OK:
         raise W4A16Error(rc, "w4a16_gemm_grouped")
+
+
+def w4a16_plan_bytes(count: int) -> int:
+    return int(_lib.w4a16_plan_bytes(count))
+
+
+def plan_build_status(problems, M: int, group: int):
+    """(status, plan) of w4a16_plan_build: `plan` is a host uint8 array."""
+    arr = problems if isinstance(problems, ctypes.Array) else make_problems(problems)
+    nbytes = w4a16_plan_bytes(len(arr))
+    plan = np.zeros(max(1, nbytes), dtype=np.uint8)
+    rc = int(_lib.w4a16_plan_build(ctypes.cast(arr, ctypes.c_void_p), len(arr), M, group,
+                                   plan.ctypes.data, nbytes))
+    return rc, plan
+
+
+def w4a16_plan_build(problems, M: int, group: int) -> np.ndarray:
+    """Host plan (uint8 array) of GEMMs sharing M and the group size, from
+    (x, qweight, scales, y, N, K) tuples or a make_problems() array; copy it to
+    device memory and pass both copies to w4a16_gemm_planned."""
+    if not isinstance(problems, ctypes.Array):
+        for (x, qw, sp, y, N, K) in problems:
+            if group > 0 and K % group == 0:
+                _check_tensors(x, qw, sp, y, M, N, K, group)
+    rc, plan = plan_build_status(problems, M, group)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_plan_build")
+    return plan
+
+
+def w4a16_plan_workspace_bytes(plan: np.ndarray) -> int:
+    return int(_lib.w4a16_plan_workspace_bytes(plan.ctypes.data))
+
+
+def planned_status(plan: np.ndarray, plan_dev, workspace, workspace_bytes: int,
+                   stream=None) -> int:
+    return int(_lib.w4a16_gemm_planned(plan.ctypes.data, _ptr(plan_dev), _ptr(workspace),
+                                       workspace_bytes, _stream(stream)))
+
+
+def w4a16_gemm_planned(plan: np.ndarray, plan_dev, workspace, workspace_bytes: int | None = None,
+                       stream=None) -> None:
+    """Every GEMM of a plan in one launch; plan_dev is a device copy of `plan`. A
+    plan whose w4a16_plan_workspace_bytes is 0 takes workspace=None."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = planned_status(plan, plan_dev, workspace, workspace_bytes, stream)
+    if rc != W4A16_OK:
+        raise W4A16Error(rc, "w4a16_gemm_planned")
 
 
 def grouped_status(problems, M, group, workspace, workspace_bytes, stream=None) -> int:

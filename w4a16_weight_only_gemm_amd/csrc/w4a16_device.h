@@ -26,6 +26,14 @@ __device__ __forceinline__ gptr<T> to_global(T* p) {
   return (gptr<T>)(p);  // address-space cast (generic to global)
 }
 
+// A value read through the constant address space: the memory must not be
+// written while the kernel runs (a plan's problem table), and a uniform
+// address then becomes a scalar load into SGPRs.
+template <typename T>
+__device__ __forceinline__ T load_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt left at their maxima). Stores
 // and loads share the vector-memory counter but may retire out of order, so
 // while a store is outstanding the compiler must wait for every load in

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "../../include/w4a16.h"
 #include "w4a16_launch.h"
@@ -22,6 +23,43 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool group_supported(int group) {
   return group == 32 || group == 64 || group == 128 || group == 256;
+}
+
+// Byte layout of a plan of `count` problems: header, problem table (room for
+// the larger of the two entry types), first problem per workgroup.
+struct PlanLayout {
+  size_t table_off, wgfirst_off, total;
+};
+
+PlanLayout plan_layout(int count) {
+  using namespace w4a16_internal;
+  const size_t entry = sizeof(StreamKProblem) > sizeof(LargeProblem) ? sizeof(StreamKProblem)
+                                                                      : sizeof(LargeProblem);
+  PlanLayout l;
+  l.table_off = kPlanHeaderBytes;
+  l.wgfirst_off = l.table_off + (entry * count + 255) / 256 * 256;
+  l.total = l.wgfirst_off + static_cast<size_t>(kPlanMaxWorkgroups) * sizeof(int);
+  return l;
+}
+
+// FNV-1a, 64-bit.
+uint64_t fnv1a64(const unsigned char* p, size_t n) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
+// The header of a host plan, or nullptr if it is not one this library built.
+const w4a16_internal::PlanHeader* plan_header(const void* plan) {
+  using namespace w4a16_internal;
+  if (!plan || (reinterpret_cast<uintptr_t>(plan) & 7u) != 0) return nullptr;
+  const PlanHeader* h = static_cast<const PlanHeader*>(plan);
+  if (h->magic != kPlanMagic || h->version != kPlanVersion) return nullptr;
+  if (h->kind != kPlanKindStreamK && h->kind != kPlanKindLarge) return nullptr;
+  return h;
 }
 
 }  // namespace
@@ -181,6 +219,104 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
     err = w4a16_internal::launch_streamk(probs, count, M, group, part,
                                          reinterpret_cast<uint32_t*>(slots), counters, stream);
   }
+  return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+size_t w4a16_plan_bytes(int count) {
+  if (count < 1 || count > w4a16_internal::kPlanMaxProblems) return 0;
+  return plan_layout(count).total;
+}
+
+int w4a16_plan_build(const w4a16_problem* problems, int count, int M, int group, void* plan,
+                     size_t plan_bytes) {
+  using namespace w4a16_internal;
+  if (!problems || !plan || count < 1 || count > kPlanMaxProblems || M < 1)
+    return W4A16_ERR_INVALID_ARG;
+  const PlanLayout lay = plan_layout(count);
+  if (plan_bytes < lay.total) return W4A16_ERR_INVALID_ARG;
+  if (!group_supported(group)) return W4A16_ERR_UNSUPPORTED;
+  long long columns = 0;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem& p = problems[i];
+    if (p.N < 0 || p.K < 0) return W4A16_ERR_INVALID_ARG;
+    if (!p.x || !p.qweight || !p.scales || !p.y) return W4A16_ERR_INVALID_ARG;
+    if (p.N < 1 || p.K < 1 || p.K % group != 0) return W4A16_ERR_UNSUPPORTED;
+    if (!aligned16(p.x) || !aligned16(p.qweight) || !aligned16(p.scales) || !aligned16(p.y))
+      return W4A16_ERR_MISALIGNED;
+    columns += p.N;
+  }
+  std::vector<StreamKProblem> sk(count);
+  for (int i = 0; i < count; ++i) {
+    sk[i] = StreamKProblem{};
+    sk[i].x = static_cast<const uint16_t*>(problems[i].x);
+    sk[i].qw = static_cast<const uint32_t*>(problems[i].qweight);
+    sk[i].sp = static_cast<const uint16_t*>(problems[i].scales);
+    sk[i].y = static_cast<uint16_t*>(problems[i].y);
+    sk[i].N = problems[i].N;
+    sk[i].K = problems[i].K;
+  }
+  unsigned char* out = static_cast<unsigned char*>(plan);
+  std::memset(out, 0, lay.total);
+  PlanHeader h = {};
+  h.magic = kPlanMagic;
+  h.version = kPlanVersion;
+  h.count = count;
+  h.M = M;
+  h.group = group;
+  h.table_off = static_cast<int>(lay.table_off);
+  h.wgfirst_off = static_cast<int>(lay.wgfirst_off);
+  h.total_columns = columns;
+  int* wgfirst = reinterpret_cast<int*>(out + lay.wgfirst_off);
+  if (M <= 16) {
+    if (build_streamk_plan(sk.data(), count, M, group, h, wgfirst) != 0)
+      return W4A16_ERR_UNSUPPORTED;
+    std::memcpy(out + lay.table_off, sk.data(), sizeof(StreamKProblem) * count);
+  } else {
+    // the MFMA tile engine: groups 32, 64 and 128 and 32-bit buffer ranges
+    if (!large_streamk_fits(sk.data(), count, M, group)) return W4A16_ERR_UNSUPPORTED;
+    std::vector<LargeProblem> lg(count);
+    for (int i = 0; i < count; ++i) {
+      lg[i] = LargeProblem{};
+      lg[i].x = sk[i].x;
+      lg[i].qw = sk[i].qw;
+      lg[i].sp = sk[i].sp;
+      lg[i].y = sk[i].y;
+      lg[i].N = sk[i].N;
+      lg[i].K = sk[i].K;
+    }
+    if (build_large_plan(lg.data(), count, M, group, h, wgfirst) != 0)
+      return W4A16_ERR_UNSUPPORTED;
+    std::memcpy(out + lay.table_off, lg.data(), sizeof(LargeProblem) * count);
+  }
+  // the checksum covers every byte of the plan, its own field read as zero
+  h.checksum = 0;
+  std::memcpy(out, &h, sizeof(h));
+  h.checksum = fnv1a64(out, lay.total);
+  std::memcpy(out, &h, sizeof(h));
+  return W4A16_OK;
+}
+
+size_t w4a16_plan_workspace_bytes(const void* plan) {
+  const w4a16_internal::PlanHeader* h = plan_header(plan);
+  return h ? static_cast<size_t>(h->workspace_bytes) : 0;
+}
+
+int w4a16_gemm_planned(const void* plan, const void* plan_dev, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  using namespace w4a16_internal;
+  const PlanHeader* hp = plan_header(plan);
+  if (!hp || !plan_dev) return W4A16_ERR_INVALID_ARG;
+  const PlanHeader h = *hp;
+  if (!aligned16(plan_dev)) return W4A16_ERR_MISALIGNED;
+  if (h.workspace_bytes > 0) {  // a plan of whole tiles needs none
+    if (!workspace || workspace_bytes < static_cast<size_t>(h.workspace_bytes))
+      return W4A16_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return W4A16_ERR_MISALIGNED;
+  }
+  const unsigned char* dev = static_cast<const unsigned char*>(plan_dev);
+  char* ws = static_cast<char*>(workspace);
+  const hipError_t err = h.kind == kPlanKindStreamK ? launch_streamk_planned(h, dev, ws, stream)
+                                                    : launch_large_planned(h, dev, ws, stream);
   return err == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 

@@ -46,6 +46,7 @@
 // beyond N are clamped on load; neither is stored.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "w4a16_device.h"
@@ -358,11 +359,22 @@ __device__ __forceinline__ int lg_unit_owner(long long u, long long U, int NW) {
 // A part is stored register-major (float r of lane l at r * 64 + l of the
 // wave's region), the layout every workgroup shares for a tile, so each
 // store and load instruction covers 256 contiguous bytes.
-template <int GS, int MB>
+// TILES (planned calls with many tiles): no stream-K split; logical
+// workgroup w runs whole tiles w, w + NW, w + 2 NW, ... of the plan's tile
+// sequence (problem by problem, row tiles of a column tile consecutive), so
+// the row tiles that share a column tile's weights run at the same time on
+// workgroups of one XCD and read those weights once through its L2. Needs no
+// workspace; used when there are enough tiles to balance the workgroups.
+template <int GS, int MB, bool TABLE, bool TILES>
 __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const LargeSKArgs args) {
   using C = LgCfg<GS, MB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lg_lds[];
   __shared__ int last_flag;
+  // A planned call whose device plan is not the one the host launched from
+  // does nothing (every workgroup takes the same exit, before any barrier).
+  if constexpr (TABLE) {
+    if (load_const(args.plan_checksum) != args.checksum) return;
+  }
   const long long U = args.units;
   const int NW = args.nwg;
   const int wg = xcd_grouped(blockIdx.x, NW);
@@ -370,11 +382,39 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
   const long long u1 = lg_first_unit(wg + 1, U, NW);
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
 
+  // Descriptor of problem p: in the kernel arguments, or in the device table
+  // of a planned call.
+  auto prob_at = [&](int p) -> LargeProblem {
+    {
+      // field by field, as scalar loads from the table or the kernel
+      // arguments (both read-only here)
+      const LargeProblem* e = (TABLE ? args.table : args.prob) + p;
+      LargeProblem r;
+      r.x = load_const(&e->x);
+      r.qw = load_const(&e->qw);
+      r.sp = load_const(&e->sp);
+      r.y = load_const(&e->y);
+      r.N = load_const(&e->N);
+      r.K = load_const(&e->K);
+      r.G = load_const(&e->G);
+      r.NCB = load_const(&e->NCB);
+      r.MT = load_const(&e->MT);
+      r.NT = load_const(&e->NT);
+      r.KT = load_const(&e->KT);
+      r.u_begin = load_const(&e->u_begin);
+      r.t_begin = load_const(&e->t_begin);
+      return r;
+    }
+  };
+  // Problem of a unit of this workgroup's range (uniform): a forward scan
+  // over the problems' first units, from problem 0 or, in a table, from the
+  // problem holding the workgroup's first unit. One scalar load per step, so
+  // no descriptor stays live in registers (an unrolled compare over all eight
+  // kept them in SGPRs, which spilled 16 bytes per lane at 128-row tiles).
   auto problem_of = [&](long long u) {
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxProblems; ++i)
-      if (i < args.nprob && u >= args.prob[i].u_begin) p = i;
+    const auto* tab = TABLE ? args.table : args.prob;
+    int p = TABLE ? load_const(args.wgfirst + wg) : 0;
+    while (p + 1 < args.nprob && load_const(&tab[p + 1].u_begin) <= u) ++p;
     return p;
   };
   auto part_of = [&](int w, int slot) {
@@ -383,11 +423,27 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
 
   TileEngine<GS, MB> e;
   Acc<MB> acc;
+  if constexpr (TILES) {
+    // args.units counts tiles here; the problem index only moves forward
+    const auto* tab = args.table;
+    int p = 0;
+    for (long long t = wg; t < U; t += NW) {
+      while (p + 1 < args.nprob && load_const(&tab[p + 1].t_begin) <= t) p = uniform(p + 1);
+      const LargeProblem pr = prob_at(p);
+      const int tile = uniform(static_cast<int>(t - pr.t_begin));
+      e.setup(lg_lds, pr.x, pr.qw, pr.sp, args.M, pr.N, pr.K, (tile % pr.MT) * C::Rows,
+              tile / pr.MT);
+      zero(acc);
+      e.kloop(acc, 0, pr.KT);
+      e.store(acc, pr.y);
+    }
+    return;
+  }
   int fin_p[2] = {-1, -1}, fin_tile[2] = {0, 0};
   int nfin = 0;
   for (long long u = u0; u < u1;) {
     const int p = problem_of(u);
-    const LargeProblem& pr = args.prob[p];
+    const LargeProblem& pr = prob_at(p);
     const int v = uniform(static_cast<int>(u - pr.u_begin));
     const int tile = uniform(v / pr.KT);
     const int k0 = v - tile * pr.KT;
@@ -434,7 +490,7 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
   // Finalize the tiles whose last part arrived here: sum the parts in
   // workgroup order, store bf16, reset the counter for the next call.
   for (int i = 0; i < nfin; ++i) {
-    const LargeProblem& pr = args.prob[fin_p[i]];
+    const LargeProblem& pr = prob_at(fin_p[i]);
     const int tile = fin_tile[i];
     const long long tile_u0 = pr.u_begin + static_cast<long long>(tile) * pr.KT;
     const int wfirst = lg_unit_owner(tile_u0, U, NW);
@@ -494,44 +550,56 @@ hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
-template <int GS, int MB>
-hipError_t launch_large_sk_t(LargeSKArgs& sk, hipStream_t stream) {
-  using C = LgCfg<GS, MB>;
-  long long units = 0;
-  int tiles = 0;
-  for (int i = 0; i < sk.nprob; ++i) {
-    LargeProblem& p = sk.prob[i];
-    p.G = p.K / GS;
+// Units and tiles of the problems for tiles of `rows` rows (group GS): fills
+// the problems' offsets and returns the unit count; *tiles_out is the tile
+// count, *nwg_out the workgroups of the persistent grid.
+long long plan_large_probs(LargeProblem* probs, int count, int M, int group, int rows,
+                           long long* tiles_out, int* nwg_out) {
+  const int T = kLgKT / group;  // groups per k-tile
+  long long units = 0, tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    LargeProblem& p = probs[i];
+    p.G = p.K / group;
     p.NCB = (p.N + 15) / 16;
-    p.MT = (sk.M + C::Rows - 1) / C::Rows;
+    p.MT = (M + rows - 1) / rows;
     p.NT = (p.NCB + kLgBlocks - 1) / kLgBlocks;
-    p.KT = (p.G + C::T - 1) / C::T;
+    p.KT = (p.G + T - 1) / T;
     p.u_begin = units;
-    p.t_begin = tiles;
+    p.t_begin = static_cast<int>(tiles);
     units += static_cast<long long>(p.MT) * p.NT * p.KT;
-    tiles += p.MT * p.NT;
+    tiles += static_cast<long long>(p.MT) * p.NT;
   }
-  sk.units = units;
   long long nwg = static_cast<long long>(device_cus());
   if (nwg > kLargeMaxWorkgroups) nwg = kLargeMaxWorkgroups;
   if (nwg > units) nwg = units;  // every workgroup owns at least one unit
-  sk.nwg = static_cast<int>(nwg);
-  const void* fn = reinterpret_cast<const void*>(&large_streamk_kernel<GS, MB>);
+  *tiles_out = tiles;
+  *nwg_out = static_cast<int>(nwg);
+  return units;
+}
+
+template <int GS, int MB, bool TABLE = false, bool TILES = false>
+hipError_t launch_large_sk_t(LargeSKArgs& sk, hipStream_t stream) {
+  using C = LgCfg<GS, MB>;
+  if constexpr (!TABLE) {
+    long long tiles = 0;
+    sk.units = plan_large_probs(sk.prob, sk.nprob, sk.M, GS, C::Rows, &tiles, &sk.nwg);
+  }
+  const void* fn = reinterpret_cast<const void*>(&large_streamk_kernel<GS, MB, TABLE, TILES>);
   const size_t lds = C::Lds;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
   void* kargs[] = {&sk};
-  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(nwg)), dim3(kLgThreads), kargs, lds,
+  return hipLaunchKernel(fn, dim3(static_cast<unsigned>(sk.nwg)), dim3(kLgThreads), kargs, lds,
                          stream);
 }
 
-template <int MB>
+template <int MB, bool TABLE = false, bool TILES = false>
 hipError_t launch_large_sk_g(LargeSKArgs& sk, int group, hipStream_t stream) {
   switch (group) {
-    case 32: return launch_large_sk_t<32, MB>(sk, stream);
-    case 64: return launch_large_sk_t<64, MB>(sk, stream);
-    case 128: return launch_large_sk_t<128, MB>(sk, stream);
+    case 32: return launch_large_sk_t<32, MB, TABLE, TILES>(sk, stream);
+    case 64: return launch_large_sk_t<64, MB, TABLE, TILES>(sk, stream);
+    case 128: return launch_large_sk_t<128, MB, TABLE, TILES>(sk, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -596,6 +664,73 @@ hipError_t launch_large_streamk(const StreamKProblem* probs, int count, int M, i
     case 32: return launch_large_sk_g<2>(sk, group, stream);
     case 64: return launch_large_sk_g<4>(sk, group, stream);
     default: return launch_large_sk_g<8>(sk, group, stream);
+  }
+}
+
+int build_large_plan(LargeProblem* probs, int count, int M, int group, PlanHeader& h,
+                     int* wgfirst) {
+  if (!large_supported(group)) return -1;
+  const int rows = large_streamk_rows(M);
+  long long tiles = 0;
+  int nwg = 0;
+  const long long units = plan_large_probs(probs, count, M, group, rows, &tiles, &nwg);
+  if (nwg < 1 || nwg > kPlanMaxWorkgroups) return -1;
+  h.kind = kPlanKindLarge;
+  h.rows = rows;
+  h.grid = nwg;
+  h.nwaves = nwg;
+  h.units = units;
+  // Enough tiles (at least kPlanTilesPerWorkgroup per workgroup): whole tiles
+  // round robin, no workspace. The grid never exceeds the tile count.
+  if (tiles >= static_cast<long long>(kPlanTilesPerWorkgroup) * nwg) {
+    h.tiles = 1;
+    h.units = tiles;
+    for (int w = 0; w < nwg; ++w) wgfirst[w] = 0;  // unused in this form
+    h.counters_off = h.slots_off = h.part_off = 0;
+    h.workspace_bytes = 0;
+    return 0;
+  }
+  h.tiles = 0;
+  h.lds_bytes = 0;  // fixed by the kernel's group size and tile rows
+  // logical workgroup w's first unit is units * w / nwg
+  int p = 0;
+  for (int w = 0; w < nwg; ++w) {
+    const long long u = units * w / nwg;
+    while (p + 1 < count && probs[p + 1].u_begin <= u) ++p;
+    wgfirst[w] = p;
+  }
+  h.counters_off = 0;
+  h.slots_off = 0;
+  h.part_off = (tiles * 4 + 255) / 256 * 256;
+  h.workspace_bytes = h.part_off + static_cast<long long>(large_streamk_part_bytes(M));
+  return 0;
+}
+
+hipError_t launch_large_planned(const PlanHeader& h, const unsigned char* plan_dev, char* ws,
+                                hipStream_t stream) {
+  LargeSKArgs sk = {};
+  sk.table = reinterpret_cast<const LargeProblem*>(plan_dev + h.table_off);
+  sk.wgfirst = reinterpret_cast<const int*>(plan_dev + h.wgfirst_off);
+  sk.plan_checksum =
+      reinterpret_cast<const unsigned long long*>(plan_dev + offsetof(PlanHeader, checksum));
+  sk.checksum = h.checksum;
+  sk.nprob = h.count;
+  sk.M = h.M;
+  sk.units = h.units;
+  sk.nwg = h.grid;
+  sk.part = reinterpret_cast<float*>(ws + h.part_off);
+  sk.counters = reinterpret_cast<int*>(ws + h.counters_off);
+  if (h.tiles) {
+    switch (h.rows) {
+      case 32: return launch_large_sk_g<2, true, true>(sk, h.group, stream);
+      case 64: return launch_large_sk_g<4, true, true>(sk, h.group, stream);
+      default: return launch_large_sk_g<8, true, true>(sk, h.group, stream);
+    }
+  }
+  switch (h.rows) {
+    case 32: return launch_large_sk_g<2, true>(sk, h.group, stream);
+    case 64: return launch_large_sk_g<4, true>(sk, h.group, stream);
+    default: return launch_large_sk_g<8, true>(sk, h.group, stream);
   }
 }
 

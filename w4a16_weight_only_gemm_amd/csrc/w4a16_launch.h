@@ -42,7 +42,14 @@ struct StreamKProblem {
 };
 
 struct StreamKArgs {
-  StreamKProblem prob[kMaxProblems];
+  StreamKProblem prob[kMaxProblems];  // the problems, unless `table` is set
+  // Planned calls: the problems in a device table (nprob entries) and, per
+  // workgroup, the problem holding its first unit; the kernel checks the
+  // device plan's checksum against `checksum` before doing anything.
+  const StreamKProblem* table;
+  const int* wgfirst;
+  const unsigned long long* plan_checksum;
+  unsigned long long checksum;
   int nprob;
   int M;
   long long units;          // total units over all problems
@@ -89,7 +96,11 @@ struct LargeProblem {
 };
 
 struct LargeSKArgs {
-  LargeProblem prob[kMaxProblems];
+  LargeProblem prob[kMaxProblems];  // the problems, unless `table` is set
+  const LargeProblem* table;        // planned calls, as in StreamKArgs
+  const int* wgfirst;
+  const unsigned long long* plan_checksum;
+  unsigned long long checksum;
   int nprob;
   int M;
   long long units;          // total units over all problems
@@ -108,6 +119,58 @@ size_t large_streamk_part_bytes(int M);
 bool large_streamk_fits(const StreamKProblem* probs, int count, int M, int group);
 hipError_t launch_large_streamk(const StreamKProblem* probs, int count, int M, int group,
                                 float* part, int* counters, hipStream_t stream);
+
+// ---- planned calls: many problems, descriptors in device memory ----
+//
+// A plan is a byte image built on the host (w4a16_plan_build) and copied by
+// the caller to device memory: a header, then the problem table (StreamKProblem
+// or LargeProblem entries, as the kernel reads them), then the first problem
+// of every workgroup. The host launches from its copy; the kernels read the
+// table from the device copy.
+constexpr uint32_t kPlanMagic = 0x4C503457u;  // "W4PL"
+constexpr uint32_t kPlanVersion = 1;
+constexpr int kPlanKindStreamK = 1;  // M <= 16: streaming kernel
+constexpr int kPlanKindLarge = 2;    // M > 16: MFMA tile engine
+constexpr int kPlanMaxProblems = 4096;
+constexpr int kPlanMaxWorkgroups = 1024;  // both grids stay below this
+constexpr int kPlanTilesPerWorkgroup = 16;  // large plans: whole tiles from this many per workgroup
+
+struct PlanHeader {
+  uint32_t magic, version;
+  int kind, count, M, group;
+  int grid;          // workgroups launched
+  int nwaves;        // stream-K: waves owning units; large: workgroups owning units
+  int nbw;           // stream-K: column blocks per super-block
+  int rows;          // large: tile rows
+  int xlds;          // stream-K: activations staged in LDS
+  int lds_bytes;     // dynamic LDS per workgroup
+  int lds_part_off;  // stream-K: LDS offset (4-byte words) of the waves' parts
+  int table_off;     // byte offset of the problem table
+  int wgfirst_off;   // byte offset of the per-workgroup first problem
+  int tiles;         // large: whole tiles dealt round robin (no workspace), else stream-K
+  long long units;
+  long long total_columns;
+  long long counters_off, slots_off, part_off;  // byte offsets in the workspace
+  long long workspace_bytes;
+  unsigned long long checksum;  // FNV-1a (64-bit) of every plan byte, this field read as 0
+  unsigned long long pad1[5];
+};
+static_assert(sizeof(PlanHeader) % 16 == 0, "16-byte multiple");
+constexpr size_t kPlanHeaderBytes = 256;
+static_assert(sizeof(PlanHeader) <= kPlanHeaderBytes, "header fits its slot");
+
+// Plans of validated problems (pointers, N and K set): fill the problems'
+// offsets, the header's launch and workspace fields and the first problem of
+// every workgroup (at most kPlanMaxWorkgroups). Return 0, or -1 when the
+// problems do not fit the form.
+int build_streamk_plan(StreamKProblem* probs, int count, int M, int group, PlanHeader& h,
+                       int* wgfirst);
+int build_large_plan(LargeProblem* probs, int count, int M, int group, PlanHeader& h,
+                     int* wgfirst);
+hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan_dev, char* ws,
+                                  hipStream_t stream);
+hipError_t launch_large_planned(const PlanHeader& h, const unsigned char* plan_dev, char* ws,
+                                hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cus();

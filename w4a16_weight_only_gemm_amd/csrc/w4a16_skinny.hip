@@ -32,6 +32,7 @@
 //   projections of a layer) can share one launch.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "../../include/w4a16.h"
@@ -419,9 +420,18 @@ struct UnitLoads {
   u32x4 x[WPL];
 };
 
-template <int GS, int WAVES, int P, bool XLDS, int NBW>
-__global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs args) {
+// With staged activations (one column block per unit) the kernel runs two
+// 8-wave workgroups per compute unit, i.e. four waves per SIMD: at most 128
+// VGPRs (the table form would otherwise take a few more).
+template <int GS, int WAVES, int P, bool XLDS, int NBW, bool TABLE>
+__global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void streamk_kernel(
+    const StreamKArgs args) {
   constexpr int WPL = GS / 32;
+  // A planned call whose device plan is not the one the host launched from
+  // does nothing (every wave of the grid takes the same exit).
+  if constexpr (TABLE) {
+    if (load_const(args.plan_checksum) != args.checksum) return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
@@ -434,12 +444,38 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   const long long u0 = wg < NW ? wave_first_unit(wg, U, NW) : U;
   const long long u1 = wg < NW ? wave_first_unit(wg + 1, U, NW) : U;
 
-  // Problem of a global unit (wave-uniform search over at most kMaxProblems).
+  // Descriptor of problem p: in the kernel arguments, or in the device table
+  // of a planned call.
+  auto prob_at = [&](int p) -> StreamKProblem {
+    {
+      // field by field, as scalar loads from the table or the kernel
+      // arguments (both read-only here)
+      const StreamKProblem* e = (TABLE ? args.table : args.prob) + p;
+      StreamKProblem r;
+      r.x = load_const(&e->x);
+      r.qw = load_const(&e->qw);
+      r.sp = load_const(&e->sp);
+      r.y = load_const(&e->y);
+      r.N = load_const(&e->N);
+      r.K = load_const(&e->K);
+      r.G = load_const(&e->G);
+      r.NCB = load_const(&e->NCB);
+      r.NSB = load_const(&e->NSB);
+      r.u_begin = load_const(&e->u_begin);
+      r.sb_begin = load_const(&e->sb_begin);
+      return r;
+    }
+  };
+  // Problem of a global unit of this workgroup's range (wave-uniform): a
+  // forward scan over the problems' first units, from problem 0 or, in a
+  // table, from the problem holding the workgroup's first unit. The scan reads
+  // one field per step as a scalar load, so no descriptor stays live in
+  // registers (an unrolled compare over all eight made the compiler keep
+  // them in SGPRs and spill).
   auto problem_of = [&](long long u) {
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxProblems; ++i)
-      if (i < args.nprob && u >= args.prob[i].u_begin) p = i;
+    const auto* tab = TABLE ? args.table : args.prob;
+    int p = TABLE ? load_const(args.wgfirst + blockIdx.x) : 0;
+    while (p + 1 < args.nprob && load_const(&tab[p + 1].u_begin) <= u) ++p;
     return p;
   };
 
@@ -453,7 +489,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   auto make_run = [&](long long u) {
     Run r;
     r.p = problem_of(u);
-    const StreamKProblem& pr = args.prob[r.p];
+    const StreamKProblem& pr = prob_at(r.p);
     const long long pend = pr.u_begin + static_cast<long long>(pr.NSB) * pr.G;
     r.v0 = uniform(static_cast<int>(u - pr.u_begin));
     r.v1 = uniform(static_cast<int>((u1 < pend ? u1 : pend) - pr.u_begin));
@@ -509,6 +545,9 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     lds_base[i] = 0;
     lds_stride[i] = 0;
   }
+  // Per-problem LDS offsets are indexed by p - plo, plo the workgroup's first
+  // problem (at most kMaxProblems problems per workgroup, checked on the host).
+  int plo = 0;
   // With XLDS, LDS also holds per problem and group the bias term -136 *
   // (sum of the group's activations) of each row, as [G][16 rows] fp32 (rows
   // past Mr repeat row Mr - 1), after the activation rows: an MFMA chain
@@ -521,28 +560,30 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
     const long long wu0 = wave_first_unit(blockIdx.x * WAVES, U, NW);
     const long long wu1 = wave_first_unit(min((blockIdx.x + 1) * WAVES, NW), U, NW);
     if (wu1 > wu0) {
-      const int plo = problem_of(wu0), phi = problem_of(wu1 - 1);
+      plo = problem_of(wu0);
+      const int phi = problem_of(wu1 - 1);
       int off = 0;  // in bf16 elements
 #pragma unroll
-      for (int i = 0; i < kMaxProblems; ++i) {
-        if (i >= plo && i <= phi) {
-          lds_base[i] = off;
-          lds_stride[i] = args.prob[i].K + 8;  // 16 bytes of padding per row against bank conflicts
-          off += Mr * lds_stride[i];
+      for (int j = 0; j < kMaxProblems; ++j) {
+        if (plo + j <= phi) {
+          lds_base[j] = off;
+          lds_stride[j] = prob_at(plo + j).K + 8;  // 16 bytes of padding per row against bank conflicts
+          off += Mr * lds_stride[j];
         }
       }
       int xoff = off / 2;  // in 4-byte words; a multiple of 4
 #pragma unroll
-      for (int i = 0; i < kMaxProblems; ++i) {
-        if (i >= plo && i <= phi) {
-          xs_base[i] = xoff;
-          xoff += args.prob[i].G * 16;
+      for (int j = 0; j < kMaxProblems; ++j) {
+        if (plo + j <= phi) {
+          xs_base[j] = xoff;
+          xoff += prob_at(plo + j).G * 16;
         }
       }
 #pragma unroll
-      for (int i = 0; i < kMaxProblems; ++i) {
-        if (i >= plo && i <= phi) {
-          const StreamKProblem& pr = args.prob[i];
+      for (int j = 0; j < kMaxProblems; ++j) {
+        if (plo + j <= phi) {
+          const int i = j;  // slot of problem plo + j in the LDS offset arrays
+          const StreamKProblem& pr = prob_at(plo + j);
           constexpr int LPG = GS / 8;  // 16-byte pieces per group
           const int chunks = pr.K / 8;
           // Mr * chunks is a multiple of LPG and each pass starts at a
@@ -583,10 +624,11 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
 #pragma unroll
         for (int i = 0; i < P; ++i) load_unit(bufA[i], run, run.v0 + i);
       }
-      const StreamKProblem& pr = args.prob[run.p];
+      const StreamKProblem& pr = prob_at(run.p);
       const int G = run.G;
-      const int xbase = XLDS ? (lds_base[run.p] + min(c16, M - 1) * lds_stride[run.p] + lg * WPL * 8) / 2 : 0;
-      const float* const xs = xsum + xs_base[run.p] + 4 * lg;  // with XLDS: this lane's rows of group 0
+      const int rp = run.p - plo;  // slot of the problem in the LDS offset arrays (with XLDS)
+      const int xbase = XLDS ? (lds_base[rp] + min(c16, M - 1) * lds_stride[rp] + lg * WPL * 8) / 2 : 0;
+      const float* const xs = xsum + xs_base[rp] + 4 * lg;  // with XLDS: this lane's rows of group 0
       int sb = uniform(run.v0 / G);
       int g = uniform(run.v0 - sb * G);
       int seg_g0 = g;  // first group of the current super-block segment
@@ -691,7 +733,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
         compute_chunk(bufB, v + P);
       }
 
-      const long long next = args.prob[run.p].u_begin + run.v1;
+      const long long next = prob_at(run.p).u_begin + run.v1;
       if (next >= u1) break;
       run = make_run(next);
     }
@@ -709,7 +751,7 @@ __global__ __launch_bounds__(64 * WAVES) void streamk_kernel(const StreamKArgs a
   for (int k = 0; k < 2; ++k) {
     const long long u = k == 0 ? u0 : u1 - 1;
     const int p = problem_of(u);
-    const StreamKProblem& pr = args.prob[p];
+    const StreamKProblem& pr = prob_at(p);
     const int G = uniform(pr.G);
     const int sb = uniform(static_cast<int>((u - pr.u_begin) / G));
     const long long s0 = pr.u_begin + static_cast<long long>(sb) * G;
@@ -798,10 +840,10 @@ constexpr int streamk_prefetch() {
   return NBW == 1 ? W4A16_STREAMK_PREFETCH : W4A16_STREAMK_WIDE_PREFETCH;
 }
 
-template <int GS, bool XLDS, int NBW>
+template <int GS, bool XLDS, int NBW, bool TABLE>
 hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStream_t stream) {
   const void* fn = reinterpret_cast<const void*>(
-      &streamk_kernel<GS, kStreamKWaves, streamk_prefetch<NBW>(), XLDS, NBW>);
+      &streamk_kernel<GS, kStreamKWaves, streamk_prefetch<NBW>(), XLDS, NBW, TABLE>);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -814,13 +856,13 @@ hipError_t launch_streamk_t(const StreamKArgs& sk, int wgs, size_t lds, hipStrea
 
 // Activations staged in LDS: one column block per unit. Read by each wave:
 // streamk_wide_blocks(group) column blocks per unit.
-template <bool XLDS>
+template <bool XLDS, bool TABLE = false>
 hipError_t launch_streamk_x(const StreamKArgs& sk, int group, int wgs, size_t lds, hipStream_t s) {
   switch (group) {
-    case 32: return launch_streamk_t<32, XLDS, XLDS ? 1 : streamk_wide_blocks(32)>(sk, wgs, lds, s);
-    case 64: return launch_streamk_t<64, XLDS, XLDS ? 1 : streamk_wide_blocks(64)>(sk, wgs, lds, s);
-    case 128: return launch_streamk_t<128, XLDS, XLDS ? 1 : streamk_wide_blocks(128)>(sk, wgs, lds, s);
-    case 256: return launch_streamk_t<256, XLDS, XLDS ? 1 : streamk_wide_blocks(256)>(sk, wgs, lds, s);
+    case 32: return launch_streamk_t<32, XLDS, XLDS ? 1 : streamk_wide_blocks(32), TABLE>(sk, wgs, lds, s);
+    case 64: return launch_streamk_t<64, XLDS, XLDS ? 1 : streamk_wide_blocks(64), TABLE>(sk, wgs, lds, s);
+    case 128: return launch_streamk_t<128, XLDS, XLDS ? 1 : streamk_wide_blocks(128), TABLE>(sk, wgs, lds, s);
+    case 256: return launch_streamk_t<256, XLDS, XLDS ? 1 : streamk_wide_blocks(256), TABLE>(sk, wgs, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -831,19 +873,19 @@ size_t streamk_lds_part_bytes(int M, int nbw) {
 }
 
 // Units of the problems with NBW column blocks per super-block, and the grid:
-// fills sk (units, nwaves, problem offsets) and returns the workgroup count.
-int plan_streamk(StreamKArgs& sk, int nbw) {
-  long long units = 0;
-  int sbs = 0;
-  for (int i = 0; i < sk.nprob; ++i) {
-    StreamKProblem& p = sk.prob[i];
+// fills the problems' offsets, *units and *nwaves and returns the workgroup
+// count; *sbs is the total number of super-blocks.
+int plan_streamk_probs(StreamKProblem* probs, int count, int nbw, long long* units_out,
+                       int* nwaves_out, long long* sbs_out) {
+  long long units = 0, sbs = 0;
+  for (int i = 0; i < count; ++i) {
+    StreamKProblem& p = probs[i];
     p.NSB = (p.NCB + nbw - 1) / nbw;
     p.u_begin = units;
-    p.sb_begin = sbs;
+    p.sb_begin = static_cast<int>(sbs);
     units += static_cast<long long>(p.NSB) * p.G;
     sbs += p.NSB;
   }
-  sk.units = units;
   int wgs = device_cus() * (nbw == 1 ? W4A16_STREAMK_WG_PER_CU : W4A16_STREAMK_WIDE_WG_PER_CU);
   const int max_waves = nbw == 1 ? kStreamKMaxWaves : kStreamKWideMaxWaves;
   if (wgs * kStreamKWaves > max_waves) wgs = max_waves / kStreamKWaves;
@@ -851,8 +893,43 @@ int plan_streamk(StreamKArgs& sk, int nbw) {
   // a super-block are then produced by consecutive non-empty waves.
   long long nw = static_cast<long long>(wgs) * kStreamKWaves;
   if (nw > units) nw = units;
-  sk.nwaves = static_cast<int>(nw);
+  *units_out = units;
+  *nwaves_out = static_cast<int>(nw);
+  if (sbs_out) *sbs_out = sbs;
   return static_cast<int>((nw + kStreamKWaves - 1) / kStreamKWaves);
+}
+
+int plan_streamk(StreamKArgs& sk, int nbw) {
+  return plan_streamk_probs(sk.prob, sk.nprob, nbw, &sk.units, &sk.nwaves, nullptr);
+}
+
+// The most LDS any workgroup needs for staged activations (Mr rows of K + 8
+// bf16 and G x 16 fp32 group sums of every problem its units touch), and the
+// most problems one workgroup touches.
+void streamk_lds_need(const StreamKProblem* probs, int count, int M, long long units, long long nw,
+                      int wgs, long long* need_out, int* touch_out) {
+  const int Mr = M < 16 ? M : 16;
+  long long need = 0;
+  int touch = 0;
+  int p = 0;  // first problem overlapping the current workgroup (ranges increase with b)
+  for (int b = 0; b < wgs; ++b) {
+    const long long wb0 = static_cast<long long>(b) * kStreamKWaves;
+    const long long wb1 = wb0 + kStreamKWaves < nw ? wb0 + kStreamKWaves : nw;
+    const long long wu0 = units * wb0 / nw;
+    const long long wu1 = units * wb1 / nw;
+    if (wu1 <= wu0) continue;
+    while (p + 1 < count && probs[p + 1].u_begin <= wu0) ++p;
+    long long bytes = 0;
+    int n = 0;
+    for (int i = p; i < count && probs[i].u_begin < wu1; ++i) {
+      bytes += static_cast<long long>(Mr) * (probs[i].K + 8) * 2 + static_cast<long long>(probs[i].G) * 16 * 4;
+      ++n;
+    }
+    if (bytes > need) need = bytes;
+    if (n > touch) touch = n;
+  }
+  *need_out = need;
+  *touch_out = touch;
 }
 
 }  // namespace
@@ -902,25 +979,9 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
   // its units touch). Beyond the budget, each wave reads activations itself
   // and takes streamk_wide_blocks(group) column blocks per unit instead.
   int wgs = plan_streamk(sk, 1);
-  const long long units = sk.units;
-  const long long nw = sk.nwaves;
-  const int Mr = M < 16 ? M : 16;
   long long need = 0;
-  for (int b = 0; b < wgs; ++b) {
-    const long long wb0 = static_cast<long long>(b) * kStreamKWaves;
-    const long long wb1 = wb0 + kStreamKWaves < nw ? wb0 + kStreamKWaves : nw;
-    const long long wu0 = units * wb0 / nw;
-    const long long wu1 = units * wb1 / nw;
-    if (wu1 <= wu0) continue;
-    long long bytes = 0;  // activation rows and their group sums
-    for (int i = 0; i < count; ++i) {
-      const long long pb = sk.prob[i].u_begin;
-      const long long pe = pb + static_cast<long long>(sk.prob[i].NSB) * sk.prob[i].G;
-      if (pe > wu0 && pb < wu1)
-        bytes += static_cast<long long>(Mr) * (sk.prob[i].K + 8) * 2 + static_cast<long long>(sk.prob[i].G) * 16 * 4;
-    }
-    if (bytes > need) need = bytes;
-  }
+  int touch = 0;
+  streamk_lds_need(sk.prob, count, M, sk.units, sk.nwaves, wgs, &need, &touch);
   // The waves' parts (level 1 of the hand-off) follow the staged activations.
   const size_t x_bytes = (static_cast<size_t>(need) + 15) / 16 * 16;
   const size_t lds = x_bytes + streamk_lds_part_bytes(M, 1);
@@ -932,6 +993,78 @@ hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int gro
   wgs = plan_streamk(sk, nbw);
   sk.lds_part_off = 0;
   return launch_streamk_x<false>(sk, group, wgs, streamk_lds_part_bytes(M, nbw), stream);
+}
+
+// Stream-K plan of validated problems (N, K, pointers set): fills the
+// problems' offsets, the header's launch and workspace fields and the first
+// problem of every workgroup.
+int build_streamk_plan(StreamKProblem* probs, int count, int M, int group, PlanHeader& h,
+                       int* wgfirst) {
+  for (int i = 0; i < count; ++i) {
+    probs[i].G = probs[i].K / group;
+    probs[i].NCB = (probs[i].N + 15) / 16;
+  }
+  long long units = 0, sbs = 0;
+  int nw = 0;
+  int wgs = plan_streamk_probs(probs, count, 1, &units, &nw, &sbs);
+  long long need = 0;
+  int touch = 0;
+  streamk_lds_need(probs, count, M, units, nw, wgs, &need, &touch);
+  const size_t x_bytes = (static_cast<size_t>(need) + 15) / 16 * 16;
+  const size_t lds = x_bytes + streamk_lds_part_bytes(M, 1);
+  int nbw = 1;
+  if (lds <= kStreamKLdsBudget && touch <= kMaxProblems) {
+    h.xlds = 1;
+    h.lds_part_off = static_cast<int>(x_bytes / 4);
+    h.lds_bytes = static_cast<int>(lds);
+  } else {
+    nbw = streamk_wide_blocks(group);
+    wgs = plan_streamk_probs(probs, count, nbw, &units, &nw, &sbs);
+    h.xlds = 0;
+    h.lds_part_off = 0;
+    h.lds_bytes = static_cast<int>(streamk_lds_part_bytes(M, nbw));
+  }
+  if (wgs < 1 || wgs > kPlanMaxWorkgroups) return -1;
+  h.kind = kPlanKindStreamK;
+  h.nbw = nbw;
+  h.grid = wgs;
+  h.nwaves = nw;
+  h.units = units;
+  // workgroup b's first unit is that of its first wave, units * 8b / nw
+  int p = 0;
+  for (int b = 0; b < wgs; ++b) {
+    const long long u = units * (static_cast<long long>(b) * kStreamKWaves) / nw;
+    while (p + 1 < count && probs[p + 1].u_begin <= u) ++p;
+    wgfirst[b] = p;
+  }
+  const int Mr = M < 16 ? M : 16;
+  const long long counter_bytes = (sbs * 4 + 255) / 256 * 256;
+  const long long slot_bytes = (sbs * nbw * Mr * 16 * 4 + 255) / 256 * 256;
+  h.counters_off = 0;
+  h.slots_off = counter_bytes;
+  h.part_off = counter_bytes + slot_bytes;
+  h.workspace_bytes = h.part_off + static_cast<long long>(streamk_part_bytes(M));
+  return 0;
+}
+
+hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan_dev, char* ws,
+                                  hipStream_t stream) {
+  StreamKArgs sk = {};
+  sk.table = reinterpret_cast<const StreamKProblem*>(plan_dev + h.table_off);
+  sk.wgfirst = reinterpret_cast<const int*>(plan_dev + h.wgfirst_off);
+  sk.plan_checksum =
+      reinterpret_cast<const unsigned long long*>(plan_dev + offsetof(PlanHeader, checksum));
+  sk.checksum = h.checksum;
+  sk.nprob = h.count;
+  sk.M = h.M;
+  sk.units = h.units;
+  sk.nwaves = h.nwaves;
+  sk.part = reinterpret_cast<float*>(ws + h.part_off);
+  sk.slots = reinterpret_cast<uint32_t*>(ws + h.slots_off);
+  sk.counters = reinterpret_cast<int*>(ws + h.counters_off);
+  sk.lds_part_off = h.lds_part_off;
+  return h.xlds ? launch_streamk_x<true, true>(sk, h.group, h.grid, h.lds_bytes, stream)
+                : launch_streamk_x<false, true>(sk, h.group, h.grid, h.lds_bytes, stream);
 }
 
 int choose_path(int M, int N, int K, int group) {
