@@ -133,7 +133,9 @@ int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* 
  * For 52,224 columns (one layer's four projections): 0.6 MB at M = 1, 10 MB
  * at M = 16, 21 to 84 MB for M > 16. Device memory owned by the caller,
  * 256-byte aligned, zero-filled once before its first use; every call leaves
- * the counters and slots at zero again, so it is reused without clearing.
+ * every byte of it at zero again (counters, slots and partial sums), so one
+ * workspace serves any sequence of calls of any kind (any M, any problems,
+ * planned or not) without clearing, as long as it is large enough for each.
  * One workspace must not serve two calls that can run at the same time.
  * Returns 0 for M < 0 or total_columns < 0.
  */

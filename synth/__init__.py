@@ -61,6 +61,9 @@ def _load():
             fn = getattr(lib, name)
             fn.restype = c_int
             fn.argtypes = [u64, u64, ctypes.c_void_p, i64, i64, i64, c_int]
+        lib.synth_x_sigma.restype = c_int
+        lib.synth_x_sigma.argtypes = [u64, u64, ctypes.c_void_p, i64, i64, i64, ctypes.c_double,
+                                      c_int]
         _lib = lib
     return _lib
 
@@ -113,11 +116,17 @@ def gen_scales(tid: int, N: int, G: int, rows=None, seed: int = SEED, threads: i
     return out
 
 
-def gen_x(tid: int, M: int, K: int, rows=None, seed: int = SEED, threads: int | None = None):
-    """uint16 bf16 bit patterns [m1-m0, K] for rows [m0, m1) of x[M][K]."""
+def gen_x(tid: int, M: int, K: int, rows=None, seed: int = SEED, threads: int | None = None,
+          sigma: float = 1.0):
+    """uint16 bf16 bit patterns [m1-m0, K] for rows [m0, m1) of x[M][K]: the
+    standard normal times sigma, rounded to bf16 (sigma = 1: the workloads)."""
     m0, m1 = (0, M) if rows is None else rows
     out = np.empty((m1 - m0, K), dtype=np.uint16)
-    rc = _load().synth_x(seed, tid, out.ctypes.data, K, m0, m1, threads or default_threads())
+    if sigma == 1.0:
+        rc = _load().synth_x(seed, tid, out.ctypes.data, K, m0, m1, threads or default_threads())
+    else:
+        rc = _load().synth_x_sigma(seed, tid, out.ctypes.data, K, m0, m1, float(sigma),
+                                   threads or default_threads())
     assert rc == 0
     return out
 

@@ -83,6 +83,7 @@ uint16_t synth_f64_to_bf16_rne(double v) {
 
 typedef struct {
   int kind;          /* 0 = q, 1 = scales, 2 = x */
+  double sigma;      /* x only: standard deviation (1 for the workloads) */
   uint64_t key;
   void* out;
   int64_t cols;      /* elements per row */
@@ -108,7 +109,7 @@ static void synth_rows(const synth_job* j) {
         double u1 = (double)((z1 >> 11) + 1) * 0x1.0p-53;
         double u2 = (double)(z2 >> 11) * 0x1.0p-53;
         double g = sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925 * u2);
-        ((uint16_t*)j->out)[base + c] = synth_f64_to_bf16_rne(g);
+        ((uint16_t*)j->out)[base + c] = synth_f64_to_bf16_rne(j->sigma * g);
       }
     }
   }
@@ -119,8 +120,8 @@ static void* synth_thread(void* p) {
   return NULL;
 }
 
-static int synth_run(int kind, uint64_t seed, uint64_t tensor_id, void* out, int64_t cols,
-                     int64_t r0, int64_t r1, int nthreads) {
+static int synth_run(int kind, double sigma, uint64_t seed, uint64_t tensor_id, void* out,
+                     int64_t cols, int64_t r0, int64_t r1, int nthreads) {
   if (!out || cols < 0 || r0 < 0 || r1 < r0) return 1;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 64) nthreads = 64;
@@ -131,6 +132,7 @@ static int synth_run(int kind, uint64_t seed, uint64_t tensor_id, void* out, int
   uint64_t key = synth_stream_key(seed, tensor_id);
   for (int t = 0; t < nthreads; ++t) {
     jobs[t].kind = kind;
+    jobs[t].sigma = sigma;
     jobs[t].key = key;
     jobs[t].out = out;
     jobs[t].cols = cols;
@@ -153,17 +155,24 @@ static int synth_run(int kind, uint64_t seed, uint64_t tensor_id, void* out, int
 /* Rows [n0, n1) of the int4 codes q[N][K] (one int8 per weight, values -8..7). */
 int synth_q(uint64_t seed, uint64_t tensor_id, int8_t* out, int64_t K, int64_t n0, int64_t n1,
             int nthreads) {
-  return synth_run(0, seed, tensor_id, out, K, n0, n1, nthreads);
+  return synth_run(0, 1.0, seed, tensor_id, out, K, n0, n1, nthreads);
 }
 
 /* Rows [n0, n1) of the fp16 group scales s[N][G] (bit patterns). */
 int synth_scales(uint64_t seed, uint64_t tensor_id, uint16_t* out, int64_t G, int64_t n0,
                  int64_t n1, int nthreads) {
-  return synth_run(1, seed, tensor_id, out, G, n0, n1, nthreads);
+  return synth_run(1, 1.0, seed, tensor_id, out, G, n0, n1, nthreads);
 }
 
 /* Rows [m0, m1) of the bf16 activations x[M][K] (bit patterns). */
 int synth_x(uint64_t seed, uint64_t tensor_id, uint16_t* out, int64_t K, int64_t m0, int64_t m1,
             int nthreads) {
-  return synth_run(2, seed, tensor_id, out, K, m0, m1, nthreads);
+  return synth_run(2, 1.0, seed, tensor_id, out, K, m0, m1, nthreads);
+}
+
+/* As synth_x, with standard deviation sigma: x[m][k] = RNE_bf16(sigma * g), g the
+ * same Box-Muller normal (sigma = 1 gives synth_x's values). */
+int synth_x_sigma(uint64_t seed, uint64_t tensor_id, uint16_t* out, int64_t K, int64_t m0,
+                  int64_t m1, double sigma, int nthreads) {
+  return synth_run(2, sigma, seed, tensor_id, out, K, m0, m1, nthreads);
 }

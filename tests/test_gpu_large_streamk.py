@@ -157,3 +157,26 @@ def test_output_head_sampled(M):
     r = tolerance_ratio(y[:, cols], oracle.gemm(x, q[cols], s[cols], g, threads=synth.default_threads()))
     log(f"head M={M}: ratio {r:.4f}")
     assert r <= 1.0
+
+
+def test_workspace_shared_by_every_kind_of_call():
+    """One workspace, zero-filled once, serves a sequence of calls that use it
+    in different layouts (MFMA stream-K at 64 and 1024 rows, the streaming
+    kernel at 1 and 16 rows): each call leaves every byte at zero, so each
+    result equals that of a call on a fresh workspace, bit for bit."""
+    import torch
+
+    import w4a16_weight_only_gemm_amd as w4
+    from gpu_util import Problem, run_ws
+    N, K, g = 5120, 2048, 128
+    need = max(w4.w4a16_workspace_bytes(M, N) for M in (1, 16, 64, 1024))
+    ws = torch.zeros((need + 3) // 4, dtype=torch.int32, device="cuda")
+    for i, M in enumerate((64, 1, 1024, 16, 1, 64)):
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 990, i), N, K)
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 990, i), N, K // g)
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 990, i, M), M, K)
+        prob = Problem(x, q, s, g)
+        y = run_ws(prob, ws=ws)
+        assert np.array_equal(y, run_ws(prob)), f"call {i} (M={M}) differs on the shared workspace"
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0, f"call {i} (M={M}) left workspace bytes set"

@@ -217,3 +217,51 @@ def test_instantiation_matrix(path, case):
     x, q, s = _random_inputs(100 + cid, M, N, K, g)
     y = Problem(x, q, s, g).run(path)
     assert tolerance_ratio(y, oracle.gemm(x, q, s, g)) <= 1.0
+
+
+# Activations of standard deviation 1000 against codes that are zero over whole
+# groups: the exact sums of those groups are 0, while the kernels' biased
+# dequantization adds and removes 24 * (row sum) in fp32 around them, an error
+# that grows with |x|, not |y|. Columns 0..15 are zero over all of K (y = 0
+# exactly, where the bound is tightest), columns 16..31 zero in every other
+# group, the rest random.
+WIDE = [(1, 64, 17408, 128), (3, 48, 5120, 128), (16, 64, 6144, 64), (20, 48, 2048, 32),
+        (70, 80, 17408, 128), (200, 64, 4096, 128)]
+
+
+def _wide_inputs(case, M, N, K, g):
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 900 + case, 0), N, K)
+    q[:16] = 0
+    for t in range(0, K // g, 2):
+        q[16:32, t * g:(t + 1) * g] = 0
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 900 + case, 0), N, K // g)
+    x = synth.gen_x(synth.tensor_id(synth.KIND_X, 900 + case, 0, M), M, K, sigma=1000.0)
+    return x, q, s
+
+
+@pytest.mark.parametrize("path", PATHS + ["ws", "noalloc"], ids=PATH_IDS + ["ws", "noalloc"])
+@pytest.mark.parametrize("case", list(enumerate(WIDE)), ids=lambda c: "x".join(map(str, c[1])))
+def test_wide_range_activations(path, case):
+    from gpu_util import run_ws
+    cid, (M, N, K, g) = case
+    log(f"wide-range x (sigma 1000) {(M, N, K, g)} path={path}")
+    x, q, s = _wide_inputs(cid, M, N, K, g)
+    prob = Problem(x, q, s, g)
+    if path == "ws":
+        y = run_ws(prob)
+    elif path == "noalloc":
+        import torch
+
+        import w4a16_weight_only_gemm_amd as w4
+        yt = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        w4.w4a16_gemm_noalloc(prob.x, prob.qw, prob.sp, yt, M, N, K, g)
+        torch.cuda.synchronize()
+        y = yt.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        y = prob.run(path)
+    ref = oracle.gemm(x, q, s, g, threads=synth.default_threads())
+    assert np.all(ref[:, :16] == 0.0)
+    r_zero = tolerance_ratio(y[:, :16], ref[:, :16])
+    r = tolerance_ratio(y, ref)
+    log(f"  ratio {r:.3f} (all-zero columns {r_zero:.3f})")
+    assert r <= 1.0

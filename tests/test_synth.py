@@ -118,3 +118,17 @@ def test_tensors_are_distinct():
     b = synth.gen_q(synth.tensor_id(synth.KIND_Q, 1, 0), 4, 64)
     c = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, 1), 4, 64)
     assert (a != b).any() and (a != c).any()
+
+
+def test_scaled_activations():
+    """sigma = 1 is gen_x bit for bit; sigma = 1000 is 1000 times the same normal,
+    each side rounded to bf16 once (relative difference at most 2 * 2^-8)."""
+    tid = synth.tensor_id(synth.KIND_X, 3, 1, 4)
+    a = synth.gen_x(tid, 4, 512)
+    assert np.array_equal(a, synth.gen_x(tid, 4, 512, sigma=1.0))
+    b = synth.gen_x(tid, 4, 512, sigma=1000.0)
+    fa = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    fb = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nz = fa != 0
+    assert np.all(np.abs(fb[nz] / (1000.0 * fa[nz]) - 1.0) <= 2.0 ** -7)
+    assert 900.0 < np.std(fb) < 1100.0

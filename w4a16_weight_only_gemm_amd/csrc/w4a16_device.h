@@ -52,26 +52,34 @@ __device__ __forceinline__ void lds_barrier() {
 // A wave-uniform value moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// bf16 bit pattern of -136.0: sign 1, exponent 134 (2^7), fraction 8/128.
-constexpr uint32_t kBiasPair = 0xC308C308u;
+// bf16 bit pattern of -24.0 (sign 1, exponent 131 = 2^4, fraction 64/128), twice.
+constexpr uint32_t kBiasPair = 0xC1C0C1C0u;
 
 // Biased dequantization of one packed word: eight 4-bit two's-complement
 // codes of k = 8j..8j+7, interleaved so that nibble v holds the code of
 // k = 8j+2v and nibble v+4 that of k = 8j+2v+1. Output register v holds, as a
 // bf16 pair, codes 2v (low half) and 2v+1 (high half), each as the exact
-// value 136 + q: (c & 0xF) ^ 8 is the offset code q + 8 in 0..15, and OR-ing
-// it into the fraction of 0x4300 (128.0, whose unit in the last place is 1)
-// gives 128 + q + 8. One shift and one and-xor per register.
+// value 24 + q: (c ^ 8) is the offset code q + 8 in 0..15, and placed in
+// fraction bits 3..6 of 16.0 (0x4180, whose fraction step there is 1) it gives
+// 16 + q + 8. The nibbles are moved to bits 3..6 and 19..22 of the register
+// (one shift), then masked and xor-ed with 0x41C0 = 0x4180 ^ (8 << 3) (one
+// and-xor): 0x41C0 ^ (c << 3) = 0x4180 | ((c ^ 8) << 3).
+//
+// Why 24 and not a larger base such as 128 + 8: the kernels remove the bias
+// through fp32 sums of base * x, which round at the magnitude of base * sum|x|;
+// 24 is the smallest base for which one or-into-the-fraction yields all sixteen
+// codes as exact integers, so the rounding that large activations leave on a
+// result near zero is 5.7 times smaller than with 136.
 //
 // MFMA consumes the eight bf16 of a register quad as k-slots 0..7, so the
 // operand is in natural k order and pairs with eight consecutive bf16
 // activations loaded as they are stored.
 __device__ __forceinline__ bf16x8 dequant_biased(uint32_t w) {
   u32x4 r;
-  r[0] = (w & 0x000F000Fu) ^ 0x43084308u;
-  r[1] = ((w >> 4) & 0x000F000Fu) ^ 0x43084308u;
-  r[2] = ((w >> 8) & 0x000F000Fu) ^ 0x43084308u;
-  r[3] = ((w >> 12) & 0x000F000Fu) ^ 0x43084308u;
+  r[0] = ((w << 3) & 0x00780078u) ^ 0x41C041C0u;
+  r[1] = ((w >> 1) & 0x00780078u) ^ 0x41C041C0u;
+  r[2] = ((w >> 5) & 0x00780078u) ^ 0x41C041C0u;
+  r[3] = ((w >> 9) & 0x00780078u) ^ 0x41C041C0u;
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -104,10 +112,10 @@ __device__ __forceinline__ float dpp_f32(float v) {
                                                      true));
 }
 
-// -136 times the sum of the 8 bf16 values of a 16-byte piece, in fp32: four
-// bf16 dot products against the pair (-136, -136). Each product is exact in
-// fp32 (8-bit by 8-bit significands); only the additions round.
-__device__ __forceinline__ float neg136_sum8(u32x4 d) {
+// -24 times the sum of the 8 bf16 values of a 16-byte piece, in fp32: four
+// bf16 dot products against the pair (-24, -24). Each product is exact in
+// fp32 (8-bit by 2-bit significands); only the additions round.
+__device__ __forceinline__ float neg_bias_sum8(u32x4 d) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 k = __builtin_bit_cast(bf16x2, kBiasPair);
   // Elements are copied to scalars first: this compiler's __builtin_bit_cast

@@ -18,9 +18,9 @@
 //  * Packed weights go straight from the tiled format into registers: a
 //    lane's words of one (16-column block, group) tile are its B operands
 //    for that group's MFMA steps.
-//  * Dequantization yields the exact biased value 136 + q (as in the small-M
-//    kernels). Instead of a second MFMA against a -136 operand, the bias is
-//    removed by starting each group's accumulation from -136 * sum_k x[m][k]
+//  * Dequantization yields the exact biased value 24 + q (as in the small-M
+//    kernels). Instead of a second MFMA against a -24 operand, the bias is
+//    removed by starting each group's accumulation from -24 * sum_k x[m][k]
 //    over the group: those row sums are formed once per workgroup while the
 //    activation tile is staged (bf16 dot products, then a DPP reduction) and
 //    kept in LDS next to the tile. Every MFMA then does useful work.
@@ -183,7 +183,7 @@ struct TileEngine {
 #pragma unroll
     for (int i = 0; i < C::Loads; ++i) {
       const int row = srow0 + i * kLgRowStep;
-      const float s = group_lane_sum<C::LPG>(neg136_sum8(r.d[i]));
+      const float s = group_lane_sum<C::LPG>(neg_bias_sum8(r.d[i]));
       sums[(spiece / C::LPG) * C::Rows + row] = s;  // every lane of the group: same value
       const int sl = lg_slot(spiece, row);
       *reinterpret_cast<u32x4*>(base + row * kLgRowBytes + sl * 16) = r.d[i];
@@ -220,7 +220,7 @@ struct TileEngine {
   }
 
   // One k-tile: 4 MFMA steps of 32 k. Step st belongs to group st / WPL of the
-  // k-tile; a group's accumulation starts from its -136 * row-sum tile and
+  // k-tile; a group's accumulation starts from its -24 * row-sum tile and
   // ends with the scaled add into acc_out.
   __device__ __forceinline__ void compute(Acc<MB>& acc_out, const BRegs<GS>& b, int t,
                                           int buf) const {
@@ -498,13 +498,18 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
     zero(acc);
     float* sum = reinterpret_cast<float*>(&acc);
     for (int w = wfirst; w <= wlast; ++w) {
-      const float* part = part_of(w, lg_first_unit(w, U, NW) >= tile_u0 ? 0 : 1);
+      float* part = part_of(w, lg_first_unit(w, U, NW) >= tile_u0 ? 0 : 1);
       float v[C::Regs];
 #pragma unroll
       for (int r = 0; r < C::Regs; ++r)
         v[r] = __hip_atomic_load(part + r * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int r = 0; r < C::Regs; ++r) sum[r] += v[r];
+      // cleared once read (the sum above used every loaded value), so the call
+      // leaves the whole workspace at zero and calls of every kind can share it
+#pragma unroll
+      for (int r = 0; r < C::Regs; ++r)
+        __hip_atomic_store(part + r * 64 + lane, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     e.setup(lg_lds, pr.x, pr.qw, pr.sp, args.M, pr.N, pr.K, (tile % pr.MT) * C::Rows,
             tile / pr.MT);

@@ -11,8 +11,8 @@
 //    the group's MFMA steps (lane l serves column l % 16 and k-slice l / 16 of
 //    every step). A wave therefore loads a unit with one contiguous vector load
 //    and feeds it HBM -> VGPR -> dequant -> MFMA without LDS.
-//  * Dequantization is to the exact biased value 136 + q in bf16 (two VALU
-//    ops per bf16 pair); a second MFMA against a constant -136 operand removes
+//  * Dequantization is to the exact biased value 24 + q in bf16 (two VALU
+//    ops per bf16 pair); a second MFMA against a constant -24 operand removes
 //    the bias, so the MFMA sees exact codes, products are exact and the fp32
 //    accumulator holds sum(x * q) over the group. The group's partial is then
 //    scaled by its fp16 scale and added to the running fp32 result.
@@ -359,7 +359,8 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[j][r] = 0.f;
   // Two parts at a time, so their loads are all in flight together; the sum
-  // runs in workgroup order.
+  // runs in workgroup order. Each part is cleared once read, so that the call
+  // leaves the whole workspace at zero (calls of every kind can then share it).
   auto load_part = [&](float (&v)[NBW][4], int c) {
     float* part = args.part + (static_cast<size_t>(c) * 2 + slot_of(c)) * NBW * Mr * 16;
 #pragma unroll
@@ -368,6 +369,16 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
       for (int r = 0; r < 4; ++r)
         v[j][r] = __hip_atomic_load(part + part_index<NBW>(j, 4 * lg + r, c16, Mr), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto clear_part = [&](int c) {
+    float* part = args.part + (static_cast<size_t>(c) * 2 + slot_of(c)) * NBW * Mr * 16;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __hip_atomic_store(part + part_index<NBW>(j, 4 * lg + r, c16, Mr), 0.f, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   int c = bfirst;
@@ -389,6 +400,9 @@ __device__ __forceinline__ void finalize_block(const StreamKArgs& args, const St
       for (int r = 0; r < 4; ++r) sum[j][r] += v0[j][r];
   }
   store_block<NBW>(pr, sb, sum, lg, c16, M);
+  // the loads above have returned (their values were summed), so the parts
+  // can be overwritten now
+  for (c = bfirst; c <= blast; ++c) clear_part(c);
   if (lane == 0)
     __hip_atomic_store(args.counters + pr.sb_begin + sb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
   // Per-problem LDS offsets are indexed by p - plo, plo the workgroup's first
   // problem (at most kMaxProblems problems per workgroup, checked on the host).
   int plo = 0;
-  // With XLDS, LDS also holds per problem and group the bias term -136 *
+  // With XLDS, LDS also holds per problem and group the bias term -24 *
   // (sum of the group's activations) of each row, as [G][16 rows] fp32 (rows
   // past Mr repeat row Mr - 1), after the activation rows: an MFMA chain
   // started from it sums a * q with the codes' bias already removed.
@@ -594,7 +608,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
             const u32x4 d =
                 *reinterpret_cast<gptr<const u32x4>>(to_global(pr.x) + static_cast<size_t>(row) * pr.K + 8 * c8);
             *reinterpret_cast<u32x4*>(xlds + (lds_base[i] + row * lds_stride[i] + 8 * c8) / 2) = d;
-            const float bsum = group_lane_sum<LPG>(neg136_sum8(d));  // the group's first lane stores
+            const float bsum = group_lane_sum<LPG>(neg_bias_sum8(d));  // the group's first lane stores
             if ((c8 % LPG) == 0) {
               float* dst = xsum + xs_base[i] + (c8 / LPG) * 16;
               dst[row] = bsum;
@@ -656,7 +670,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
               for (int t = 0; t < WPL; ++t) a[t] = act_frag(buf[i].x[t]);
             }
             if constexpr (NBW == 1) {
-              // from -136 * (row sums): sum of a * q (exact products)
+              // from -24 * (row sums): sum of a * q (exact products)
               f32x4 acc = *reinterpret_cast<const f32x4*>(xs + g * 16);
 #pragma unroll
               for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[0].w[t]), acc);
@@ -665,7 +679,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
 #pragma unroll
               for (int r = 0; r < 4; ++r) yacc[0][r] = __builtin_fmaf(sc, acc[r], yacc[0][r]);
             } else {
-              // -136 * (row sums of the group) once, as the start of every block's sum
+              // -24 * (row sums of the group) once, as the start of every block's sum
               f32x4 accb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
