@@ -67,7 +67,7 @@ typedef enum {
 /* Kernel paths; W4A16_PATH_AUTO lets the M-dispatch heuristic choose. */
 typedef enum {
   W4A16_PATH_AUTO = 0,
-  W4A16_PATH_SKINNY = 1, /* small M: per-wave weight streaming, 16-row MFMA tiles, split-K */
+  W4A16_PATH_SKINNY = 1, /* small M: workgroups of 16-64 rows x 32-64 columns over all of K, waves split K */
   W4A16_PATH_LARGE = 2   /* large M: LDS-staged activation tiles, bf16 MFMA, per-group fp32 scaling */
 } w4a16_path;
 

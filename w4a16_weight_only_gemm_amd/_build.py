@@ -8,8 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["w4a16_host.cpp", "w4a16_skinny.hip", "w4a16_large.hip", "w4a8.hip", "w4a16_probe.hip",
-           "w4a16_noalloc.hip"]
+SOURCES = ["w4a16_host.cpp", "w4a16_plain.hip", "w4a16_skinny.hip", "w4a16_large.hip", "w4a8.hip",
+           "w4a16_probe.hip", "w4a16_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -1,0 +1,331 @@
+// w4a16_plain.hip -- the kernel behind w4a16_gemm for small M (no workspace).
+//
+// Without a workspace no output can be summed across workgroups, so a
+// workgroup owns whole output tiles: NB consecutive 16-column blocks (16 NB
+// columns) and MB 16-row blocks, over the whole of K. Its waves split K into
+// equal contiguous ranges of groups and are summed through LDS at the end.
+//
+//  * Weights: per group a wave loads one tile of the packed format for each
+//    of its NB column blocks (the lane's words are its MFMA B operands), P
+//    groups ahead, non-temporal: every weight byte is read from HBM once.
+//  * Activations: one fragment per row block and MFMA step feeds NB column
+//    blocks, so the activation bytes a workgroup reads per weight byte fall as
+//    1/NB (each activation element is read once per workgroup: the waves
+//    cover disjoint K ranges). With XLDS (M <= 16 rows whose whole K fits),
+//    the workgroup stages its rows in LDS once, with each group's -24 * row
+//    sums, and the waves read fragments from there.
+//  * Dequantization to the exact biased codes 24 + q, MFMA 16x16x32 bf16; the
+//    bias leaves through the accumulator start: -24 * (row sums), from LDS
+//    with XLDS, else one MFMA chain against a -24 operand per row block,
+//    shared by the NB column blocks. Then one fp32 FMA per output and group
+//    applies the group's scale.
+//
+// The host picks (MB, NB, waves, groups in flight, staging) from M, N and K
+// (launch_plain_g) so that the grid has enough workgroups for the compute
+// units and each wave keeps enough bytes in flight.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/w4a16.h"
+#include "w4a16_device.h"
+#include "w4a16_launch.h"
+
+namespace w4a16_internal {
+namespace {
+
+constexpr size_t kPlainLdsLimit = 160 * 1024;  // LDS of one compute unit
+
+template <int WPL>
+struct PWords {
+  uint32_t w[WPL];
+};
+
+template <int WPL>
+__device__ __forceinline__ void load_tile_words(PWords<WPL>& out, gptr<const uint32_t> p) {
+  if constexpr (WPL == 1) {
+    out.w[0] = __builtin_nontemporal_load(p);
+  } else if constexpr (WPL == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<gptr<const u32x2>>(p));
+    out.w[0] = v[0];
+    out.w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < WPL / 4; ++h) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<gptr<const u32x4>>(p) + h);
+      out.w[4 * h + 0] = v[0];
+      out.w[4 * h + 1] = v[1];
+      out.w[4 * h + 2] = v[2];
+      out.w[4 * h + 3] = v[3];
+    }
+  }
+}
+
+// One group's loads for this lane: NB weight tiles, NB scale pairs and (without
+// XLDS) the MB x WPL activation fragments.
+template <int WPL, int MB, int NB, bool XLDS>
+struct PStage {
+  PWords<WPL> w[NB];
+  uint32_t s2[NB];
+  u32x4 x[XLDS ? 1 : MB][WPL];
+};
+
+// WM: waves along the rows. The workgroup's WAVES waves form WM x (WAVES / WM):
+// wave w takes row blocks [(w % WM) MB / WM, ...) and the (w / WM)-th of the
+// WAVES / WM ranges of K. With WM > 1 the waves of one K range share each
+// weight tile (one is read from HBM, the others hit the caches: the loads are
+// then ordinary, not non-temporal) and each holds the activations of fewer
+// rows, which leaves registers for more groups in flight.
+template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1>
+__global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __restrict__ x,
+                                                          const uint32_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ sp,
+                                                          uint16_t* __restrict__ y, int M, int N,
+                                                          int K) {
+  constexpr int WPL = GS / 32;  // MFMA steps per group = packed words per lane per tile
+  constexpr int LPG = GS / 8;   // 16-byte pieces of a row per group
+  constexpr int WK = WAVES / WM;  // waves along K
+  constexpr int MBW = MB / WM;    // row blocks per wave
+  static_assert(!XLDS || MB == 1, "staged activations: one row block");
+  static_assert(WK * WM == WAVES && MBW * WM == MB, "waves and row blocks divide evenly");
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int c16 = lane & 15, lg = lane >> 4;
+  const int G = K / GS;
+  const int NCB = (N + 15) / 16;
+  const int b0 = blockIdx.x * NB;
+  const int m0 = blockIdx.y * 16 * MB;
+  const int Mr = min(M - m0, 16 * MB);  // rows of this row tile
+  const int wm = wave % WM, wk = wave / WM;
+  const int mbw0 = wm * MBW;             // this wave's first row block
+  // this wave's groups [g0, g1) (wave-uniform)
+  const int g0 = static_cast<int>(static_cast<long long>(G) * wk / WK);
+  const int g1 = static_cast<int>(static_cast<long long>(G) * (wk + 1) / WK);
+
+  extern __shared__ __attribute__((aligned(16))) uint32_t plds[];
+  // XLDS layout: rows [Mr][K + 8] bf16 (16 bytes of padding per row against
+  // bank conflicts), then [G][16] fp32 -24 * row sums (rows past Mr repeat
+  // row Mr - 1), then the reduction area.
+  const int xstride = K + 8;                        // bf16 elements
+  const int sum_off = XLDS ? (Mr * xstride) / 2 : 0;  // 4-byte words; Mr * xstride is even
+  float* const xsum = reinterpret_cast<float*>(plds + sum_off);
+  float* const red = reinterpret_cast<float*>(plds + (XLDS ? sum_off + G * 16 : 0));
+
+  // Column blocks past the last are clamped on load (their results are not stored).
+  gptr<const uint32_t> wbase[NB];
+  gptr<const uint32_t> sbase[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int b = min(b0 + nb, NCB - 1);
+    wbase[nb] = to_global(qw) + static_cast<size_t>(b) * G * 64 * WPL + lane * WPL;
+    sbase[nb] = reinterpret_cast<gptr<const uint32_t>>(to_global(sp) + static_cast<size_t>(b) * G * 16 +
+                                                       (c16 & ~1));
+  }
+  // activation rows of this lane's A operand, one per row block (rows past M
+  // repeat the last row; their MFMA output rows are never stored)
+  gptr<const uint16_t> xrow[MBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    const int m = min(m0 + 16 * (mbw0 + mb) + c16, M - 1);
+    xrow[mb] = to_global(x) + static_cast<size_t>(m) * K + lg * WPL * 8;
+  }
+
+  const int glast = g1 - 1;
+  auto load_stage = [&](PStage<WPL, MBW, NB, XLDS>& st, int grp) {
+    grp = min(grp, glast);  // past the wave's last group: re-read it (cache hits, unused)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const gptr<const uint32_t> wp = wbase[nb] + static_cast<size_t>(grp) * 64 * WPL;
+      if constexpr (WM == 1) {
+        load_tile_words<WPL>(st.w[nb], wp);
+      } else {
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) st.w[nb].w[i] = wp[i];
+      }
+      st.s2[nb] = sbase[nb][static_cast<size_t>(grp) * 8];
+    }
+    if constexpr (!XLDS) {
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int t = 0; t < WPL; ++t)
+          st.x[mb][t] = *reinterpret_cast<gptr<const u32x4>>(xrow[mb] + static_cast<size_t>(grp) * GS + 8 * t);
+    }
+  };
+
+  PStage<WPL, MBW, NB, XLDS> stage[P];
+  const bool active = g1 > g0;
+  if (active) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) load_stage(stage[p], g0 + p);
+  }
+
+  if constexpr (XLDS) {
+    // Stage the row tile's activations and each group's -24 * row sums. A
+    // group's LPG pieces of a row are consecutive elements of the loop (Mr *
+    // K / 8 is a multiple of LPG, each pass a multiple of 64), so they sit in
+    // consecutive lanes of one pass, all active together.
+    const int chunks = K / 8;
+    for (int e = threadIdx.x; e < Mr * chunks; e += 64 * WAVES) {
+      const int row = e / chunks, c8 = e - row * chunks;
+      const u32x4 d = *reinterpret_cast<gptr<const u32x4>>(to_global(x) +
+                                                          static_cast<size_t>(m0 + row) * K + 8 * c8);
+      *reinterpret_cast<u32x4*>(plds + (row * xstride + 8 * c8) / 2) = d;
+      const float bsum = group_lane_sum<LPG>(neg_bias_sum8(d));
+      if ((c8 % LPG) == 0) {
+        float* dst = xsum + (c8 / LPG) * 16;
+        dst[row] = bsum;
+        if (row == Mr - 1)
+          for (int m = Mr; m < 16; ++m) dst[m] = bsum;
+      }
+    }
+    lds_barrier();  // LDS only: the weight loads in flight keep flying
+  }
+
+  const bf16x8 bias = bias_operand();
+  f32x4 yacc[MBW][NB];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) yacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (active) {
+    const int xl = (min(c16, Mr - 1) * xstride + lg * WPL * 8) / 2;  // XLDS: this lane's row, 4-byte words
+    for (int c = g0; c < g1; c += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int grp = c + p;
+        if (grp < g1) {
+          PStage<WPL, MBW, NB, XLDS>& st = stage[p];
+#pragma unroll
+          for (int mb = 0; mb < MBW; ++mb) {
+            bf16x8 a[WPL];
+            f32x4 accb;
+            if constexpr (XLDS) {
+              const uint32_t* xp = plds + xl + (grp * GS) / 2;
+#pragma unroll
+              for (int t = 0; t < WPL; ++t)
+                a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + 4 * t));
+              accb = *reinterpret_cast<const f32x4*>(xsum + grp * 16 + 4 * lg);
+            } else {
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) a[t] = act_frag(st.x[mb][t]);
+              accb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              f32x4 acc = accb;
+#pragma unroll
+              for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(st.w[nb].w[t]), acc);
+              const float s = fp16_bits_to_f32(static_cast<uint16_t>(st.s2[nb] >> (16 * (c16 & 1))));
+#pragma unroll
+              for (int r = 0; r < 4; ++r) yacc[mb][nb][r] = __builtin_fmaf(s, acc[r], yacc[mb][nb][r]);
+            }
+          }
+          load_stage(st, grp + P);
+        }
+      }
+    }
+  }
+
+  // K reduction over the waves of each K range, through LDS: the value of
+  // register r of (row block mb, column block nb) of lane l from the waves of
+  // K range k at red[((k * MB + mb) * NB + nb) * 4 + r][l]; then each thread
+  // sums the K ranges of its outputs in order. The accumulator of lane l holds
+  // rows 4 (l / 16) + r of column l % 16 of its 16 x 16 block.
+  if constexpr (XLDS) __syncthreads();  // the staged rows are no longer read
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(((wk * MB + mbw0 + mb) * NB + nb) * 4 + r) * 64 + lane] = yacc[mb][nb][r];
+  __syncthreads();
+  constexpr int OUTS = MB * NB * 256;
+  for (int e = threadIdx.x; e < OUTS; e += 64 * WAVES) {
+    // e = ((mb * NB + nb) * 4 + r) * 64 + l
+    const int l = e & 63, r = (e >> 6) & 3, blk = e >> 8;
+    const int mb = blk / NB, nb = blk - mb * NB;
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < WK; ++k) sum += red[((k * MB + mb) * NB + nb) * 256 + r * 64 + l];
+    const int m = m0 + 16 * mb + 4 * (l >> 4) + r;
+    const int n = (b0 + nb) * 16 + (l & 15);
+    if (m < M && n < N) to_global(y)[static_cast<size_t>(m) * N + n] = f32_to_bf16_bits(sum);
+  }
+}
+
+template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1>
+hipError_t launch_plain_t(const GemmArgs& a, hipStream_t stream) {
+  const int NCB = (a.N + 15) / 16;
+  dim3 grid((NCB + NB - 1) / NB, (a.M + 16 * MB - 1) / (16 * MB));
+  const int Mr = a.M < 16 * MB ? a.M : 16 * MB;
+  size_t lds = static_cast<size_t>(WAVES / WM) * MB * NB * 256 * sizeof(float);
+  if (XLDS) lds += static_cast<size_t>(Mr) * (a.K + 8) * 2 + static_cast<size_t>(a.K / GS) * 16 * 4;
+  const void* fn = reinterpret_cast<const void*>(&plain_kernel<GS, MB, NB, WAVES, P, XLDS, WM>);
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  const uint16_t* x = a.x;
+  const uint32_t* qw = a.qweight;
+  const uint16_t* sp = a.scales;
+  uint16_t* y = a.y;
+  int M = a.M, N = a.N, K = a.K;
+  void* kargs[] = {&x, &qw, &sp, &y, &M, &N, &K};
+  return hipLaunchKernel(fn, grid, dim3(64 * WAVES), kargs, lds, stream);
+}
+
+// Shapes measured on the decode layer set (qkv 5120x7168, o 6144x5120, gate_up
+// 5120x34816, down 17408x5120) at group 128, as four separate calls, over
+// every (row blocks, column blocks, waves, groups in flight, staging) form
+// that fits: wide N (gate_up, 2176 column blocks) prefers 4-wave workgroups
+// with 2 to 4 column blocks each; deep K at one or two rows prefers 16 waves
+// and staged rows; the rest 8 waves below 9 rows, 4 waves above, 2 column
+// blocks. Group 256 (twice the registers per group) keeps fewer groups in
+// flight.
+template <int GS>
+hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
+  constexpr int P2 = GS >= 256 ? 1 : 2;
+  constexpr int P4 = GS >= 256 ? 2 : 4;
+  const bool wide = (a.N + 15) / 16 >= 1024;
+  const size_t xlds_rows = static_cast<size_t>(a.M < 16 ? a.M : 16) * (a.K + 8) * 2 +
+                           static_cast<size_t>(a.K / GS) * 64;
+  if (a.M <= 16) {
+    if (wide) {
+      if (a.M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit)
+        return launch_plain_t<GS, 1, 2, 4, P4, true>(a, s);
+      if (a.M <= 4) return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
+      return launch_plain_t<GS, 1, 4, 4, P2, false>(a, s);
+    }
+    if (a.M <= 2 && a.K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit)
+      return launch_plain_t<GS, 1, 2, 16, P2, true>(a, s);
+    if (a.M <= 8) return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
+    return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
+  }
+  if (a.M <= 32) {
+    if (wide) return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
+    return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
+  }
+  // 33 and more rows: 64-row tiles (grid.y covers any M)
+  if (wide) return launch_plain_t<GS, 4, 4, 4, 1, false>(a, s);
+  return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
+  switch (a.group) {
+    case 32: return launch_plain_g<32>(a, stream);
+    case 64: return launch_plain_g<64>(a, stream);
+    case 128: return launch_plain_g<128>(a, stream);
+    case 256: return launch_plain_g<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace w4a16_internal

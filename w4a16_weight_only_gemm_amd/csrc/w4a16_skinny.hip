@@ -1,9 +1,10 @@
-// w4a16_skinny.hip -- the small-M paths (decode and speculative-verify blocks).
+// w4a16_skinny.hip -- the streaming kernel for small M (decode and
+// speculative-verify blocks) behind the workspace entry points and planned
+// calls.
 //
 // At small M the GEMM is bound by the weight stream: every packed weight is
 // read from HBM exactly once and shared by all M rows (ai.satyajit.si page,
-// section "One weight read, shared by every stream"). Both kernels here are
-// built around that stream and share one inner step:
+// section "One weight read, shared by every stream"). The inner step:
 //
 //  * A unit is one tile of the packed format: 16 output columns x one group
 //    (1 KB of packed weights at group 128), stored contiguously in the order
@@ -12,24 +13,21 @@
 //    every step). A wave therefore loads a unit with one contiguous vector load
 //    and feeds it HBM -> VGPR -> dequant -> MFMA without LDS.
 //  * Dequantization is to the exact biased value 24 + q in bf16 (two VALU
-//    ops per bf16 pair); a second MFMA against a constant -24 operand removes
-//    the bias, so the MFMA sees exact codes, products are exact and the fp32
+//    ops per bf16 pair); the bias is removed through the accumulator start
+//    (-24 times the group's row sums, or an MFMA chain against a constant -24
+//    operand), so the MFMA sees exact codes, products are exact and the fp32
 //    accumulator holds sum(x * q) over the group. The group's partial is then
 //    scaled by its fp16 scale and added to the running fp32 result.
 //  * Rows are padded to 16: padded rows repeat row M-1 and are never stored
 //    (an MFMA output row depends only on its own A row).
 //
-// splitk_kernel: a workgroup owns one 16-column block and its whole K range,
-//   split over its waves and reduced through LDS. Needs no workspace.
 // streamk_kernel: a persistent grid of long-lived waves splits the linear
 //   sequence of units (problem, column block, group) -- contiguous in memory --
 //   evenly, so every wave streams one long contiguous run of weights. Column
-//   blocks cut between waves are combined through a caller-provided workspace:
-//   each wave writes its part, and the last to arrive (an atomic counter per
-//   block) sums the parts in wave order and stores the bf16 result, so the
-//   result does not depend on timing. The hand-off uses agent-scope atomics
-//   and explicit waits, not device-wide fences (see publish_part). Several problems (for example the four
-//   projections of a layer) can share one launch.
+//   blocks cut between waves are combined through a caller-provided workspace
+//   in a fixed order, so the result does not depend on timing (see the
+//   hand-off below). Several problems (the four projections of a layer, or a
+//   whole planned step) share one launch.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -49,26 +47,6 @@ struct Words {
 // One unit's packed words for this lane (WPL consecutive words), non-temporal:
 // every weight byte is read once.
 template <int WPL>
-__device__ __forceinline__ void load_words(Words<WPL>& out, const uint32_t* p) {
-  if constexpr (WPL == 1) {
-    out.w[0] = __builtin_nontemporal_load(p);
-  } else if constexpr (WPL == 2) {
-    u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    out.w[0] = v[0];
-    out.w[1] = v[1];
-  } else {
-#pragma unroll
-    for (int h = 0; h < WPL / 4; ++h) {
-      u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + h);
-      out.w[4 * h + 0] = v[0];
-      out.w[4 * h + 1] = v[1];
-      out.w[4 * h + 2] = v[2];
-      out.w[4 * h + 3] = v[3];
-    }
-  }
-}
-
-template <int WPL>
 __device__ __forceinline__ void load_words_g(Words<WPL>& out, gptr<const uint32_t> p) {
   if constexpr (WPL == 1) {
     out.w[0] = __builtin_nontemporal_load(p);
@@ -85,115 +63,6 @@ __device__ __forceinline__ void load_words_g(Words<WPL>& out, gptr<const uint32_
       out.w[4 * h + 2] = v[2];
       out.w[4 * h + 3] = v[3];
     }
-  }
-}
-
-// acc = sum over the group's WPL MFMA steps of a_t * q_t (exact codes).
-template <int WPL>
-__device__ __forceinline__ f32x4 group_product(const Words<WPL>& wq, const bf16x8 (&a)[WPL],
-                                               bf16x8 bias) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < WPL; ++t) {
-    const bf16x8 b = dequant_biased(wq.w[t]);
-    acc = mfma16(a[t], b, acc);
-    acc = mfma16(a[t], bias, acc);
-  }
-  return acc;
-}
-
-// ============================================================== split-K kernel
-
-template <int GS, int RB, int WAVES, int P>
-__global__ __launch_bounds__(64 * WAVES) void splitk_kernel(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
-    const uint16_t* __restrict__ sp, uint16_t* __restrict__ y, int M, int N, int K) {
-  constexpr int WPL = GS / 32;  // packed words per lane per group = MFMA steps per group
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c16 = lane & 15;
-  const int lg = lane >> 4;
-  const int cb = blockIdx.x;
-  const int n0 = cb * 16;
-  const int m0 = blockIdx.y * 16 * RB;
-  const int G = K / GS;
-  // This wave's groups [g0, g1); wave-uniform, so the loop runs on scalar branches.
-  const int g0 = static_cast<int>(static_cast<long long>(G) * wave / WAVES);
-  const int g1 = static_cast<int>(static_cast<long long>(G) * (wave + 1) / WAVES);
-
-  const bf16x8 bias = bias_operand();
-  f32x4 yacc[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) yacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (g1 > g0) {
-    const int glast = g1 - 1;
-    const uint32_t* wp = qw + static_cast<size_t>(cb) * G * 64 * WPL + lane * WPL;
-    const uint16_t* sn = sp + static_cast<size_t>(cb) * G * 16 + c16;
-    const uint16_t* xr[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int m = min(m0 + 16 * rb + c16, M - 1);
-      xr[rb] = x + static_cast<size_t>(m) * K + lg * WPL * 8;
-    }
-    // Vector-memory loads retire in issue order, so a group's activations are
-    // issued together with its weights, P groups ahead. Loads past the wave's
-    // last group re-read it (cache hits), so every load is unconditional.
-    auto load_group = [&](Words<WPL>& o, uint16_t& s, u32x4 (&xa)[RB][WPL], int grp) {
-      grp = min(grp, glast);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-        for (int t = 0; t < WPL; ++t)
-          xa[rb][t] = *reinterpret_cast<const u32x4*>(xr[rb] + static_cast<size_t>(grp) * GS + 8 * t);
-      }
-      load_words<WPL>(o, wp + static_cast<size_t>(grp) * 64 * WPL);
-      s = sn[static_cast<size_t>(grp) * 16];
-    };
-
-    Words<WPL> wq[P];
-    uint16_t sq[P];
-    u32x4 xq[P][RB][WPL];
-#pragma unroll
-    for (int p = 0; p < P; ++p) load_group(wq[p], sq[p], xq[p], g0 + p);
-
-    for (int c = g0; c < g1; c += P) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int grp = c + p;
-        if (grp < g1) {
-          const float s = fp16_bits_to_f32(sq[p]);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            bf16x8 a[WPL];
-#pragma unroll
-            for (int t = 0; t < WPL; ++t) a[t] = act_frag(xq[p][rb][t]);
-            const f32x4 acc = group_product<WPL>(wq[p], a, bias);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[rb][r] = __builtin_fmaf(s, acc[r], yacc[rb][r]);
-          }
-          load_group(wq[p], sq[p], xq[p], grp + P);
-        }
-      }
-    }
-  }
-
-  // Split-K reduction over the waves of the workgroup. The accumulator of lane
-  // l holds rows 4*(l/16)+r of column l%16 of each 16x16 row block.
-  __shared__ float red[WAVES][RB][16][17];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][rb][4 * lg + r][c16] = yacc[rb][r];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < RB * 256; e += 64 * WAVES) {
-    const int rb = e >> 8, row = (e >> 4) & 15, col = e & 15;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += red[w][rb][row][col];
-    const int m = m0 + 16 * rb + row, nn = n0 + col;
-    if (m < M && nn < N) y[static_cast<size_t>(m) * N + nn] = f32_to_bf16_bits(sum);
   }
 }
 
@@ -810,36 +679,6 @@ namespace {
 #define W4A16_STREAMK_WG_PER_CU 2
 #endif
 
-// Split-K shape (waves per workgroup = split-K ways, groups in flight per
-// wave), by M. Measured on the four projections of a decoder layer as separate
-// calls: at M <= 7 eight waves with one group in flight were fastest; from
-// M = 8 on (one, two or four row blocks) four waves with two groups in flight,
-// as the activation loads (one 16-byte fragment per row and MFMA step) grow
-// with M and fewer, deeper-pipelined waves hide them better.
-template <int GS, int RB, int WAVES, int P>
-hipError_t launch_splitk_t(const GemmArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 15) / 16, (a.M + 16 * RB - 1) / (16 * RB));
-  dim3 block(64 * WAVES);
-  const uint16_t* x = a.x;
-  const uint32_t* qw = a.qweight;
-  const uint16_t* sp = a.scales;
-  uint16_t* y = a.y;
-  int M = a.M, N = a.N, K = a.K;
-  void* kargs[] = {&x, &qw, &sp, &y, &M, &N, &K};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&splitk_kernel<GS, RB, WAVES, P>), grid,
-                         block, kargs, 0, stream);
-}
-
-template <int GS>
-hipError_t launch_splitk_g(const GemmArgs& a, hipStream_t stream) {
-  if (a.M <= 7) return launch_splitk_t<GS, 1, 8, 1>(a, stream);
-  if (a.M <= 16) return launch_splitk_t<GS, 1, 4, 2>(a, stream);
-  if (a.M <= 32) return launch_splitk_t<GS, 2, 4, 2>(a, stream);
-  // at 256-wide groups two groups in flight of four row blocks take every
-  // register of the SIMD; one in flight there
-  return launch_splitk_t<GS, 4, 4, (GS >= 256 ? 1 : 2)>(a, stream);
-}
-
 #ifndef W4A16_STREAMK_WIDE_PREFETCH
 #define W4A16_STREAMK_WIDE_PREFETCH 1
 #endif
@@ -963,16 +802,6 @@ int device_cus() {
   return cached[dev];
 }
 
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
-  switch (a.group) {
-    case 32: return launch_splitk_g<32>(a, stream);
-    case 64: return launch_splitk_g<64>(a, stream);
-    case 128: return launch_splitk_g<128>(a, stream);
-    case 256: return launch_splitk_g<256>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 hipError_t launch_streamk(const StreamKProblem* probs, int count, int M, int group, float* part,
                           uint32_t* slots, int* counters, hipStream_t stream) {
   if (count < 1 || count > kMaxProblems || M < 1 || M > 16) return hipErrorInvalidValue;
@@ -1081,11 +910,15 @@ hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan
                 : launch_streamk_x<false, true>(sk, h.group, h.grid, h.lds_bytes, stream);
 }
 
+// w4a16_gemm's M-dispatch. Measured on the decode layer set as four plain
+// calls: the small-M kernel (w4a16_plain.hip) takes 46.5 us at M = 1, 75 at 16,
+// 188 at 64, 341 at 128 and 406 at 192, the one-workgroup-per-tile MFMA engine
+// 470 to 485 us up to M = 128 and 556 at 192 and 256 (where the two tie).
 int choose_path(int M, int N, int K, int group) {
   (void)N;
   (void)K;
   (void)group;
-  return M <= 64 ? W4A16_PATH_SKINNY : W4A16_PATH_LARGE;
+  return M <= 192 ? W4A16_PATH_SKINNY : W4A16_PATH_LARGE;
 }
 
 }  // namespace w4a16_internal
