@@ -2,25 +2,29 @@
 
 A step is one pass of the hot path over one batch: the four projections of one
 27B-class layer (qkv 5120x7168, o 6144x5120, gate+up 5120x34816, down
-17408x5120, group 128) at M activation rows, one w4a16_gemm_grouped call through
-the C ABI (--separate: four w4a16_gemm calls). Weights are packed once per layer
-and kept in HBM; successive steps cycle through --layers distinct layer sets
-(1.39 GB at the default 8) so that no step finds its weights in the 256 MB
-last-level cache. Inputs are resident on the device before the timed region
-starts. The default warmup is long enough (3000 steps) for the clocks to reach
-their sustained level before timing.
+17408x5120, group 128) at M activation rows. The headline step is one
+w4a16_gemm_grouped launch of the four projections as independent GEMMs (with a
+caller workspace); next to it, at every M, the same step as four w4a16_gemm
+calls (no workspace). Weights of --layers distinct layer sets (the 64-layer
+stack by default, 11.07 GB) are packed once and kept in HBM; successive steps
+cycle through them, and through 8 activation/output sets, so no step finds its
+operands in the 256 MB last-level cache. Inputs are resident on the device
+before any timed region.
 
+Timing: a time-based clock warm-up (--clock-warmup seconds of back-to-back
+launches, declared in the line), then per M and step kind --warmup untimed
+steps, exactly --steps timed back-to-back steps (ms_per_step), and --reps (at
+least 50) individually timed steps for the median and p10/p90; the plain calls
+also per projection. GPU clocks and power are sampled once a second with
+amd-smi. Extra entries: every M of --m-list both ways, config 0 (tiny GEMV)
+latency, the full step over all layer sets as one planned launch
+(w4a16_gemm_planned) next to one grouped launch per layer, the W4A8 step, the
+practical read ceiling and the CPU oracle baseline at M = 1, 16 and 64.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
   python bench.py --sweep   the full-step sweep over a 64-layer stack at
                             M = 1 .. 1024 with the step-time model fitted to it
-
-The headline line reports the decode layer set (M = 1) in HBM TB/s over
-algorithmic bytes (packed weights + scales + activations + outputs, counted once
-per call). Extra entries report the verify block (M = 16, TB/s), the batched
-step (M = 1024, TFLOP/s) and the W4A8 step at M = 256 and 1024 (each
-projection's activations quantized to int8, then the int8 MFMA GEMM; TOP/s
-against the int8 MFMA peak).
-
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L] [--graph]
+  python bench.py --head    the output-head workload (N = 248,320)
 """
 from __future__ import annotations
 
@@ -148,27 +152,33 @@ def load_traffic(kernel: str, workload: str):
 
 
 class LayerStore:
-    """Packed weights and scales of L layer sets, resident on the device."""
+    """Packed weights and scales of L layer sets, resident on the device (packing
+    runs in host threads: the generator and the packer release the GIL)."""
 
     def __init__(self, layers: int):
+        from concurrent.futures import ThreadPoolExecutor
+
         import numpy as np
         import torch
 
         import synth
         import w4a16_weight_only_gemm_amd as w4
         self.projs = synth.LAYER_PROJECTIONS
-        self.layers = []
-        for layer in range(layers):
-            entry = []
-            for pi, p in enumerate(self.projs):
-                q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K)
-                s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N,
-                                     p.K // GROUP)
-                qw, sp = w4.w4a16_pack(q, s, GROUP)
-                entry.append((torch.from_numpy(qw.view(np.int32)).to("cuda"),
-                              torch.from_numpy(sp.view(np.int16)).to("cuda")))
-                del q, s, qw, sp
-            self.layers.append(entry)
+
+        def pack(job):
+            layer, pi = job
+            p = self.projs[pi]
+            q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K, threads=2)
+            s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N, p.K // GROUP,
+                                 threads=2)
+            return w4.w4a16_pack(q, s, GROUP)
+
+        jobs = [(layer, pi) for layer in range(layers) for pi in range(len(self.projs))]
+        self.layers = [[None] * len(self.projs) for _ in range(layers)]
+        with ThreadPoolExecutor(max_workers=max(1, synth.default_threads() // 2)) as ex:
+            for (layer, pi), (qw, sp) in zip(jobs, ex.map(pack, jobs)):
+                self.layers[layer][pi] = (torch.from_numpy(qw.view(np.int32)).to("cuda"),
+                                          torch.from_numpy(sp.view(np.int16)).to("cuda"))
         torch.cuda.synchronize()
 
     @property
@@ -176,10 +186,75 @@ class LayerStore:
         return sum(t.numel() * t.element_size() for e in self.layers for pair in e for t in pair)
 
 
-class Workload:
-    """Activations, outputs and launch arguments at M rows for every layer set."""
+class ClockSampler:
+    """GPU clocks and socket power sampled once a second with amd-smi in a
+    background thread, as the throughput page does next to every run ("Update,
+    12 November"): the mean over the XCDs' current gfx clocks, and the socket
+    power. summary(t0, t1) reports the samples taken in [t0, t1]."""
 
-    def __init__(self, store: LayerStore, M: int, grouped: bool):
+    def __init__(self, period: float = 1.0):
+        import threading
+        self.period = period
+        self.samples = []   # (time, mean gfx MHz, min gfx MHz, socket W)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _sample(self):
+        import subprocess
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"],
+                             capture_output=True, text=True, timeout=10)
+        data = json.loads(out.stdout)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                  and isinstance(v["clk"].get("value"), (int, float))]
+        power = gpu["power"]["socket_power"]["value"]
+        if clocks:
+            self.samples.append((time.time(), sum(clocks) / len(clocks), min(clocks), float(power)))
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self._sample()
+            except Exception as e:  # no amd-smi, or output it cannot parse: no samples
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def summary(self, t0: float, t1: float):
+        import statistics
+        s = [x for x in self.samples if t0 <= x[0] <= t1]
+        if not s:
+            return {"samples": 0, "note": self.error or "no sample fell in this interval"}
+        return {"samples": len(s), "sclk_mhz_median": statistics.median(x[1] for x in s),
+                "sclk_mhz_min": min(x[2] for x in s),
+                "power_w_median": statistics.median(x[3] for x in s)}
+
+
+def stats_ms(values):
+    """median, p10 and p90 (ms) of a list of durations in ms."""
+    import numpy as np
+    a = np.asarray(values, dtype=np.float64)
+    return {"reps": int(a.size), "median_ms": float(np.median(a)),
+            "p10_ms": float(np.percentile(a, 10)), "p90_ms": float(np.percentile(a, 90))}
+
+
+class Workload:
+    """Activations, outputs and launch arguments of one layer-set step at M rows.
+    Steps cycle through the store's layer sets (weights) and through `xsets`
+    activation and output sets, so no step finds its operands in the cache
+    from the step before."""
+
+    def __init__(self, store: LayerStore, M: int, xsets: int = 8):
         import ctypes
 
         import numpy as np
@@ -187,14 +262,13 @@ class Workload:
 
         import synth
         import w4a16_weight_only_gemm_amd as w4
-        self.M = M
-        self.store = store
-        self.grouped = grouped
+        self.M, self.store = M, store
+        self.L, self.X = len(store.layers), xsets
         self.x, self.y = [], []
-        for layer in range(len(store.layers)):
+        for i in range(xsets):
             xs, ys = [], []
             for pi, p in enumerate(store.projs):
-                xb = synth.gen_x(synth.tensor_id(synth.KIND_X, layer, pi, M), M, p.K)
+                xb = synth.gen_x(synth.tensor_id(synth.KIND_X, i, pi, M), M, p.K)
                 xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16))
                 ys.append(torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda"))
             self.x.append(xs)
@@ -202,45 +276,44 @@ class Workload:
         cols = sum(p.N for p in store.projs)
         self.ws_bytes = w4.w4a16_workspace_bytes(M, cols)
         self.ws = torch.zeros(max(1, self.ws_bytes // 4), dtype=torch.int32, device="cuda")
-        # raw launch arguments, so the timed loop does no Python-side checking
-        self.args, self.problems = [], []
-        for layer in range(len(store.layers)):
+        # raw launch arguments per step kind, so the timed loops do no Python checking
+        self.plain, self.problems, self._keep = [], [], []
+        for layer in range(self.L):
+            xi = layer % xsets
             la, entries = [], []
             for pi, p in enumerate(store.projs):
                 qw, sp = store.layers[layer][pi]
-                la.append((self.x[layer][pi].data_ptr(), qw.data_ptr(), sp.data_ptr(),
-                           self.y[layer][pi].data_ptr(), M, p.N, p.K, GROUP))
-                entries.append((self.x[layer][pi], qw, sp, self.y[layer][pi], p.N, p.K))
-            self.args.append(la)
+                la.append((self.x[xi][pi].data_ptr(), qw.data_ptr(), sp.data_ptr(),
+                           self.y[xi][pi].data_ptr(), M, p.N, p.K, GROUP))
+                entries.append((self.x[xi][pi], qw, sp, self.y[xi][pi], p.N, p.K))
+            self.plain.append(la)
             arr = w4.make_problems(entries)
-            self.problems.append((arr, ctypes.cast(arr, ctypes.c_void_p).value))
+            self._keep.append(arr)
+            self.problems.append(ctypes.cast(arr, ctypes.c_void_p).value)
 
-    def step_bytes(self) -> int:
-        return sum(algorithmic_bytes(self.M, p.N, p.K, GROUP) for p in self.store.projs)
+    def step_bytes(self, only=None) -> int:
+        return sum(algorithmic_bytes(self.M, p.N, p.K, GROUP)
+                   for i, p in enumerate(self.store.projs) if only is None or i == only)
 
-    def step_flops(self) -> int:
-        return sum(flops(self.M, p.N, p.K) for p in self.store.projs)
+    def step_flops(self, only=None) -> int:
+        return sum(flops(self.M, p.N, p.K)
+                   for i, p in enumerate(self.store.projs) if only is None or i == only)
 
+    # one step (grouped: one w4a16_gemm_grouped launch; plain: four w4a16_gemm calls)
+    def grouped_step(self, lib, stream, s: int):
+        rc = lib.w4a16_gemm_grouped(self.problems[s % self.L], len(self.store.projs), self.M, GROUP,
+                                    self.ws.data_ptr(), self.ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
 
-def run_steps(wl: Workload, lib, stream: int, first: int, count: int, only=None):
-    """Launch `count` steps starting at step index `first`. Grouped steps are one
-    launch (all four projections); otherwise four. With `only`, each step
-    launches just projection `only` (to time the dominant launch by itself)."""
-    L = len(wl.args)
-    for s in range(first, first + count):
-        if wl.grouped:
-            rc = lib.w4a16_gemm_grouped(wl.problems[s % L][1], 4, wl.M, GROUP,
-                                        wl.ws.data_ptr(), wl.ws_bytes, stream)
-            if rc != 0:
-                raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
-            continue
-        la = wl.args[s % L]
-        for pi, a in enumerate(la):
-            if only is not None and pi != only:
-                continue
-            rc = lib.w4a16_gemm(*a, stream)
-            if rc != 0:
-                raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+    def plain_call(self, lib, stream, s: int, pi: int):
+        rc = lib.w4a16_gemm(*self.plain[s % self.L][pi], stream)
+        if rc != 0:
+            raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+
+    def plain_step(self, lib, stream, s: int):
+        for pi in range(len(self.store.projs)):
+            self.plain_call(lib, stream, s, pi)
 
 
 def timed(fn, stream_obj) -> float:
@@ -254,69 +327,110 @@ def timed(fn, stream_obj) -> float:
     return t0.elapsed_time(t1)
 
 
-def time_workload(wl: Workload, steps: int, warmup: int, use_graph: bool, dom: int = 2):
-    """(ms per step, mean dominant-launch duration in ms, steps timed).
+def event_durations(fns, reps: int, stream_obj):
+    """Durations (ms) of `reps` rounds of the launches fns[0](r), fns[1](r), ...,
+    issued back to back, from HIP events recorded on the launch stream between
+    consecutive launches: result[r][i] is launch i of round r."""
+    import torch
+    n = len(fns)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps * n + 1)]
+    evs[0].record(stream_obj)
+    k = 1
+    for r in range(reps):
+        for f in fns:
+            f(r)
+            evs[k].record(stream_obj)
+            k += 1
+    torch.cuda.synchronize()
+    return [[evs[r * n + i].elapsed_time(evs[r * n + i + 1]) for i in range(n)] for r in range(reps)]
 
-    The dominant launch (the grouped launch, or projection `dom` otherwise) is
-    timed by itself: `steps` back-to-back launches between two events on the
-    stream they are launched on, divided by `steps`."""
+
+def clock_warmup(fn, seconds: float):
+    """Launch fn() back to back for about `seconds` of wall time (a time-based
+    warm-up: the clocks reach their sustained level only after a few thousand
+    launches, whatever --warmup says)."""
+    import torch
+    t_end = time.time() + seconds
+    n = 0
+    while n < 2 or time.time() < t_end:
+        for _ in range(16):
+            fn()
+        n += 16
+        torch.cuda.synchronize()
+    return n
+
+
+def window_stats(fn, reps: int, per: int, stream_obj):
+    """Per-call durations (ms) from `reps` windows of `per` back-to-back calls
+    fn(r * per + i), each window bracketed by HIP events on the launch stream
+    (no event between the calls of a window, which would add a gap); median and
+    p10/p90 over the windows' means."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record(stream_obj)
+    for r in range(reps):
+        for i in range(per):
+            fn(r * per + i)
+        evs[r + 1].record(stream_obj)
+    torch.cuda.synchronize()
+    st = stats_ms([evs[r].elapsed_time(evs[r + 1]) / per for r in range(reps)])
+    st["calls_per_rep"] = per
+    return st
+
+
+def measure(wl: Workload, kind: str, steps: int, warmup: int, reps: int, warm_s: float = 0.3):
+    """One step kind at wl.M: a time-based warm-up of this very step (warm_s
+    seconds: the clocks settle differently for different M), `warmup` untimed
+    steps, the mean ms per step over exactly `steps` back-to-back steps, then
+    the median and p10/p90 over `reps` windows of 10 back-to-back steps (and,
+    for the plain calls, of each projection's call alone)."""
     import torch
 
     import w4a16_weight_only_gemm_amd as w4
     lib = w4._lib
     cur = torch.cuda.current_stream()
     stream = cur.cuda_stream
-    L = len(wl.args)
-
-    run_steps(wl, lib, stream, 0, warmup)
+    step = wl.grouped_step if kind == "grouped" else wl.plain_step
+    clock_warmup(lambda: step(lib, stream, 0), warm_s)
+    for s in range(warmup):
+        step(lib, stream, s)
     torch.cuda.synchronize()
-    if use_graph:
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(cur)
-        with torch.cuda.stream(s):
-            run_steps(wl, lib, s.cuda_stream, 0, L)  # warm the capture stream
-        cur.wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            run_steps(wl, lib, torch.cuda.current_stream().cuda_stream, 0, L)
-        for _ in range(max(1, warmup // L)):
-            graph.replay()
-        reps = max(1, steps // L)
-        torch.cuda.synchronize()
-
-        def replay():
-            for _ in range(reps):
-                graph.replay()
-        step_ms, nsteps = timed(replay, cur) / (reps * L), reps * L
-    else:
-        step_ms, nsteps = timed(lambda: run_steps(wl, lib, stream, 0, steps), cur) / steps, steps
-
-    only = None if wl.grouped else dom
-    run_steps(wl, lib, stream, 0, warmup, only=only)
-    torch.cuda.synchronize()
-    dom_ms = timed(lambda: run_steps(wl, lib, stream, 0, steps, only=only), cur) / steps
-    return step_ms, dom_ms, nsteps
+    ms = timed(lambda: [step(lib, stream, s) for s in range(steps)], cur) / steps
+    out = {"ms_per_step": ms, "warmup_s": warm_s}
+    out["step"] = window_stats(lambda s: step(lib, stream, s), reps, 10, cur)
+    if kind == "plain":
+        out["per_projection"] = {}
+        for pi, p in enumerate(wl.store.projs):
+            st = window_stats(lambda s, pi=pi: wl.plain_call(lib, stream, s, pi), reps, 10, cur)
+            st["tbps_at_median"] = wl.step_bytes(pi) / (st["median_ms"] * 1e-3) / 1e12
+            st["tflops_at_median"] = wl.step_flops(pi) / (st["median_ms"] * 1e-3) / 1e12
+            out["per_projection"][p.name] = st
+    return out
 
 
-def check_parity(wl: Workload, layer: int, cols: int = 64):
-    """Sampled parity of the last outputs of one layer against the oracle:
-    max over sampled elements of |y - y_ref| / (1e-2 (1 + |y_ref|))."""
+def check_parity(wl: Workload, kind: str, cols: int = 64):
+    """One step on layer set 0 with activation set 0, then sampled parity of its
+    outputs against the oracle: max over sampled elements of
+    |y - y_ref| / (1e-2 (1 + |y_ref|)) (all columns of the sample, up to 64 rows)."""
     import numpy as np
     import torch
 
     import oracle
     import synth
+    import w4a16_weight_only_gemm_amd as w4
+    stream = torch.cuda.current_stream().cuda_stream
+    (wl.grouped_step if kind == "grouped" else wl.plain_step)(w4._lib, stream, 0)
+    torch.cuda.synchronize()
     worst = 0.0
     for pi, p in enumerate(wl.store.projs):
         rng = np.random.default_rng(pi)
         c = np.sort(rng.choice(p.N, cols, replace=False))
         rows = min(wl.M, 64)
-        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K)[c]
-        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N, p.K // GROUP)[c]
-        x = synth.gen_x(synth.tensor_id(synth.KIND_X, layer, pi, wl.M), wl.M, p.K, rows=(0, rows))
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, pi), p.N, p.K)[c]
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, pi), p.N, p.K // GROUP)[c]
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 0, pi, wl.M), wl.M, p.K, rows=(0, rows))
         ref = oracle.gemm(x, q, s, GROUP, threads=synth.default_threads())
-        y = wl.y[layer][pi][:rows].view(torch.int16).cpu().numpy().view(np.uint16)[:, c]
+        y = wl.y[0][pi][:rows].view(torch.int16).cpu().numpy().view(np.uint16)[:, c]
         yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         worst = max(worst, float(np.max(np.abs(yv - ref) / (1e-2 * (1 + np.abs(ref))))))
     return worst
@@ -339,17 +453,21 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
     cur = torch.cuda.current_stream()
     stream = cur.cuda_stream
     M = wl.M
-    L = len(wl.args)
+    L = wl.L
     steps_args, keep = [], []
+    xq_sets = {}
     for layer in range(L):
+        xi = layer % wl.X
+        if xi not in xq_sets:
+            xq_sets[xi] = [(torch.empty((M, p.K), dtype=torch.int8, device="cuda"),
+                            torch.empty((M,), dtype=torch.float32, device="cuda"))
+                           for p in wl.store.projs]
         qents, gents = [], []
         for pi, p in enumerate(wl.store.projs):
-            xq = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
-            sx = torch.empty((M,), dtype=torch.float32, device="cuda")
-            x, qw, sp, y = wl.args[layer][pi][:4]
+            xq, sx = xq_sets[xi][pi]
+            x, qw, sp, y = wl.plain[layer][pi][:4]
             qents.append((x, xq.data_ptr(), sx.data_ptr(), p.K))
             gents.append((xq.data_ptr(), sx.data_ptr(), qw, sp, y, p.N, p.K))
-            keep += [xq, sx]
         qa = w4.make_w4a8_quantize_problems(qents)
         ga = w4.make_w4a8_problems(gents)
         keep += [qa, ga]
@@ -367,11 +485,12 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
             if rc != 0:
                 raise RuntimeError(f"w4a8_gemm_grouped failed with status {rc}")
 
+    clock_warmup(lambda: run(0, 1), 0.3)
     run(0, warmup)
     torch.cuda.synchronize()
     step_ms = timed(lambda: run(0, steps), cur) / steps
     dom_ms = timed(lambda: run(0, steps, gemm_only=True), cur) / steps
-    run(0, L)  # every layer's outputs from the full chain
+    run(0, 1)  # layer set 0, activation set 0, through the full chain
     torch.cuda.synchronize()
     worst = 0.0
     for pi, p in enumerate(wl.store.projs):
@@ -387,6 +506,183 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
         yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         worst = max(worst, float(np.max(np.abs(yv - ref) / (1e-2 * (1 + np.abs(ref))))))
     return step_ms, dom_ms, worst
+
+
+def tiny_latency(reps: int = 200):
+    """Config 0 (M = 1, K = 256, N = 512, group 64) through w4a16_gemm: per-call
+    latency from events between back-to-back calls (cache-resident; latency
+    only), and its parity ratio against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import w4a16_weight_only_gemm_amd as w4
+    t = synth.TINY
+    M, N, K, g = t["M"], t["N"], t["K"], t["group"]
+    x, q, s = synth.tiny_inputs()
+    qw, sp = w4.w4a16_pack(q, s, g)
+    dx = torch.from_numpy(x.view(np.int16)).to("cuda")
+    dq = torch.from_numpy(qw.view(np.int32)).to("cuda")
+    ds = torch.from_numpy(sp.view(np.int16)).to("cuda")
+    dy = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    cur = torch.cuda.current_stream()
+    args = (dx.data_ptr(), dq.data_ptr(), ds.data_ptr(), dy.data_ptr(), M, N, K, g, cur.cuda_stream)
+
+    def call(_r):
+        rc = w4._lib.w4a16_gemm(*args)
+        if rc != 0:
+            raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+    for r in range(100):
+        call(r)
+    d = event_durations([call], reps, cur)
+    y = (dy.cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = oracle.gemm(x, q, s, g)
+    parity = float(np.max(np.abs(y - ref) / (1e-2 * (1 + np.abs(ref)))))
+    t0 = time.perf_counter()
+    n_cpu = 0
+    while time.perf_counter() - t0 < 0.5:
+        oracle.gemm(x, q, s, g)
+        n_cpu += 1
+    cpu_us = (time.perf_counter() - t0) / n_cpu * 1e6
+    st = stats_ms([v[0] for v in d])
+    return {"workload": f"tiny GEMV M={M} K={K} N={N} group {g}, one w4a16_gemm call "
+                        f"(cache-resident: latency only)",
+            "latency_us_median": st["median_ms"] * 1e3, "latency_us_p10": st["p10_ms"] * 1e3,
+            "latency_us_p90": st["p90_ms"] * 1e3, "reps": st["reps"], "parity_ratio": parity,
+            "oracle_us_one_thread": cpu_us}
+
+
+def stack_steps(store: LayerStore, rows, sampler=None, passes: int = 10, xsets: int = 8,
+                plain: bool = False):
+    """The full-step workload (every layer of the store, four projections each)
+    at each M in `rows`: one planned launch over all of the step's GEMMs, one
+    grouped launch per layer and (with plain) four w4a16_gemm calls per layer,
+    each timed over `passes` steps after a 300 ms warm-up. Activations from the
+    seeded generator, one set per (layer % xsets, projection); outputs per
+    layer."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    cur = torch.cuda.current_stream()
+    stream = cur.cuda_stream
+    projs = store.projs
+    L = len(store.layers)
+    W = store.weight_bytes
+    per_row = L * sum(2 * (p.K + p.N) for p in projs)
+    flops_row = L * sum(2 * p.K * p.N for p in projs)
+    out = []
+    for M in rows:
+        t_begin = time.time()
+        X = min(xsets, L)
+        xs = [[torch.from_numpy(synth.gen_x(synth.tensor_id(synth.KIND_X, i, pi, M), M, p.K)
+                                .view(np.int16)).to("cuda").view(torch.bfloat16)
+               for pi, p in enumerate(projs)] for i in range(X)]
+        ys = [[torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
+              for _ in range(L)]
+        entries = [(xs[l % X][i], store.layers[l][i][0], store.layers[l][i][1], ys[l][i], p.N, p.K)
+                   for l in range(L) for i, p in enumerate(projs)]
+        plan = w4.w4a16_plan_build(entries, M, GROUP)
+        plan_dev = torch.from_numpy(plan).to("cuda")
+        pws_bytes = w4.w4a16_plan_workspace_bytes(plan)
+        pws = torch.zeros(max(1, pws_bytes // 4), dtype=torch.int32, device="cuda")
+        cols = sum(p.N for p in projs)
+        gws_bytes = w4.w4a16_workspace_bytes(M, cols)
+        gws = torch.zeros(max(1, gws_bytes // 4), dtype=torch.int32, device="cuda")
+        arrs = [w4.make_problems(entries[4 * l:4 * l + 4]) for l in range(L)]
+        ptrs = [ctypes.cast(a, ctypes.c_void_p).value for a in arrs]
+
+        def planned():
+            rc = lib.w4a16_gemm_planned(plan.ctypes.data, plan_dev.data_ptr(), pws.data_ptr(),
+                                        pws_bytes, stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_gemm_planned failed with status {rc}")
+
+        def grouped():
+            for ptr in ptrs:
+                rc = lib.w4a16_gemm_grouped(ptr, len(projs), M, GROUP, gws.data_ptr(), gws_bytes,
+                                            stream)
+                if rc != 0:
+                    raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
+
+        def plain_calls():
+            for (x, qw, sp, y, N, K) in entries:
+                rc = lib.w4a16_gemm(x.data_ptr(), qw.data_ptr(), sp.data_ptr(), y.data_ptr(), M, N,
+                                    K, GROUP, stream)
+                if rc != 0:
+                    raise RuntimeError(f"w4a16_gemm failed with status {rc}")
+
+        b = W + M * per_row
+        f = M * flops_row
+        row = {"M": M}
+        kinds = [("planned", planned), ("grouped_per_layer", grouped)]
+        if plain:
+            kinds.append(("plain_calls", plain_calls))
+        for name, fn in kinds:
+            clock_warmup(fn, 0.3)
+            st = window_stats(lambda r: fn(), passes, 1, cur)
+            ms = st["median_ms"]
+            row[name] = {"ms_per_step_median": ms, "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+                         "tbps": b / (ms * 1e-3) / 1e12, "tflops": f / (ms * 1e-3) / 1e12,
+                         "positions_per_s": M / (ms * 1e-3),
+                         "hbm_frac": b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                         "mfma_frac": f / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+        if sampler is not None:
+            row["clock"] = sampler.summary(t_begin, time.time())
+        out.append(row)
+        pl = row["planned"]
+        print(f"# stack M={M}: planned {pl['ms_per_step_median']:.3f} ms/step ({pl['tbps']:.2f} TB/s,"
+              f" {pl['tflops']:.1f} TFLOP/s); grouped per layer "
+              f"{row['grouped_per_layer']['ms_per_step_median']:.3f} ms", file=sys.stderr, flush=True)
+        del xs, ys, pws, gws, plan_dev, arrs
+        torch.cuda.empty_cache()
+    return {"W": W, "per_row": per_row, "flops_row": flops_row, "rows": out}
+
+
+def cpu_baseline(seconds_target: float = 15.0, single_seconds: float = 5.0,
+                 other_rows=(16, 64), other_seconds: float = 5.0):
+    """The oracle, as it stands, on the host cores, in the metric's unit:
+    decode layer sets (M = 1), projection after projection, layer after layer,
+    for about `seconds_target` seconds on all host threads, then about
+    `single_seconds` on one thread; then the layer sets at each M of
+    `other_rows` for about `other_seconds` each on all threads."""
+    import synth
+    import oracle
+
+    def run(M, threads, seconds):
+        done_bytes, done_flops, t_total, count, layer = 0, 0, 0.0, 0, 0
+        while t_total < seconds:
+            for pi, p in enumerate(synth.LAYER_PROJECTIONS):
+                x, q, s = synth.layer_inputs(layer % 64, pi, M)
+                t0 = time.perf_counter()
+                oracle.gemm(x, q, s, GROUP, threads=threads)
+                t_total += time.perf_counter() - t0
+                done_bytes += algorithmic_bytes(M, p.N, p.K, GROUP)
+                done_flops += flops(M, p.N, p.K)
+                count += 1
+                if t_total >= seconds:
+                    break
+            layer += 1
+        return done_bytes / t_total / 1e12, done_flops / t_total / 1e12, count, t_total
+
+    threads = synth.default_threads()
+    value, _, count, t_total = run(1, threads, seconds_target)
+    single, _, count1, t1 = run(1, 1, single_seconds)
+    out = {"value": value, "unit": "TB/s", "cores": threads, "kind": "oracle",
+           "single_thread_value": single,
+           "sample": f"{count} projection GEMMs of decode layer sets (M=1, group {GROUP}), fp64 "
+                     f"oracle, {t_total:.1f} s on {threads} threads; single thread: {count1} "
+                     f"projection GEMMs, {t1:.1f} s", "by_M": {}}
+    for M in other_rows:
+        tb, tf, c, tt = run(M, threads, other_seconds)
+        out["by_M"][str(M)] = {"tbps": tb, "tflops": tf, "cores": threads,
+                               "sample": f"{c} projection GEMMs of layer sets at M={M}, {tt:.1f} s"}
+    return out
 
 
 def read_ceiling(nbytes: int, buffers: int = 8, steps: int = 500, warmup: int = 1000):
@@ -417,39 +713,6 @@ def read_ceiling(nbytes: int, buffers: int = 8, steps: int = 500, warmup: int = 
     ms = timed(lambda: run(steps), cur) / steps
     del bufs
     return nbytes / (ms * 1e-3) / 1e9, ms
-
-
-def cpu_baseline(seconds_target: float = 15.0, single_seconds: float = 5.0):
-    """The oracle, as it stands, on the host cores: decode layer sets (M = 1),
-    projection after projection, layer after layer, until about
-    `seconds_target` seconds of CPU work on all host threads, then about
-    `single_seconds` on one thread; throughput in the metric's unit."""
-    import synth
-    import oracle
-
-    def run(threads, seconds):
-        done_bytes, t_total, count, layer = 0, 0.0, 0, 0
-        while t_total < seconds:
-            for pi, p in enumerate(synth.LAYER_PROJECTIONS):
-                x, q, s = synth.layer_inputs(layer % 64, pi, 1)
-                t0 = time.perf_counter()
-                oracle.gemm(x, q, s, GROUP, threads=threads)
-                t_total += time.perf_counter() - t0
-                done_bytes += algorithmic_bytes(1, p.N, p.K, GROUP)
-                count += 1
-                if threads == 1 and t_total >= seconds:
-                    break
-            layer += 1
-        return done_bytes / t_total / 1e12, count, layer, t_total
-
-    threads = synth.default_threads()
-    value, count, layers, t_total = run(threads, seconds_target)
-    single, count1, _, t1 = run(1, single_seconds)
-    return {"value": value, "unit": "TB/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": single,
-            "sample": f"{count} projection GEMMs (decode layer sets M=1, {layers} layers, "
-                      f"group {GROUP}), fp64 oracle, {t_total:.1f} s on {threads} threads; "
-                      f"single thread: {count1} projection GEMMs, {t1:.1f} s"}
 
 
 COPY_BYTES = 512 << 20  # calibration kernels: 512 MiB written (fill), 512 MiB read (sum)
@@ -512,94 +775,29 @@ def traffic_from_pmc(fetch_csv: str, write_csv: str, kernel_substr: str, key: st
 SWEEP_ROWS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024)
 
 
-def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS):
+def run_sweep(layers: int, passes: int, rows=SWEEP_ROWS, plain: bool = True):
     """The full-step sweep: a stack of `layers` layer sets (64 by default, the
     27B-class depth), each step one pass over every layer's four projections
-    at M rows; per-M step time, then the step-time model fitted to it."""
-    import torch
-
-    import w4a16_weight_only_gemm_amd as w4
-    lib = w4._lib
+    at M rows; per-M step time of one planned launch (the primary figure), of
+    one grouped launch per layer and of four plain calls per layer, then the
+    step-time model fitted to the planned times."""
     store = LayerStore(layers)
-    projs = store.projs
-    W = store.weight_bytes
-    per_row = layers * sum(2 * (p.K + p.N) for p in projs)          # x in, y out per row
-    flops_row = layers * sum(2 * p.K * p.N for p in projs)
-    cur = torch.cuda.current_stream()
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(0)
-    out = []
-    for M in rows:
-        # activations ~N(0, 1) in bf16, one set per layer and projection
-        xs = [[torch.randn((M, p.K), generator=gen, device="cuda").to(torch.bfloat16) for p in projs]
-              for _ in range(layers)]
-        ys = [[torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
-              for _ in range(layers)]
-        grouped = True
-        cols = sum(p.N for p in projs)
-        ws_bytes = w4.w4a16_workspace_bytes(M, cols)
-        ws = torch.zeros(max(1, ws_bytes // 4), dtype=torch.int32, device="cuda")
-        launches = []
-        for layer in range(layers):
-            entries = [(xs[layer][i], store.layers[layer][i][0], store.layers[layer][i][1],
-                        ys[layer][i], p.N, p.K) for i, p in enumerate(projs)]
-            if grouped:
-                arr = w4.make_problems(entries)
-                launches.append(("g", arr))
-            else:
-                launches.append(("s", [(e[0].data_ptr(), e[1].data_ptr(), e[2].data_ptr(),
-                                        e[3].data_ptr(), M, e[4], e[5], GROUP) for e in entries]))
-        import ctypes
-        stream = cur.cuda_stream
-
-        def one_pass():
-            for kind, a in launches:
-                if kind == "g":
-                    rc = lib.w4a16_gemm_grouped(ctypes.cast(a, ctypes.c_void_p).value, len(projs), M,
-                                                GROUP, ws.data_ptr(), ws_bytes, stream)
-                    if rc != 0:
-                        raise RuntimeError(f"w4a16_gemm_grouped failed with status {rc}")
-                else:
-                    for args in a:
-                        rc = lib.w4a16_gemm(*args, stream)
-                        if rc != 0:
-                            raise RuntimeError(f"w4a16_gemm failed with status {rc}")
-
-        # warm up for 300 ms (at least two passes): clocks reach their
-        # sustained level only after a few thousand launches
-        import time
-        t_end = time.time() + 0.3
-        n_warm = 0
-        while n_warm < 2 or time.time() < t_end:
-            one_pass()
-            n_warm += 1
-            torch.cuda.synchronize()
-
-        def timed_passes():
-            for _ in range(passes):
-                one_pass()
-        ms = timed(timed_passes, cur) / passes
-        b = W + M * per_row
-        f = M * flops_row
-        row = {"M": M, "ms_per_step": ms, "tbps": b / (ms * 1e-3) / 1e12,
-               "tflops": f / (ms * 1e-3) / 1e12, "positions_per_s": M / (ms * 1e-3),
-               "hbm_frac": b / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-               "mfma_frac": f / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
-        out.append(row)
-        print(f"# sweep M={M}: {ms:.3f} ms/step, {row['tbps']:.2f} TB/s, {row['tflops']:.1f} TFLOP/s",
-              file=sys.stderr, flush=True)
-        del xs, ys, ws, launches
-        torch.cuda.empty_cache()
-    eta, P, bend = fit_step_model([r["M"] for r in out], [r["ms_per_step"] * 1e-3 for r in out],
+    res = stack_steps(store, rows, passes=passes, plain=plain)
+    W, per_row, flops_row = res["W"], res["per_row"], res["flops_row"]
+    out = res["rows"]
+    eta, P, bend = fit_step_model([r["M"] for r in out],
+                                  [r["planned"]["ms_per_step_median"] * 1e-3 for r in out],
                                   W, per_row, flops_row, HBM_PEAK_GBS * 1e9)
     return {"workload": f"{layers}-layer stack of the decode layer set (qkv, o, gate_up, down), group "
-                        f"{GROUP}; one step = every layer's four projections at M rows, one grouped "
-                        f"launch per layer",
+                        f"{GROUP}; one step = every layer's four projections at M rows, "
+                        f"independent GEMMs: one planned launch over all of them (primary), one "
+                        f"grouped launch per layer, or four w4a16_gemm calls per layer",
             "weight_bytes": W, "rows": out,
             "model": {"eta": eta, "P_tflops": P / 1e12, "bend_rows": bend,
                       "bw_gbs": HBM_PEAK_GBS, "per_row_bytes": per_row, "flops_per_row": flops_row,
+                      "fitted_to": "planned launch",
                       "note": "t_step(M) = max((W + M a) / (eta BW), M F / P), eta and P the "
-                              "best fractions seen over the sweep"}}
+                              "best fractions seen over the sweep (an optimistic envelope)"}}
 
 
 HEAD_N, HEAD_K = 248320, 5120
@@ -650,31 +848,39 @@ def run_head(steps: int, warmup: int, rows=HEAD_ROWS):
             "rows": out}
 
 
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=3000)
-    ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--graph", action="store_true",
-                    help="replay the steps from a captured HIP graph (no host launch cost)")
+    ap.add_argument("--layers", type=int, default=64,
+                    help="layer sets kept resident and cycled through (64: the 27B-class stack)")
+    ap.add_argument("--clock-warmup", type=float, default=2.0,
+                    help="seconds of back-to-back launches before any timing, whatever --warmup "
+                         "says (declared in the line)")
+    ap.add_argument("--reps", type=int, default=100,
+                    help="individually timed steps behind each median and p10/p90 (>= 50)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--m-list", default="1,16,1024")
+    ap.add_argument("--m-list", default="1,16,64,1024")
+    ap.add_argument("--stack-m-list", default="1,16,64,1024",
+                    help="row counts of the full-step (all layers) planned launch; empty: none")
     ap.add_argument("--w4a8-m-list", default="256,1024",
                     help="row counts of the W4A8 batched step (empty: none)")
+    ap.add_argument("--no-smi", action="store_true", help="do not sample clocks with amd-smi")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for PMC byte calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="compute profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--traffic-key", default="streamk_grouped|M=1")
     ap.add_argument("--traffic-kernel", default="::streamk_kernel<")
-    ap.add_argument("--separate", action="store_true",
-                    help="four launches per step at every M (no grouped streaming launch)")
+    ap.add_argument("--only", choices=["grouped", "plain"],
+                    help="time only this step kind at each M of --m-list (for profiling)")
     ap.add_argument("--sweep", action="store_true",
                     help="full-step sweep over a layer stack at M = 1..1024 and the step-time "
                          "model fitted to it (one JSON object), instead of the headline line")
     ap.add_argument("--sweep-layers", type=int, default=64)
-    ap.add_argument("--sweep-passes", type=int, default=5)
+    ap.add_argument("--sweep-passes", type=int, default=10)
     ap.add_argument("--head", action="store_true",
                     help="output-head workload (N = 248,320, K = 5120) at M = 1..16 (one JSON "
                          "object), instead of the headline line")
@@ -693,7 +899,7 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    import w4a16_weight_only_gemm_amd  # noqa: F401  (fails loudly without the library)
+    import w4a16_weight_only_gemm_amd as w4  # fails loudly without the library
     if args.sweep:
         print(json.dumps(run_sweep(args.sweep_layers, args.sweep_passes)))
         return 0
@@ -701,55 +907,97 @@ def main(argv=None):
         print(json.dumps(run_head(args.steps, min(args.warmup, 1000))))
         return 0
 
+    sampler = None if args.no_smi else ClockSampler().start()
     t0 = time.time()
     store = LayerStore(args.layers)
     print(f"# packed {args.layers} layer sets, {store.weight_bytes / 1e9:.3f} GB resident, "
           f"{time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    lib = w4._lib
+    cur = torch.cuda.current_stream()
+    stream = cur.cuda_stream
+    ms_list = [int(v) for v in args.m_list.split(",")]
+    kinds = [args.only] if args.only else ["grouped", "plain"]
+    reps = max(50, args.reps)
+
+    # time-based clock warm-up on the headline step
+    wl0 = Workload(store, ms_list[0])
+    t_w = time.time()
+    n_w = clock_warmup(lambda: wl0.grouped_step(lib, stream, 0), args.clock_warmup)
+    warm = {"seconds": args.clock_warmup, "launches": n_w}
+    if sampler is not None:
+        warm["clock"] = sampler.summary(t_w, time.time())
+    del wl0
 
     results = {}
-    for M in [int(v) for v in args.m_list.split(",")]:
-        wl = Workload(store, M, grouped=not args.separate)
-        ms, dom_ms, nsteps = time_workload(wl, args.steps, args.warmup, args.graph)
-        parity = check_parity(wl, 0)
-        results[M] = (wl, ms, dom_ms, parity, nsteps)
-        print(f"# M={M}: {ms * 1e3:.2f} us/step, dominant launch {dom_ms * 1e3:.2f} us, "
-              f"parity ratio {parity:.3f}", file=sys.stderr, flush=True)
+    for M in ms_list:
+        wl = Workload(store, M)
+        entry = {}
+        for kind in kinds:
+            t_k = time.time()
+            r = measure(wl, kind, args.steps, args.warmup, reps)
+            r["parity_ratio"] = check_parity(wl, kind)
+            b, f = wl.step_bytes(), wl.step_flops()
+            ms = r["ms_per_step"]
+            r.update({"tbps": b / (ms * 1e-3) / 1e12, "tflops": f / (ms * 1e-3) / 1e12,
+                      "positions_per_s": M / (ms * 1e-3)})
+            if sampler is not None:
+                r["clock"] = sampler.summary(t_k, time.time())
+            entry[kind] = r
+            print(f"# M={M} {kind}: {ms * 1e3:.2f} us/step (median {r['step']['median_ms'] * 1e3:.2f},"
+                  f" p10 {r['step']['p10_ms'] * 1e3:.2f}, p90 {r['step']['p90_ms'] * 1e3:.2f}), "
+                  f"{r['tbps']:.3f} TB/s, {r['tflops']:.1f} TFLOP/s, parity ratio "
+                  f"{r['parity_ratio']:.3f}", file=sys.stderr, flush=True)
+        results[M] = (wl.step_bytes(), wl.step_flops(), entry)
         del wl
+        torch.cuda.empty_cache()
+    if args.only:
+        if args.copy_calibration:
+            copy_calibration()
+        print(json.dumps({str(M): e for M, (_, _, e) in results.items()}))
+        return 0
 
-    M0 = int(args.m_list.split(",")[0])
-    wl, ms, dom_ms, parity, nsteps = results[M0]
-    step_bytes = wl.step_bytes()
-    value = step_bytes / (ms * 1e-3) / 1e12
-    gu = store.projs[2]
-    if wl.grouped:
-        dom_name = "grouped stream-K launch (qkv+o+gate_up+down) at M=%d" % M0
-        dom_key = "streamk_grouped"
-        dom_bytes = step_bytes
-    else:
-        dom_name = "gate_up projection (5120x34816) at M=%d" % M0
-        dom_key = "gate_up"
-        dom_bytes = algorithmic_bytes(M0, gu.N, gu.K, GROUP)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    workload = (f"decode layer set M={M0}: qkv 5120x7168, o 6144x5120, gate_up 5120x34816, "
-                f"down 17408x5120; int4 weights, group {GROUP}, fp16 scales, bf16 activations")
-    traffic = load_traffic(dom_key, f"M={M0}")
+    M0 = ms_list[0]
+    b0, f0, e0 = results[M0]
+    head = e0["grouped"]
+    ms = head["ms_per_step"]
+    value = b0 / (ms * 1e-3) / 1e12
+    # dominant kernel: the grouped stream-K launch itself (one launch per step),
+    # its mean duration over the timed steps
+    achieved = b0 / (ms * 1e-3) / 1e9
+    traffic = load_traffic("streamk_grouped", f"M={M0}")
+    workload = (f"decode layer set M={M0} as ONE w4a16_gemm_grouped launch of its four "
+                f"independent projections (qkv 5120x7168, o 6144x5120, gate_up 5120x34816, down "
+                f"17408x5120), caller workspace; int4 weights, group {GROUP}, fp16 scales, bf16 "
+                f"activations; {args.layers} layer sets cycled")
     extra = []
-    for M, (wl2, ms2, dom2, par2, _) in results.items():
-        if M == M0:
-            continue
-        b, f = wl2.step_bytes(), wl2.step_flops()
-        e = {"M": M, "ms_per_step": ms2, "tbps": b / (ms2 * 1e-3) / 1e12,
-             "tflops": f / (ms2 * 1e-3) / 1e12, "positions_per_s": M / (ms2 * 1e-3),
-             "parity_ratio": par2}
-        if M >= 256:
-            e["roofline"] = {"bound": "mfma", "achieved": e["tflops"], "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": e["tflops"] / BF16_PEAK_TFLOPS}
-        else:
-            e["roofline"] = {"bound": "hbm", "achieved": e["tbps"] * 1e3, "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": e["tbps"] * 1e3 / HBM_PEAK_GBS}
-        extra.append(e)
+    for M, (b, f, e) in results.items():
+        for kind, r in e.items():
+            if M == M0 and kind == "grouped":
+                continue
+            x = {"M": M, "call": ("one w4a16_gemm_grouped launch (four independent projections)"
+                                  if kind == "grouped" else
+                                  "four w4a16_gemm calls (no workspace), one per projection"),
+                 **{k: v for k, v in r.items()}}
+            if M >= 256:
+                x["roofline"] = {"bound": "mfma", "achieved": r["tflops"], "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": r["tflops"] / BF16_PEAK_TFLOPS}
+            else:
+                x["roofline"] = {"bound": "hbm", "achieved": r["tbps"] * 1e3, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": r["tbps"] * 1e3 / HBM_PEAK_GBS}
+            extra.append(x)
+    extra.append({"config0": tiny_latency()})
+    print(f"# config 0 latency: {extra[-1]['config0']['latency_us_median']:.2f} us median",
+          file=sys.stderr, flush=True)
+    stack_rows = [int(v) for v in args.stack_m_list.split(",") if v]
+    if stack_rows:
+        st = stack_steps(store, stack_rows, sampler=sampler)
+        extra.append({"stack": {
+            "workload": f"full step: all {args.layers} layer sets x four projections as independent "
+                        f"GEMMs ({st['W'] / 1e9:.3f} GB of packed weights and scales): one "
+                        f"w4a16_gemm_planned launch per step, next to one grouped launch per layer",
+            "rows": st["rows"]}})
     for M in [int(v) for v in args.w4a8_m_list.split(",") if v]:
-        wl8 = Workload(store, M, grouped=False)
+        wl8 = Workload(store, M)
         ms8, dom8, par8 = time_w4a8(wl8, args.steps, min(args.warmup, 1000))
         f = wl8.step_flops()
         e = {"path": "w4a8", "M": M, "ms_per_step": ms8, "tops": f / (ms8 * 1e-3) / 1e12,
@@ -762,7 +1010,7 @@ def main(argv=None):
                          "frac": f / (dom8 * 1e-3) / 1e12 / INT8_PEAK_TOPS,
                          "kernel": "w4a8_gemm_grouped launch (qkv+o+gate_up+down) at M=%d" % M}
         if M in results:
-            e["speedup_vs_w4a16_step"] = results[M][1] / ms8
+            e["speedup_vs_w4a16_step"] = results[M][2]["grouped"]["ms_per_step"] / ms8
         print(f"# W4A8 M={M}: {ms8 * 1e3:.2f} us/step, {e['tops']:.1f} TOP/s, grouped GEMM "
               f"{dom8 * 1e3:.2f} us, parity ratio {par8:.3f}", file=sys.stderr, flush=True)
         extra.append(e)
@@ -773,7 +1021,7 @@ def main(argv=None):
         "value": value,
         "unit": "TB/s",
         "n_gpus": 1,
-        "steps": nsteps,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -782,25 +1030,29 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "M": M0, "group": GROUP, "layers_rotated": args.layers,
-                   "graph": bool(args.graph), "positions_per_s": M0 / (ms * 1e-3),
-                   "parity_ratio": parity},
+                   "positions_per_s": M0 / (ms * 1e-3), "parity_ratio": head["parity_ratio"],
+                   "clock_warmup": warm, "step": head["step"], "clock": head.get("clock")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": dom_name},
+                     "kernel": "streamk_kernel: the grouped launch (qkv+o+gate_up+down) at M=%d, "
+                               "mean over the %d timed steps (one launch each)" % (M0, args.steps)},
         "extra": extra,
     }
-    ceil_gbs, ceil_ms = read_ceiling(step_bytes)
+    ceil_gbs, ceil_ms = read_ceiling(b0)
     line["practical_ceiling"] = {
         "value": ceil_gbs, "unit": "GB/s", "frac_of_peak": ceil_gbs / HBM_PEAK_GBS,
         "m1_frac_of_ceiling": achieved / ceil_gbs,
         "kernel": "w4a16_read_probe: one read of the layer set's %d bytes per launch in the "
                   "weight-stream access pattern, 8 rotating buffers, %.2f us per launch"
-                  % (step_bytes - step_bytes % 16, ceil_ms * 1e3)}
+                  % (b0 - b0 % 16, ceil_ms * 1e3)}
     print(f"# practical read ceiling: {ceil_gbs:.0f} GB/s ({ceil_ms * 1e3:.2f} us per "
-          f"{step_bytes / 1e6:.2f} MB); the M={M0} launch reaches {achieved / ceil_gbs:.1%} of it",
+          f"{b0 / 1e6:.2f} MB); the M={M0} launch reaches {achieved / ceil_gbs:.1%} of it",
           file=sys.stderr, flush=True)
     if args.copy_calibration:
         copy_calibration()
+    if sampler is not None:
+        sampler.stop()
+        line["clock_samples"] = {"count": len(sampler.samples), "error": sampler.error}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line))

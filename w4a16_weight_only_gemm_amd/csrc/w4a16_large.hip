@@ -506,10 +506,14 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
 #pragma unroll
       for (int r = 0; r < C::Regs; ++r) sum[r] += v[r];
       // cleared once read (the sum above used every loaded value), so the call
-      // leaves the whole workspace at zero and calls of every kind can share it
+      // leaves the whole workspace at zero and calls of every kind can share
+      // it. The stores follow the sum, so every load has returned; nothing
+      // reads the part again in this call, so plain stores of 16 bytes per
+      // lane do (the wave's Regs x 64 floats in Regs / 4 instructions)
 #pragma unroll
-      for (int r = 0; r < C::Regs; ++r)
-        __hip_atomic_store(part + r * 64 + lane, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < C::Regs / 4; ++j)
+        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                    reinterpret_cast<gptr<u32x4>>(to_global(part)) + j * 64 + lane);
     }
     e.setup(lg_lds, pr.x, pr.qw, pr.sp, args.M, pr.N, pr.K, (tile % pr.MT) * C::Rows,
             tile / pr.MT);
