@@ -18,7 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# W4A16_ORACLE_LIB names another build of oracle.c (the sanitizer test runs the
+# pins against an address/undefined-behaviour sanitizer build through it).
+_LIB_PATH = os.environ.get("W4A16_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
