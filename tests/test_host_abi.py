@@ -137,8 +137,8 @@ def test_select_path():
     assert w4.w4a16_select_path(1, 7168, 5120, 128) == w4.W4A16_PATH_SKINNY
     assert w4.w4a16_select_path(16, 5120, 17408, 128) == w4.W4A16_PATH_SKINNY
     assert w4.w4a16_select_path(1024, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
-    assert w4.w4a16_select_path(192, 5120, 6144, 128) == w4.W4A16_PATH_SKINNY
-    assert w4.w4a16_select_path(193, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
+    assert w4.w4a16_select_path(320, 5120, 6144, 128) == w4.W4A16_PATH_SKINNY
+    assert w4.w4a16_select_path(321, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
     assert w4.w4a16_select_path(1, 512, 256, 48) == -1
     assert w4.w4a16_select_path(-1, 512, 256, 64) == -1
 

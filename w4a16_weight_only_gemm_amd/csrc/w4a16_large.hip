@@ -81,21 +81,6 @@ struct LgCfg {
 };
 
 
-// LDS slot of 16-byte piece p of row r of the activation tile (256-byte
-// rows: one row per line of the 64 banks): p ^ r' ^ ((r' & 4) << 1), r' = r
-// mod 16. A 128-bit LDS read is served in four passes of 16 lanes, the lanes
-// of a pass being those with equal (l5, l2 ^ l3 ^ l4) (found by counting
-// SQ_LDS_BANK_CONFLICT over address patterns on gfx950). A fragment read
-// puts rows 0..15 in lanes 0..15 and pieces p + WPL j in lane group j; with
-// the plain p ^ r' two rows of one pass share a slot at group 128 (four
-// conflict cycles per 128-bit read, as counted). With the extra bit
-// every pass reads 16 distinct slots at groups 128, 64 and 32, and the
-// staging writes (four rows of 16 pieces per wave) stay conflict-free.
-__device__ __forceinline__ int lg_slot(int piece, int row) {
-  const int r = row & 15;
-  return piece ^ r ^ ((r & 4) << 1);
-}
-
 template <int GS, int MB>
 struct StageRegs {
   u32x4 d[LgCfg<GS, MB>::Loads];

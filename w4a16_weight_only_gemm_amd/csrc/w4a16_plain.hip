@@ -76,7 +76,15 @@ struct PStage {
 // weight tile (one is read from HBM, the others hit the caches: the loads are
 // then ordinary, not non-temporal) and each holds the activations of fewer
 // rows, which leaves registers for more groups in flight.
-template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1>
+//
+// XS (group 128, no XLDS): the activation fragments are loaded coalesced --
+// 16 lanes read one row's 256 contiguous bytes of the group, so every load
+// instruction uses whole 128-byte lines -- and turned into the MFMA operand
+// arrangement through a wave-private LDS area (row-swizzled, lg_slot, so both
+// the writes and the 16-row fragment reads are free of bank conflicts). Read
+// directly in operand order, the four lanes of a row sit 64 bytes apart and a
+// load instruction touches 32 lines, a quarter of each.
+template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1, bool XS = false>
 __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ qw,
                                                           const uint16_t* __restrict__ sp,
@@ -88,6 +96,7 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
   constexpr int MBW = MB / WM;    // row blocks per wave
   static_assert(!XLDS || MB == 1, "staged activations: one row block");
   static_assert(WK * WM == WAVES && MBW * WM == MB, "waves and row blocks divide evenly");
+  static_assert(!XS || (GS == 128 && !XLDS), "coalesced staging: group 128, rows not in LDS");
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int c16 = lane & 15, lg = lane >> 4;
@@ -109,7 +118,12 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
   const int xstride = K + 8;                        // bf16 elements
   const int sum_off = XLDS ? (Mr * xstride) / 2 : 0;  // 4-byte words; Mr * xstride is even
   float* const xsum = reinterpret_cast<float*>(plds + sum_off);
+  // XS: this wave's staging area, MBW row blocks of 16 rows x 256 bytes, after
+  // the reduction area
+  constexpr int kXsWaveBytes = XS ? MBW * 16 * 256 : 0;
   float* const red = reinterpret_cast<float*>(plds + (XLDS ? sum_off + G * 16 : 0));
+  unsigned char* const xs_lds = reinterpret_cast<unsigned char*>(plds) +
+                                static_cast<size_t>(WK) * MB * NB * 1024 + wave * kXsWaveBytes;
 
   // Column blocks past the last are clamped on load (their results are not stored).
   gptr<const uint32_t> wbase[NB];
@@ -123,11 +137,23 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
   }
   // activation rows of this lane's A operand, one per row block (rows past M
   // repeat the last row; their MFMA output rows are never stored)
-  gptr<const uint16_t> xrow[MBW];
+  // XS: load instruction i of a row block covers rows 4i + lane / 16, each
+  // 16-lane row reading its 16 pieces of 16 bytes
+  gptr<const uint16_t> xrow[XS ? MBW * 4 : MBW];
+  if constexpr (XS) {
 #pragma unroll
-  for (int mb = 0; mb < MBW; ++mb) {
-    const int m = min(m0 + 16 * (mbw0 + mb) + c16, M - 1);
-    xrow[mb] = to_global(x) + static_cast<size_t>(m) * K + lg * WPL * 8;
+    for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = min(m0 + 16 * (mbw0 + mb) + 4 * i + lg, M - 1);
+        xrow[mb * 4 + i] = to_global(x) + static_cast<size_t>(m) * K + 8 * c16;
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+      const int m = min(m0 + 16 * (mbw0 + mb) + c16, M - 1);
+      xrow[mb] = to_global(x) + static_cast<size_t>(m) * K + lg * WPL * 8;
+    }
   }
 
   const int glast = g1 - 1;
@@ -144,7 +170,13 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
       }
       st.s2[nb] = sbase[nb][static_cast<size_t>(grp) * 8];
     }
-    if constexpr (!XLDS) {
+    if constexpr (XS) {
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st.x[mb][i] = *reinterpret_cast<gptr<const u32x4>>(xrow[mb * 4 + i] + static_cast<size_t>(grp) * GS);
+    } else if constexpr (!XLDS) {
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
@@ -208,8 +240,22 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
                 a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + 4 * t));
               accb = *reinterpret_cast<const f32x4*>(xsum + grp * 16 + 4 * lg);
             } else {
+              if constexpr (XS) {
+                // coalesced pieces into the wave's area, then operand fragments
+                // out of it (the same wave writes and reads: LDS keeps order)
+                unsigned char* area = xs_lds + mb * 16 * 256;
 #pragma unroll
-              for (int t = 0; t < WPL; ++t) a[t] = act_frag(st.x[mb][t]);
+                for (int i = 0; i < 4; ++i) {
+                  const int row = 4 * i + lg;
+                  *reinterpret_cast<u32x4*>(area + row * 256 + lg_slot(c16, row) * 16) = st.x[mb][i];
+                }
+#pragma unroll
+                for (int t = 0; t < WPL; ++t)
+                  a[t] = *reinterpret_cast<const bf16x8*>(area + c16 * 256 + lg_slot(lg * WPL + t, c16) * 16);
+              } else {
+#pragma unroll
+                for (int t = 0; t < WPL; ++t) a[t] = act_frag(st.x[mb][t]);
+              }
               accb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int t = 0; t < WPL; ++t) accb = mfma16(a[t], bias, accb);
@@ -258,14 +304,15 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
   }
 }
 
-template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1>
+template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1, bool XS = false>
 hipError_t launch_plain_t(const GemmArgs& a, hipStream_t stream) {
   const int NCB = (a.N + 15) / 16;
   dim3 grid((NCB + NB - 1) / NB, (a.M + 16 * MB - 1) / (16 * MB));
   const int Mr = a.M < 16 * MB ? a.M : 16 * MB;
   size_t lds = static_cast<size_t>(WAVES / WM) * MB * NB * 256 * sizeof(float);
   if (XLDS) lds += static_cast<size_t>(Mr) * (a.K + 8) * 2 + static_cast<size_t>(a.K / GS) * 16 * 4;
-  const void* fn = reinterpret_cast<const void*>(&plain_kernel<GS, MB, NB, WAVES, P, XLDS, WM>);
+  if (XS) lds += static_cast<size_t>(WAVES) * (MB / WM) * 16 * 256;
+  const void* fn = reinterpret_cast<const void*>(&plain_kernel<GS, MB, NB, WAVES, P, XLDS, WM, XS>);
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
@@ -307,13 +354,26 @@ hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
     if (a.M <= 8) return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
     return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
   }
-  if (a.M <= 32) {
-    if (wide) return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
-    return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
+  if constexpr (GS == 128) {
+    // coalesced activation loads through a wave-private LDS area (XS); the
+    // layer set as four calls: 85 us at M = 32 (116 with operand-order loads),
+    // 143 us at M = 64 (188)
+    if (a.M <= 32) {
+      if (wide) return launch_plain_t<GS, 2, 4, 4, 1, false, 1, true>(a, s);
+      if (a.K >= 12288) return launch_plain_t<GS, 2, 2, 8, 2, false, 1, true>(a, s);
+      return launch_plain_t<GS, 2, 2, 16, 1, false, 2, true>(a, s);
+    }
+    if (wide) return launch_plain_t<GS, 4, 4, 8, 1, false, 4, true>(a, s);
+    return launch_plain_t<GS, 4, 2, 16, 2, false, 4, true>(a, s);
+  } else {
+    if (a.M <= 32) {
+      if (wide) return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
+      return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
+    }
+    // 33 and more rows: 64-row tiles (grid.y covers any M)
+    if (wide) return launch_plain_t<GS, 4, 4, 4, 1, false>(a, s);
+    return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
   }
-  // 33 and more rows: 64-row tiles (grid.y covers any M)
-  if (wide) return launch_plain_t<GS, 4, 4, 4, 1, false>(a, s);
-  return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
 }
 
 }  // namespace

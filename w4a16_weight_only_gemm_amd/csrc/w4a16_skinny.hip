@@ -911,14 +911,15 @@ hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan
 }
 
 // w4a16_gemm's M-dispatch. Measured on the decode layer set as four plain
-// calls: the small-M kernel (w4a16_plain.hip) takes 46.5 us at M = 1, 75 at 16,
-// 188 at 64, 341 at 128 and 406 at 192, the one-workgroup-per-tile MFMA engine
-// 470 to 485 us up to M = 128 and 556 at 192 and 256 (where the two tie).
+// calls: the small-M kernel (w4a16_plain.hip) takes 47 us at M = 1, 75 at 16,
+// 152 at 64, 240 at 128, 313 at 192, 403 at 256, 502 at 320 and 583 at 384;
+// the one-workgroup-per-tile MFMA engine 467 to 483 us up to M = 128 and 555 to
+// 559 us from 160 to 384.
 int choose_path(int M, int N, int K, int group) {
   (void)N;
   (void)K;
   (void)group;
-  return M <= 192 ? W4A16_PATH_SKINNY : W4A16_PATH_LARGE;
+  return M <= 320 ? W4A16_PATH_SKINNY : W4A16_PATH_LARGE;
 }
 
 }  // namespace w4a16_internal
