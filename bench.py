@@ -128,11 +128,19 @@ def fit_step_model(rows, step_s, W: float, per_row_bytes: float, flops_per_row: 
     return eta, P, bend
 
 
+# The sources the streaming kernel (streamk_kernel, the one whose traffic is
+# measured) is compiled from: its own file, the shared device helpers and the
+# launch and boundary headers. A change to any of them voids stored counters.
+STREAMK_SOURCES = ("w4a16_weight_only_gemm_amd/csrc/w4a16_skinny.hip",
+                   "w4a16_weight_only_gemm_amd/csrc/w4a16_device.h",
+                   "w4a16_weight_only_gemm_amd/csrc/w4a16_launch.h",
+                   "include/w4a16.h")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "w4a16_weight_only_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in STREAMK_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 

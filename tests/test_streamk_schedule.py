@@ -27,7 +27,12 @@ import pytest
 
 WAVES = 8
 MAX_WAVES = 8192
-LDS_BUDGET = 64 * 1024
+LDS_BUDGET = 78 * 1024
+
+
+def sum_stride(M):
+    """Floats per group of staged row sums: 16 rows, or 8 with at most 4 rows."""
+    return 8 if M <= 4 else 16
 
 
 def first_unit(w, U, NW):
@@ -83,8 +88,8 @@ def plan(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
         wu0, wu1 = units * wb0 // nw, units * wb1 // nw
         if wu1 <= wu0:
             continue
-        # activation rows and their group sums (G x 16 fp32)
-        e = sum(Mr * (p["K"] + 8) * 2 + p["G"] * 64 for p in table
+        # activation rows and their group sums (G x sum_stride fp32)
+        e = sum(Mr * (p["K"] + 8) * 2 + p["G"] * sum_stride(M) * 4 for p in table
                 if p["u_begin"] + p["NSB"] * p["G"] > wu0 and p["u_begin"] < wu1)
         need = max(need, e)
     x_bytes = (need + 15) // 16 * 16
@@ -152,7 +157,7 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                 xoff = off // 2
                 for i in touched:
                     xs_base[i] = xoff
-                    xoff += table[i]["G"] * 16
+                    xoff += table[i]["G"] * sum_stride(M)
                 assert xoff * 4 <= x_bytes
         lds_parts = {}                      # (local wave, slot) -> super-block
         for wave in range(WAVES):
@@ -177,8 +182,9 @@ def simulate(problems, M, group, cus=256, wg_per_cu=2, nbw=None):
                     assert tile * 16 + 15 < pr["NCB"] * 16 * pr["G"]
                 row = min(15, M - 1)
                 assert row * pr["K"] + g * group + 3 * wpl * 8 + 8 * (wpl - 1) + 7 < M * pr["K"]
-                if xlds:  # this unit's group sums (rows 4 * lg .. + 3, lg <= 3)
-                    assert (xs_base[p] + g * 16 + 12 + 4) * 4 <= part_off
+                if xlds:  # this unit's group sums (4 floats at 4 * lg, lg <= 3, or <= 1 when compact)
+                    ss = sum_stride(M)
+                    assert (xs_base[p] + g * ss + (12 if ss == 16 else 4) + 4) * 4 <= part_off
                 if seg_g0 is None:
                     seg_g0 = g
                 if g == pr["G"] - 1 or u == u1 - 1:

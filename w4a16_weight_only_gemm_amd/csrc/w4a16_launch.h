@@ -26,7 +26,12 @@ bool large_supported(int group);
 constexpr int kMaxProblems = 8;
 constexpr int kStreamKWaves = 8;                // waves per workgroup
 constexpr int kStreamKMaxWaves = 8192;          // grid never exceeds this many waves
-constexpr size_t kStreamKLdsBudget = 64 * 1024;  // staged activations per workgroup
+// Staged activations, their row sums and the waves' parts per workgroup: two
+// workgroups fit in a compute unit's 160 KB.
+constexpr size_t kStreamKLdsBudget = 78 * 1024;
+// Floats per group in the staged row sums: rows 0..15, or with at most 4 rows
+// rows 0..3 and then the last row four times (the padding rows' value).
+__host__ __device__ constexpr int streamk_sum_stride(int M) { return M <= 4 ? 8 : 16; }
 
 struct StreamKProblem {
   const uint16_t* x;        // bf16 [M][K]

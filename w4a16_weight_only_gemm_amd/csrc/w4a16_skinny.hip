@@ -432,9 +432,12 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
   // problem (at most kMaxProblems problems per workgroup, checked on the host).
   int plo = 0;
   // With XLDS, LDS also holds per problem and group the bias term -24 *
-  // (sum of the group's activations) of each row, as [G][16 rows] fp32 (rows
-  // past Mr repeat row Mr - 1), after the activation rows: an MFMA chain
-  // started from it sums a * q with the codes' bias already removed.
+  // (sum of the group's activations) of each row, as [G][SS] fp32 after the
+  // activation rows: an MFMA chain started from it sums a * q with the codes'
+  // bias already removed. SS = 16 holds rows 0..15 (rows past Mr repeat row
+  // Mr - 1); with at most 4 rows SS = 8: rows 0..3, then row Mr - 1 four
+  // times, which lanes of rows 4..15 (all padding) read.
+  const int SS = streamk_sum_stride(M);
   int xs_base[kMaxProblems];
 #pragma unroll
   for (int i = 0; i < kMaxProblems; ++i) xs_base[i] = 0;
@@ -459,7 +462,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
       for (int j = 0; j < kMaxProblems; ++j) {
         if (plo + j <= phi) {
           xs_base[j] = xoff;
-          xoff += prob_at(plo + j).G * 16;
+          xoff += prob_at(plo + j).G * SS;
         }
       }
 #pragma unroll
@@ -479,10 +482,10 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
             *reinterpret_cast<u32x4*>(xlds + (lds_base[i] + row * lds_stride[i] + 8 * c8) / 2) = d;
             const float bsum = group_lane_sum<LPG>(neg_bias_sum8(d));  // the group's first lane stores
             if ((c8 % LPG) == 0) {
-              float* dst = xsum + xs_base[i] + (c8 / LPG) * 16;
+              float* dst = xsum + xs_base[i] + (c8 / LPG) * SS;
               dst[row] = bsum;
               if (row == Mr - 1)
-                for (int m = Mr; m < 16; ++m) dst[m] = bsum;
+                for (int m = Mr; m < SS; ++m) dst[m] = bsum;
             }
           }
         }
@@ -511,7 +514,8 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
       const int G = run.G;
       const int rp = run.p - plo;  // slot of the problem in the LDS offset arrays (with XLDS)
       const int xbase = XLDS ? (lds_base[rp] + min(c16, M - 1) * lds_stride[rp] + lg * WPL * 8) / 2 : 0;
-      const float* const xs = xsum + xs_base[rp] + 4 * lg;  // with XLDS: this lane's rows of group 0
+      // with XLDS: this lane's rows of group 0
+      const float* const xs = xsum + xs_base[rp] + 4 * (SS == 16 ? lg : min(lg, 1));
       int sb = uniform(run.v0 / G);
       int g = uniform(run.v0 - sb * G);
       int seg_g0 = g;  // first group of the current super-block segment
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES, (XLDS && GS <= 128) ? 4 : 1) void strea
             }
             if constexpr (NBW == 1) {
               // from -24 * (row sums): sum of a * q (exact products)
-              f32x4 acc = *reinterpret_cast<const f32x4*>(xs + g * 16);
+              f32x4 acc = *reinterpret_cast<const f32x4*>(xs + g * SS);
 #pragma unroll
               for (int t = 0; t < WPL; ++t) acc = mfma16(a[t], dequant_biased(buf[i].w[0].w[t]), acc);
               const float sc =
@@ -775,7 +779,8 @@ void streamk_lds_need(const StreamKProblem* probs, int count, int M, long long u
     long long bytes = 0;
     int n = 0;
     for (int i = p; i < count && probs[i].u_begin < wu1; ++i) {
-      bytes += static_cast<long long>(Mr) * (probs[i].K + 8) * 2 + static_cast<long long>(probs[i].G) * 16 * 4;
+      bytes += static_cast<long long>(Mr) * (probs[i].K + 8) * 2 +
+               static_cast<long long>(probs[i].G) * streamk_sum_stride(M) * 4;
       ++n;
     }
     if (bytes > need) need = bytes;
