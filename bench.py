@@ -163,7 +163,7 @@ class LayerStore:
     """Packed weights and scales of L layer sets, resident on the device (packing
     runs in host threads: the generator and the packer release the GIL)."""
 
-    def __init__(self, layers: int):
+    def __init__(self, layers: int, projs=None, proj_base: int = 0):
         from concurrent.futures import ThreadPoolExecutor
 
         import numpy as np
@@ -171,13 +171,17 @@ class LayerStore:
 
         import synth
         import w4a16_weight_only_gemm_amd as w4
-        self.projs = synth.LAYER_PROJECTIONS
+        # the full layer's projections, or another set (the tensor-parallel
+        # shard) whose tensors take projection slots proj_base + index
+        self.projs = projs or synth.LAYER_PROJECTIONS
+        self.proj_base = proj_base
 
         def pack(job):
             layer, pi = job
             p = self.projs[pi]
-            q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, pi), p.N, p.K, threads=2)
-            s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, pi), p.N, p.K // GROUP,
+            slot = proj_base + pi
+            q = synth.gen_q(synth.tensor_id(synth.KIND_Q, layer, slot), p.N, p.K, threads=2)
+            s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, layer, slot), p.N, p.K // GROUP,
                                  threads=2)
             return w4.w4a16_pack(q, s, GROUP)
 
@@ -276,7 +280,7 @@ class Workload:
         for i in range(xsets):
             xs, ys = [], []
             for pi, p in enumerate(store.projs):
-                xb = synth.gen_x(synth.tensor_id(synth.KIND_X, i, pi, M), M, p.K)
+                xb = synth.gen_x(synth.tensor_id(synth.KIND_X, i, store.proj_base + pi, M), M, p.K)
                 xs.append(torch.from_numpy(xb.view(np.int16)).to("cuda").view(torch.bfloat16))
                 ys.append(torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda"))
             self.x.append(xs)
@@ -434,9 +438,11 @@ def check_parity(wl: Workload, kind: str, cols: int = 64):
         rng = np.random.default_rng(pi)
         c = np.sort(rng.choice(p.N, cols, replace=False))
         rows = min(wl.M, 64)
-        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, pi), p.N, p.K)[c]
-        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, pi), p.N, p.K // GROUP)[c]
-        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 0, pi, wl.M), wl.M, p.K, rows=(0, rows))
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, wl.store.proj_base + pi), p.N, p.K)[c]
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, wl.store.proj_base + pi), p.N,
+                             p.K // GROUP)[c]
+        x = synth.gen_x(synth.tensor_id(synth.KIND_X, 0, wl.store.proj_base + pi, wl.M), wl.M, p.K,
+                        rows=(0, rows))
         ref = oracle.gemm(x, q, s, GROUP, threads=synth.default_threads())
         y = wl.y[0][pi][:rows].view(torch.int16).cpu().numpy().view(np.uint16)[:, c]
         yv = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -505,8 +511,9 @@ def time_w4a8(wl: Workload, steps: int, warmup: int):
         rng = np.random.default_rng(10 + pi)
         c = np.sort(rng.choice(p.N, 64, replace=False))
         rows = min(M, 16)
-        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, pi), p.N, p.K)[c]
-        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, pi), p.N, p.K // GROUP)[c]
+        q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 0, wl.store.proj_base + pi), p.N, p.K)[c]
+        s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 0, wl.store.proj_base + pi), p.N,
+                             p.K // GROUP)[c]
         x = synth.gen_x(synth.tensor_id(synth.KIND_X, 0, pi, M), M, p.K, rows=(0, rows))
         xq, sx = oracle.quantize_rows(x)
         ref = oracle.gemm_w4a8(xq, sx, q, s, GROUP)
@@ -562,7 +569,7 @@ def tiny_latency(reps: int = 200):
 
 
 def stack_steps(store: LayerStore, rows, sampler=None, passes: int = 10, xsets: int = 8,
-                plain: bool = False):
+                plain: bool = False, label: str = "stack"):
     """The full-step workload (every layer of the store, four projections each)
     at each M in `rows`: one planned launch over all of the step's GEMMs, one
     grouped launch per layer and (with plain) four w4a16_gemm calls per layer,
@@ -588,7 +595,8 @@ def stack_steps(store: LayerStore, rows, sampler=None, passes: int = 10, xsets: 
     for M in rows:
         t_begin = time.time()
         X = min(xsets, L)
-        xs = [[torch.from_numpy(synth.gen_x(synth.tensor_id(synth.KIND_X, i, pi, M), M, p.K)
+        xs = [[torch.from_numpy(synth.gen_x(synth.tensor_id(synth.KIND_X, i, store.proj_base + pi, M),
+                                            M, p.K)
                                 .view(np.int16)).to("cuda").view(torch.bfloat16)
                for pi, p in enumerate(projs)] for i in range(X)]
         ys = [[torch.empty((M, p.N), dtype=torch.bfloat16, device="cuda") for p in projs]
@@ -644,7 +652,7 @@ def stack_steps(store: LayerStore, rows, sampler=None, passes: int = 10, xsets: 
             row["clock"] = sampler.summary(t_begin, time.time())
         out.append(row)
         pl = row["planned"]
-        print(f"# stack M={M}: planned {pl['ms_per_step_median']:.3f} ms/step ({pl['tbps']:.2f} TB/s,"
+        print(f"# {label} M={M}: planned {pl['ms_per_step_median']:.3f} ms/step ({pl['tbps']:.2f} TB/s,"
               f" {pl['tflops']:.1f} TFLOP/s); grouped per layer "
               f"{row['grouped_per_layer']['ms_per_step_median']:.3f} ms", file=sys.stderr, flush=True)
         del xs, ys, pws, gws, plan_dev, arrs
@@ -873,6 +881,8 @@ def main(argv=None):
     ap.add_argument("--m-list", default="1,16,64,1024")
     ap.add_argument("--stack-m-list", default="1,16,64,1024",
                     help="row counts of the full-step (all layers) planned launch; empty: none")
+    ap.add_argument("--shard-m-list", default="1,16,64",
+                    help="row counts of the tensor-parallel (8-way) shard step; empty to skip")
     ap.add_argument("--w4a8-m-list", default="256,1024",
                     help="row counts of the W4A8 batched step (empty: none)")
     ap.add_argument("--no-smi", action="store_true", help="do not sample clocks with amd-smi")
@@ -1004,6 +1014,21 @@ def main(argv=None):
                         f"GEMMs ({st['W'] / 1e9:.3f} GB of packed weights and scales): one "
                         f"w4a16_gemm_planned launch per step, next to one grouped launch per layer",
             "rows": st["rows"]}})
+    shard_rows = [int(v) for v in args.shard_m_list.split(",") if v]
+    if shard_rows:
+        import synth
+        sst = LayerStore(args.layers, synth.TP8_SHARD_PROJECTIONS, synth.SHARD_PROJ_BASE)
+        sh = stack_steps(sst, shard_rows, sampler=sampler, plain=True, label="tp8 shard")
+        extra.append({"tp8_shard": {
+            "workload": f"one GPU's share of the full step under 8-way tensor parallelism: all "
+                        f"{args.layers} layers x (qkv 5120x896, o 768x5120, gate_up 5120x4352, down "
+                        f"2176x5120; qkv and gate_up split by columns, o and down by K) "
+                        f"({sh['W'] / 1e9:.3f} GB): one planned launch per step, one grouped "
+                        f"launch per layer, or four w4a16_gemm calls per layer (the all-reduce "
+                        f"of o and down not included)",
+            "rows": sh["rows"]}})
+        del sst
+        torch.cuda.empty_cache()
     for M in [int(v) for v in args.w4a8_m_list.split(",") if v]:
         wl8 = Workload(store, M)
         ms8, dom8, par8 = time_w4a8(wl8, args.steps, min(args.warmup, 1000))

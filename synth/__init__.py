@@ -150,6 +150,18 @@ LAYER_PROJECTIONS = (
 GROUP = 128
 N_LAYERS = 64
 
+# One GPU's share of the same layer under 8-way tensor parallelism: qkv and
+# gate_up split by columns (N / 8), o and down by rows of K (K / 8; each GPU
+# then holds a partial y that an all-reduce sums). Their tensors take
+# projection slots SHARD_PROJ_BASE + index, apart from the full layer's.
+TP8_SHARD_PROJECTIONS = (
+    Projection("qkv", 5120, 896),
+    Projection("o", 768, 5120),
+    Projection("gate_up", 5120, 4352),
+    Projection("down", 2176, 5120),
+)
+SHARD_PROJ_BASE = 8
+
 # The small GEMV case the oracle finishes instantly.
 TINY = dict(M=1, K=256, N=512, group=64)
 TINY_PROJ = 15  # projection slot reserved for the tiny case's tensor ids
