@@ -95,10 +95,12 @@ def _layer_problems(M, layer=0):
 
 
 @pytest.mark.parametrize("layer", [0, 63])
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
 def test_layer_set_grouped_full(M, layer):
     """The four projections of a layer in one launch, every output checked
-    (layers 0 and 63: the first and last of the 64-layer stack)."""
+    (layers 0 and 63: the first and last of the 64-layer stack). The launch
+    forms: rows staged in LDS (M = 1, 2), six-column-block units with each
+    wave reading its activation fragments (M = 3, 4, 16)."""
     import torch
     import w4a16_weight_only_gemm_amd as w4
     probs, data = _layer_problems(M, layer)
