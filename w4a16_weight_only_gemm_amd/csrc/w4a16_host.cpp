@@ -97,10 +97,10 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
       for (int slice = 0; slice < 4; ++slice) {
         for (int col = 0; col < 16; ++col) {
           const size_t n = b * 16 + col;
-          const int8_t* codes = q + n * K + static_cast<size_t>(t) * group + slice * wpl * 8;
           for (int w = 0; w < wpl; ++w) {
             uint32_t word = 0;
-            if (n < static_cast<size_t>(N)) {
+            if (n < static_cast<size_t>(N)) {  // padding columns of the last block: zero codes
+              const int8_t* codes = q + n * K + static_cast<size_t>(t) * group + slice * wpl * 8;
               // nibble v holds the code of k = 2v, nibble v + 4 that of k = 2v + 1
               for (int v = 3; v >= 0; --v)
                 word = (word << 4) | (static_cast<uint32_t>(codes[8 * w + 2 * v + 1]) & 0xFu);
