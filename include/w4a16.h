@@ -67,8 +67,9 @@ typedef enum {
 /* Kernel paths; W4A16_PATH_AUTO lets the M-dispatch heuristic choose. */
 typedef enum {
   W4A16_PATH_AUTO = 0,
-  W4A16_PATH_SKINNY = 1, /* small M: workgroups of 16-64 rows x 32-64 columns over all of K, waves split K */
-  W4A16_PATH_LARGE = 2   /* large M: LDS-staged activation tiles, bf16 MFMA, per-group fp32 scaling */
+  W4A16_PATH_SKINNY = 1, /* workgroups of 16-64 rows x 32-80 columns over all of K, waves split K */
+  W4A16_PATH_LARGE = 2   /* workgroups of 32-128 rows x 256 columns over all of K, LDS-staged
+                            activation tiles, waves split N */
 } w4a16_path;
 
 /* Bytes of the packed weights, ceil(N/16)*16*K/2, and of the packed scales,
@@ -325,6 +326,14 @@ int w4a8_gemm_grouped(const w4a8_problem* problems, int count, int M, int group,
 /* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
  * host integers), or -1 for an unsupported shape. */
 int w4a16_select_path(int M, int N, int K, int group);
+
+/* The kernel form w4a16_gemm_ex runs for this shape on `path` (the library's
+ * own choice, from time models of its kernels; the pages give none): writes the
+ * workgroup's output tile (*rows x *cols) and its waves, and returns the path
+ * that runs (W4A16_PATH_AUTO resolved), or -1 (nothing written) for an
+ * unsupported shape, a bad path or a null output pointer. Host arithmetic only,
+ * for tests and profiles. */
+int w4a16_select_form(int M, int N, int K, int group, int path, int* rows, int* cols, int* waves);
 
 /* Static text for a status code; never NULL. */
 const char* w4a16_status_string(int status);

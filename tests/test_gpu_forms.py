@@ -1,0 +1,117 @@
+"""GPU parity of every kernel form w4a16_gemm can run, through the C ABI.
+
+w4a16_gemm picks a form per shape from time models of its kernels (the
+library's own choice; w4a16_select_form reports it): up to 16 rows the small-M
+forms of the plain kernel; from 17 rows either a plain-kernel form (16, 32 or
+64 rows by 32 to 80 columns per workgroup; at group 128 the activation
+fragments pass through a wave-private LDS area) or the whole-K tile engine
+(32, 64 or 128 rows by 256 columns; at 32 and 64 rows loads run three
+k-tiles ahead). Each case below is a shape for which the automatic choice is
+one given form (asserted first, on the host), ragged in M and N, with several
+workgroups along N; the result is checked against the oracle,
+|y - y_ref| <= 1e-2 (1 + |y_ref|): every output, or, above 24 rows where the
+oracle would take long, 24 sampled rows (the first, the last, 22 at random). Forced paths cover
+the tile engine at 1 and 16 rows and the plain kernel at several hundred."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import Problem, tolerance_ratio
+
+pytestmark = pytest.mark.gpu
+
+AUTO, SKINNY, LARGE = 0, 1, 2
+
+# ((M, N, K, group), expected (path, rows, cols, waves))
+FORM_CASES = [
+    ((17, 100, 4096, 128), (1, 16, 32, 8)),
+    ((17, 5000, 8192, 128), (1, 16, 64, 8)),
+    ((17, 9000, 8192, 128), (1, 16, 80, 8)),
+    ((17, 100, 256, 128), (1, 32, 32, 16)),
+    ((17, 9000, 256, 128), (1, 32, 48, 16)),
+    ((37, 7001, 256, 128), (1, 32, 64, 16)),
+    ((17, 17000, 1024, 128), (1, 32, 80, 8)),
+    ((37, 9000, 256, 128), (1, 64, 64, 16)),
+    ((333, 520, 256, 128), (2, 32, 256, 8)),
+    ((37, 35001, 256, 128), (2, 64, 256, 8)),
+    ((517, 12001, 256, 128), (2, 128, 256, 8)),
+    ((17, 100, 512, 64), (1, 32, 32, 4)),
+    ((17, 17000, 2048, 64), (1, 32, 64, 4)),
+    ((37, 100, 512, 64), (1, 64, 32, 4)),
+    ((17, 520, 256, 64), (2, 32, 256, 8)),
+    ((37, 35001, 256, 64), (2, 64, 256, 8)),
+    ((517, 12001, 256, 64), (2, 128, 256, 8)),
+    ((17, 100, 512, 32), (1, 32, 32, 4)),
+    ((37, 100, 512, 32), (1, 64, 32, 4)),
+    ((17, 520, 256, 32), (2, 32, 256, 8)),
+    ((37, 35001, 256, 32), (2, 64, 256, 8)),
+    ((17, 17000, 256, 256), (1, 32, 64, 4)),
+    ((37, 100, 256, 256), (1, 64, 32, 4)),
+    ((37, 17000, 256, 256), (1, 64, 64, 4)),
+]
+
+# ((M, N, K, group), forced path, expected form)
+FORCED_CASES = [
+    ((1, 1000, 1024, 128), LARGE, (2, 32, 256, 8)),
+    ((16, 700, 512, 64), LARGE, (2, 32, 256, 8)),
+    ((700, 300, 512, 128), SKINNY, None),
+    ((517, 300, 512, 32), SKINNY, None),
+]
+
+SAMPLE_ABOVE = 2e8  # multiply-adds above which the oracle computes sampled rows only
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    import w4a16_weight_only_gemm_amd  # noqa: F401  (fails loudly if the library is missing)
+    yield
+
+
+def _check(cid, M, N, K, g, path):
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 700 + cid, 0), N, K)
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 700 + cid, 0), N, K // g)
+    x = synth.gen_x(synth.tensor_id(synth.KIND_X, 700 + cid, 0, M), M, K)
+    y = Problem(x, q, s, g).run(path)
+    if M * N * K > SAMPLE_ABOVE and M > 24:
+        rng = np.random.default_rng(cid)
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 22, replace=False)]))
+    else:
+        rows = np.arange(M)
+    ref = oracle.gemm(x[rows], q, s, g, threads=synth.default_threads())
+    r = tolerance_ratio(y[rows], ref)
+    log(f"  {len(rows)} rows checked, tolerance ratio {r:.4f}")
+    assert r <= 1.0
+
+
+@pytest.mark.parametrize("case", list(enumerate(FORM_CASES)),
+                         ids=lambda c: "x".join(map(str, c[1][0])))
+def test_auto_form_parity(case):
+    import w4a16_weight_only_gemm_amd as w4
+    cid, ((M, N, K, g), form) = case
+    got = w4.w4a16_select_form(M, N, K, g)
+    log(f"form case M={M} N={N} K={K} g={g}: form {got}")
+    assert got == form
+    _check(cid, M, N, K, g, AUTO)
+
+
+@pytest.mark.parametrize("case", list(enumerate(FORCED_CASES)),
+                         ids=lambda c: f"{'x'.join(map(str, c[1][0]))}-path{c[1][1]}")
+def test_forced_form_parity(case):
+    import w4a16_weight_only_gemm_amd as w4
+    cid, ((M, N, K, g), path, form) = case
+    got = w4.w4a16_select_form(M, N, K, g, path)
+    log(f"forced case M={M} N={N} K={K} g={g} path={path}: form {got}")
+    assert got[0] == path
+    if form is not None:
+        assert got == form
+    _check(100 + cid, M, N, K, g, path)

@@ -134,13 +134,65 @@ def test_gemm_argument_checks_without_launch():
 
 
 def test_select_path():
-    assert w4.w4a16_select_path(1, 7168, 5120, 128) == w4.W4A16_PATH_SKINNY
-    assert w4.w4a16_select_path(16, 5120, 17408, 128) == w4.W4A16_PATH_SKINNY
-    assert w4.w4a16_select_path(1024, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
-    assert w4.w4a16_select_path(320, 5120, 6144, 128) == w4.W4A16_PATH_SKINNY
-    assert w4.w4a16_select_path(321, 5120, 6144, 128) == w4.W4A16_PATH_LARGE
+    S, L = w4.W4A16_PATH_SKINNY, w4.W4A16_PATH_LARGE
+    assert w4.w4a16_select_path(1, 7168, 5120, 128) == S
+    assert w4.w4a16_select_path(16, 5120, 17408, 128) == S
+    assert w4.w4a16_select_path(16, 34816, 5120, 128) == S          # up to 16 rows: always
+    assert w4.w4a16_select_path(17, 34816, 5120, 128) == L          # 136 column tiles fill the CUs
+    assert w4.w4a16_select_path(64, 34816, 5120, 128) == L
+    assert w4.w4a16_select_path(64, 5120, 17408, 128) == S          # 20 column tiles do not
+    assert w4.w4a16_select_path(192, 5120, 6144, 128) == S
+    assert w4.w4a16_select_path(320, 5120, 6144, 128) == L
+    assert w4.w4a16_select_path(1024, 5120, 6144, 128) == L
+    assert w4.w4a16_select_path(1024, 16, 256, 128) == L            # above 320 rows: always
+    assert w4.w4a16_select_path(64, 34816, 5120, 256) == S          # no tile engine at group 256
     assert w4.w4a16_select_path(1, 512, 256, 48) == -1
     assert w4.w4a16_select_path(-1, 512, 256, 64) == -1
+
+
+# (M, N, K, group) -> (path, rows, cols, waves) that w4a16_gemm runs: the
+# decode layer set (qkv 5120x7168, o 6144x5120, gate_up 5120x34816, down
+# 17408x5120) at the row counts of its sweep, the time models' choices.
+FORMS = {
+    (1, 7168, 5120, 128): (1, 16, 32, 8), (1, 34816, 5120, 128): (1, 16, 32, 4),
+    (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 64, 4),
+    (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (2, 32, 256, 8),
+    (32, 5120, 17408, 128): (1, 16, 64, 8), (64, 7168, 5120, 128): (1, 32, 64, 16),
+    (64, 5120, 6144, 128): (1, 32, 48, 16), (64, 34816, 5120, 128): (2, 64, 256, 8),
+    (64, 5120, 17408, 128): (1, 16, 80, 8), (128, 7168, 5120, 128): (1, 64, 64, 16),
+    (128, 5120, 17408, 128): (1, 32, 80, 8), (256, 7168, 5120, 128): (2, 32, 256, 8),
+    (1024, 34816, 5120, 128): (2, 128, 256, 8), (1024, 5120, 17408, 128): (2, 32, 256, 8),
+    (64, 5120, 17408, 64): (1, 64, 32, 4), (64, 34816, 5120, 64): (2, 64, 256, 8),
+}
+
+
+def test_select_form():
+    for (M, N, K, g), want in FORMS.items():
+        got = w4.w4a16_select_form(M, N, K, g)
+        assert got == want, ((M, N, K, g), got, want)
+        assert got[0] == w4.w4a16_select_path(M, N, K, g)
+    # forced paths: the tile engine at any M (32-row tiles at 1 row), the small-M
+    # kernel at any M; group 256 has no tile engine (w4a16_gemm_ex falls back)
+    assert w4.w4a16_select_form(1, 7168, 5120, 128, w4.W4A16_PATH_LARGE) == (2, 32, 256, 8)
+    assert w4.w4a16_select_form(1024, 5120, 6144, 128, w4.W4A16_PATH_SKINNY)[0] == 1
+    assert w4.w4a16_select_form(1024, 5120, 6144, 256, w4.W4A16_PATH_LARGE)[0] == 1
+    assert w4.w4a16_select_form(1, 512, 256, 48) is None
+    assert w4.w4a16_select_form(1, 512, 256, 64, path=7) is None
+    assert w4.w4a16_select_form(-1, 512, 256, 64) is None
+    r = ctypes.c_int(-5)
+    assert w4._lib.w4a16_select_form(1, 512, 256, 64, 0, None, ctypes.byref(r), ctypes.byref(r)) == -1
+    assert r.value == -5
+
+
+def test_select_form_bounds():
+    """Every chosen form exists and tiles the output: rows 16..128, columns
+    32..256 in 16-column blocks, 4..16 waves, over a grid of shapes."""
+    for M in (1, 2, 3, 5, 9, 16, 17, 31, 33, 64, 65, 100, 200, 320, 321, 700, 5000):
+        for N in (1, 16, 100, 1000, 5000, 34816, 248320):
+            for K, g in ((128, 32), (256, 64), (5120, 128), (17408, 128), (4096, 256)):
+                p, r, c, w = w4.w4a16_select_form(M, N, K, g)
+                assert p in (1, 2) and r in (16, 32, 64, 128) and c % 16 == 0
+                assert 32 <= c <= 256 and w in (4, 8, 16)
 
 
 def test_workspace_sizes():

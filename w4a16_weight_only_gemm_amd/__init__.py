@@ -75,6 +75,7 @@ SIGNATURES = {
     "w4a16_plan_workspace_bytes": (_sz, [_vp]),
     "w4a16_gemm_planned": (_int, [_vp, _vp, _vp, _sz, _vp]),
     "w4a16_select_path": (_int, [_int, _int, _int, _int]),
+    "w4a16_select_form": (_int, [_int, _int, _int, _int, _int, _vp, _vp, _vp]),
     "w4a8_quantize": (_int, [_vp, _vp, _vp, _int, _int, _vp]),
     "w4a8_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
     "w4a8_quantize_grouped": (_int, [_vp, _int, _int, _vp]),
@@ -113,6 +114,15 @@ def w4a16_scales_bytes(N: int, K: int, group: int) -> int:
 
 def w4a16_select_path(M: int, N: int, K: int, group: int) -> int:
     return int(_lib.w4a16_select_path(M, N, K, group))
+
+
+def w4a16_select_form(M: int, N: int, K: int, group: int, path: int = 0):
+    """(path, rows, cols, waves) of the kernel form w4a16_gemm_ex runs for the
+    shape, or None for an unsupported shape."""
+    r, c, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    p = int(_lib.w4a16_select_form(M, N, K, group, path, ctypes.byref(r), ctypes.byref(c),
+                                   ctypes.byref(w)))
+    return None if p < 0 else (p, r.value, c.value, w.value)
 
 
 def w4a16_pack(q: np.ndarray, scales: np.ndarray, group: int):

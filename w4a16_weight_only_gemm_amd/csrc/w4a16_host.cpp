@@ -127,6 +127,13 @@ int w4a16_select_path(int M, int N, int K, int group) {
   return w4a16_internal::choose_path(M, N, K, group);
 }
 
+int w4a16_select_form(int M, int N, int K, int group, int path, int* rows, int* cols, int* waves) {
+  if (M < 0 || N < 1 || K < 1 || !group_supported(group) || K % group != 0) return -1;
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_LARGE) return -1;
+  if (!rows || !cols || !waves) return -1;
+  return w4a16_internal::describe_form(M, N, K, group, path, rows, cols, waves);
+}
+
 int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* y, int M,
                   int N, int K, int group, int path, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return W4A16_ERR_INVALID_ARG;

@@ -28,11 +28,14 @@
 //    running fp32 result, as in the other kernels.
 //
 // Two schedules share that tile engine:
-//  * large_kernel: one workgroup per 128 x 256 tile, the whole K range; needs
-//    no workspace. Workgroups are numbered so that the 8 XCDs (which take
-//    workgroups round robin) each own a contiguous range of tiles, row tiles
-//    fastest: the row tiles that share a column tile's weights run together
-//    on one XCD and find those weights in its L2.
+//  * tile_kernel: one workgroup per 32, 64 or 128 x 256 tile, the whole K
+//    range; needs no workspace. The tile height is the one a time model of
+//    the three forms puts first for the shape (tile_estimate_us); at 32 and
+//    64 rows the loads run three k-tiles ahead. Workgroups are numbered so
+//    that the 8 XCDs (which take workgroups round robin) each own a
+//    contiguous range of tiles, row tiles fastest: the row tiles that share a
+//    column tile's weights run together on one XCD and find those weights in
+//    its L2.
 //  * large_streamk_kernel: a persistent grid splits the (problem, tile,
 //    k-tile) iterations of up to 8 problems evenly, so the machine stays full
 //    whatever the tile count (at M = 128 one layer has only about 200 tiles
@@ -285,6 +288,44 @@ struct TileEngine {
     }
   }
 
+  // k-tiles [k0, k1) with the loads of k-tile t + D issued before k-tile t
+  // computes: D register sets of activation pieces and D + 1 of weights (the
+  // LDS double buffer as in kloop). For workgroups that each own a whole K
+  // range at tile counts near the number of compute units, where one
+  // workgroup's k-tiles follow each other on load latency rather than on
+  // arithmetic. The step is unrolled over D (D + 1) k-tiles so that every
+  // register set has a fixed name (an indexed copy would wait for its loads).
+  template <int D>
+  __device__ __forceinline__ void kloop_deep(Acc<MB>& acc, int k0, int k1) const {
+    constexpr int PER = D * (D + 1);  // a multiple of D, D + 1 and 2
+    StageRegs<GS, MB> sr[D];
+    BRegs<GS> b[D + 1];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int t = k0 + j < k1 ? k0 + j : k1 - 1;  // past the end: reload (unused)
+      stage_load(sr[j], t);
+      load_b(b[j], t);
+    }
+    stage_store(sr[0], 0);
+    lds_barrier();
+    for (int t0 = k0; t0 < k1; t0 += PER) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        // k-tile t = t0 + j: its weights are b[j % (D + 1)], its activations
+        // sit in LDS buffer j & 1; sr[j % D] and b[(j + D) % (D + 1)] are free
+        const int t = t0 + j;
+        if (t >= k1) break;
+        const int tl = t + D < k1 ? t + D : k1 - 1;
+        stage_load(sr[j % D], tl);
+        load_b(b[(j + D) % (D + 1)], tl);
+        __builtin_amdgcn_sched_barrier(0);  // issue the loads before the math
+        compute(acc, b[j % (D + 1)], t, j & 1);
+        stage_store(sr[(j + 1) % D], (j + 1) & 1);
+        lds_barrier();
+      }
+    }
+  }
+
   // bf16 (RNE) stores of the rows and columns that exist.
   __device__ __forceinline__ void store(const Acc<MB>& acc, uint16_t* y) const {
     gptr<uint16_t> yg = to_global(y);
@@ -307,9 +348,10 @@ struct TileEngine {
 
 // =================================================== one workgroup per tile
 
-template <int GS>
-__global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT, int NT) {
-  constexpr int MB = 8;
+// MB x 16 rows by 256 columns per workgroup over the whole K range, loads
+// issued D k-tiles ahead (D = 1: kloop).
+template <int GS, int MB, int D>
+__global__ __launch_bounds__(kLgThreads, 1) void tile_kernel(GemmArgs a, int MT, int NT) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lg_lds[];
   const int tile = xcd_grouped(blockIdx.x, MT * NT);
   const int mt = tile % MT, nt = tile / MT;
@@ -318,7 +360,10 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_kernel(GemmArgs a, int MT
   Acc<MB> acc;
   zero(acc);
   const int kt = (e.G + LgCfg<GS, MB>::T - 1) / LgCfg<GS, MB>::T;
-  e.kloop(acc, 0, kt);
+  if constexpr (D == 1)
+    e.kloop(acc, 0, kt);
+  else
+    e.template kloop_deep<D>(acc, 0, kt);
   e.store(acc, a.y);
 }
 
@@ -511,13 +556,13 @@ __global__ __launch_bounds__(kLgThreads, 1) void large_streamk_kernel(const Larg
 
 // ================================================================ launchers
 
-template <int GS>
-hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
-  constexpr int MB = 8;
+template <int GS, int MB, int D>
+hipError_t launch_tile_t(const GemmArgs& a, hipStream_t stream) {
+  using C = LgCfg<GS, MB>;
   const int NCB = (a.N + 15) / 16;
   const int NT = (NCB + kLgBlocks - 1) / kLgBlocks;
-  const void* fn = reinterpret_cast<const void*>(&large_kernel<GS>);
-  const size_t lds = LgCfg<GS, MB>::Lds;
+  const void* fn = reinterpret_cast<const void*>(&tile_kernel<GS, MB, D>);
+  const size_t lds = C::Lds;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
@@ -525,14 +570,14 @@ hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
   // of x (and the packed weights must stay below 4 GB, checked by the caller).
   const long long row_bytes = 2LL * a.K;
   long long rows_per_launch = (0xFFFFFFFFLL - 16) / row_bytes;
-  rows_per_launch -= rows_per_launch % LgCfg<GS, MB>::Rows;
-  if (rows_per_launch < LgCfg<GS, MB>::Rows) return hipErrorInvalidValue;
+  rows_per_launch -= rows_per_launch % C::Rows;
+  if (rows_per_launch < C::Rows) return hipErrorInvalidValue;
   for (long long r0 = 0; r0 < a.M; r0 += rows_per_launch) {
     GemmArgs part = a;
     part.M = static_cast<int>(a.M - r0 < rows_per_launch ? a.M - r0 : rows_per_launch);
     part.x = a.x + r0 * a.K;
     part.y = a.y + r0 * a.N;
-    int MT = (part.M + LgCfg<GS, MB>::Rows - 1) / LgCfg<GS, MB>::Rows;
+    int MT = (part.M + C::Rows - 1) / C::Rows;
     const long long total = static_cast<long long>(MT) * NT;
     if (total < 1 || total > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     int ntc = NT;
@@ -542,6 +587,18 @@ hipError_t launch_large_t(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// 32- and 64-row tiles keep loads three k-tiles ahead (at those tile counts a
+// workgroup's k-tiles wait on load latency); 128-row tiles have the
+// arithmetic to cover one.
+template <int GS>
+hipError_t launch_tile_g(const GemmArgs& a, int rows, hipStream_t stream) {
+  switch (rows) {
+    case 32: return launch_tile_t<GS, 2, 3>(a, stream);
+    case 64: return launch_tile_t<GS, 4, 3>(a, stream);
+    default: return launch_tile_t<GS, 8, 1>(a, stream);
+  }
 }
 
 // Units and tiles of the problems for tiles of `rows` rows (group GS): fills
@@ -602,15 +659,44 @@ hipError_t launch_large_sk_g(LargeSKArgs& sk, int group, hipStream_t stream) {
 
 bool large_supported(int group) { return group == 32 || group == 64 || group == 128; }
 
+// Whole-K tile forms, per k-tile of 128 (microseconds, one MI355X, decode
+// layer set and its tensor-parallel shard at M = 17 to 512): one workgroup of
+// 32, 64 or 128 rows per compute unit takes 0.75, 1.08 or 1.9; a second round
+// of workgroups costs as much again, except at 32 rows, where two workgroups
+// share a compute unit and n rounds cost about 0.8 n.
+double tile_estimate_us(int M, int N, int K, int group, int* rows_out) {
+  const long long NT = ((static_cast<long long>(N) + 15) / 16 + kLgBlocks - 1) / kLgBlocks;
+  const long long G = K / group;
+  const long long T = kLgKT / group;
+  const double kt = static_cast<double>((G + T - 1) / T);
+  const int rows_opt[3] = {32, 64, 128};
+  const double per_ktile[3] = {0.75, 1.08, 1.9};
+  double best = 0.0;
+  int best_rows = 128;
+  for (int i = 0; i < 3; ++i) {
+    const long long tiles = (static_cast<long long>(M) + rows_opt[i] - 1) / rows_opt[i] * NT;
+    const long long n = (tiles + kModelCUs - 1) / kModelCUs;
+    const double rounds = i == 0 && n > 1 ? 0.8 * static_cast<double>(n) : static_cast<double>(n);
+    const double est = kt * per_ktile[i] * rounds + 1.0;
+    if (i == 0 || est < best) {
+      best = est;
+      best_rows = rows_opt[i];
+    }
+  }
+  if (rows_out) *rows_out = best_rows;
+  return best;
+}
+
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream) {
   // packed weights and scales are addressed with 32-bit buffer offsets
   const long long qbytes = static_cast<long long>((a.N + 15) / 16) * 16 * a.K / 2;
-  if (qbytes > 0xFFFFFFF0LL) return launch_skinny(a, stream);
+  if (qbytes > 0xFFFFFFF0LL || !large_supported(a.group)) return launch_skinny(a, stream);
+  int rows = 128;
+  tile_estimate_us(a.M, a.N, a.K, a.group, &rows);
   switch (a.group) {
-    case 32: return launch_large_t<32>(a, stream);
-    case 64: return launch_large_t<64>(a, stream);
-    case 128: return launch_large_t<128>(a, stream);
-    default: return launch_skinny(a, stream);  // group 256: split-K kernel
+    case 32: return launch_tile_g<32>(a, rows, stream);
+    case 64: return launch_tile_g<64>(a, rows, stream);
+    default: return launch_tile_g<128>(a, rows, stream);
   }
 }
 

@@ -22,6 +22,20 @@ hipError_t launch_large(const GemmArgs& a, hipStream_t stream);
 // Group sizes the tiled large-M kernel handles (others fall back to split-K).
 bool large_supported(int group);
 
+// ---- w4a16_gemm's choice of kernel form (host arithmetic only) ----
+// Compute units the time models below assume (one MI355X); the choice is a
+// pure function of the shape, so it is the same on every device and call.
+constexpr int kModelCUs = 256;
+// Modelled time (microseconds) of the best whole-K tile form (tile_kernel) for
+// the shape, and its tile height (32, 64 or 128 rows) in *rows_out.
+double tile_estimate_us(int M, int N, int K, int group, int* rows_out);
+// plain_kernel forms (w4a16_plain.hip); the form launch_skinny runs for a
+// shape, its workgroup geometry, and the modelled time of the best form at
+// more than 16 rows.
+int plain_form(int M, int N, int K, int group);
+void plain_form_shape(int form, int* rows, int* cols, int* waves);
+double plain_estimate_us(int M, int N, int K, int group);
+
 // ---- stream-K (persistent, several problems per launch, M <= 16) ----
 constexpr int kMaxProblems = 8;
 constexpr int kStreamKWaves = 8;                // waves per workgroup
@@ -187,5 +201,8 @@ hipError_t launch_read_probe(const void* buf, long long words, uint32_t* sink, h
 
 // M-dispatch: W4A16_PATH_SKINNY or W4A16_PATH_LARGE for a supported shape.
 int choose_path(int M, int N, int K, int group);
+// The workgroup tile (rows x columns, waves) that w4a16_gemm_ex runs for a
+// supported shape on `path` (W4A16_PATH_AUTO resolved first); returns the path.
+int describe_form(int M, int N, int K, int group, int path, int* rows, int* cols, int* waves);
 
 }  // namespace w4a16_internal

@@ -21,8 +21,9 @@
 //    applies the group's scale.
 //
 // The host picks (MB, NB, waves, groups in flight, staging) from M, N and K
-// (launch_plain_g) so that the grid has enough workgroups for the compute
-// units and each wave keeps enough bytes in flight.
+// (plain_form) so that the grid has enough workgroups for the compute units,
+// no compute unit holds more than it must, and each wave keeps enough bytes
+// in flight.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -327,56 +328,147 @@ hipError_t launch_plain_t(const GemmArgs& a, hipStream_t stream) {
   return hipLaunchKernel(fn, grid, dim3(64 * WAVES), kargs, lds, stream);
 }
 
-// Shapes measured on the decode layer set (qkv 5120x7168, o 6144x5120, gate_up
-// 5120x34816, down 17408x5120) at group 128, as four separate calls, over
-// every (row blocks, column blocks, waves, groups in flight, staging) form
-// that fits: wide N (gate_up, 2176 column blocks) prefers 4-wave workgroups
-// with 2 to 4 column blocks each; deep K at one or two rows prefers 16 waves
-// and staged rows; the rest 8 waves below 9 rows, 4 waves above, 2 column
-// blocks. Group 256 (twice the registers per group) keeps fewer groups in
-// flight.
+// The forms w4a16_gemm runs, by index (plain_form picks one per shape).
+enum PlainForm : int {
+  // up to 16 rows (one row block): measured on the decode layer set (qkv
+  // 5120x7168, o 6144x5120, gate_up 5120x34816, down 17408x5120, group 128)
+  // over every (column blocks, waves, groups in flight, staging) form that
+  // fits: wide N (2176 column blocks) prefers 4-wave workgroups with 2 to 4
+  // column blocks; deep K at one or two rows 16 waves and staged rows; the
+  // rest 8 waves below 9 rows, 4 waves above. Group 256 (twice the registers
+  // per group) keeps fewer groups in flight.
+  kWideStaged,   // 1 x 2 blocks, 4 waves, rows in LDS
+  kWide2,        // 1 x 2, 4 waves
+  kWide4,        // 1 x 4, 4 waves
+  kDeepStaged,   // 1 x 2, 16 waves, rows in LDS
+  kSmall8,       // 1 x 2, 8 waves
+  // more rows at group 128, activation fragments through a wave-private LDS
+  // area (XS); MB x NB blocks, waves (along rows x along K)
+  kXs1x2,        // 1 x 2, 8 waves (1 x 8)
+  kXs1x4,        // 1 x 4, 8 waves (1 x 8)
+  kXs1x5,        // 1 x 5, 8 waves (1 x 8)
+  kXs2x2,        // 2 x 2, 16 waves (2 x 8)
+  kXs2x3,        // 2 x 3, 16 waves (2 x 8)
+  kXs2x4,        // 2 x 4, 16 waves (2 x 8)
+  kXs2x5,        // 2 x 5, 8 waves (2 x 4)
+  kXs4x4,        // 4 x 4, 16 waves (4 x 4)
+  // more rows at groups 32, 64 and 256, fragments loaded in operand order
+  kOp2x2,        // 2 x 2, 4 waves
+  kOp2x4,        // 2 x 4, 4 waves
+  kOp4x2,        // 4 x 2, 4 waves
+  kOp4x4,        // 4 x 4, 4 waves
+  kPlainForms
+};
+
+struct PlainFormInfo {
+  int mb, nb, waves;
+};
+constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
+    {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8},
+    {1, 2, 8}, {1, 4, 8}, {1, 5, 8}, {2, 2, 16}, {2, 3, 16}, {2, 4, 16}, {2, 5, 8}, {4, 4, 16},
+    {2, 2, 4}, {2, 4, 4}, {4, 2, 4}, {4, 4, 4}};
+
+constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
+                                  kXs2x3, kXs2x4, kXs2x5, kXs4x4};
+
+// Modelled time of an XS form (microseconds): at 17 to 320 rows each
+// workgroup streams its MB x 16 activation rows (from L2) and NB weight
+// columns over all of K at about 45 GB/s per compute unit, after a fixed
+// start of 4 us (8 waves) or 1.5 us (16 waves: more loads in flight from the
+// first group); a compute unit that holds n workgroups takes n times as long.
+// Fitted to the decode layer set and its tensor-parallel shard (qkv 5120x896,
+// o 768x5120, gate_up 5120x4352, down 2176x5120) at M = 17 to 320, where the
+// form it puts first is within 1 % of the fastest of every form measured,
+// summed over the shapes.
+double xs_estimate_us(PlainForm f, int M, int N, int K) {
+  const PlainFormInfo& i = kPlainFormInfo[f];
+  const long long ncb = (static_cast<long long>(N) + 15) / 16;
+  const long long wgs = (ncb + i.nb - 1) / i.nb * ((static_cast<long long>(M) + 16 * i.mb - 1) / (16 * i.mb));
+  const long long rounds = (wgs + kModelCUs - 1) / kModelCUs;
+  const double bytes = static_cast<double>(K) * (32.0 * i.mb + 8.0 * i.nb);
+  return static_cast<double>(rounds) * (bytes / 45000.0 + (i.waves == 16 ? 1.5 : 4.0));
+}
+
+PlainForm best_xs_form(int M, int N, int K, double* est_out) {
+  PlainForm best = kXsForms[0];
+  double best_est = xs_estimate_us(best, M, N, K);
+  for (PlainForm f : kXsForms) {
+    const double e = xs_estimate_us(f, M, N, K);
+    if (e < best_est) {
+      best_est = e;
+      best = f;
+    }
+  }
+  if (est_out) *est_out = best_est;
+  return best;
+}
+
 template <int GS>
 hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
   constexpr int P2 = GS >= 256 ? 1 : 2;
   constexpr int P4 = GS >= 256 ? 2 : 4;
-  const bool wide = (a.N + 15) / 16 >= 1024;
-  const size_t xlds_rows = static_cast<size_t>(a.M < 16 ? a.M : 16) * (a.K + 8) * 2 +
-                           static_cast<size_t>(a.K / GS) * 64;
-  if (a.M <= 16) {
-    if (wide) {
-      if (a.M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit)
-        return launch_plain_t<GS, 1, 2, 4, P4, true>(a, s);
-      if (a.M <= 4) return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
-      return launch_plain_t<GS, 1, 4, 4, P2, false>(a, s);
-    }
-    if (a.M <= 2 && a.K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit)
-      return launch_plain_t<GS, 1, 2, 16, P2, true>(a, s);
-    if (a.M <= 8) return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
-    return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
+  switch (plain_form(a.M, a.N, a.K, GS)) {
+    case kWideStaged: return launch_plain_t<GS, 1, 2, 4, P4, true>(a, s);
+    case kWide2: return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
+    case kWide4: return launch_plain_t<GS, 1, 4, 4, P2, false>(a, s);
+    case kDeepStaged: return launch_plain_t<GS, 1, 2, 16, P2, true>(a, s);
+    case kSmall8: return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
+    case kOp2x2: return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
+    case kOp2x4: return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
+    case kOp4x2: return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
+    case kOp4x4: return launch_plain_t<GS, 4, 4, 4, 1, false>(a, s);
+    default: break;
   }
   if constexpr (GS == 128) {
-    // coalesced activation loads through a wave-private LDS area (XS); the
-    // layer set as four calls: 85 us at M = 32 (116 with operand-order loads),
-    // 143 us at M = 64 (188)
-    if (a.M <= 32) {
-      if (wide) return launch_plain_t<GS, 2, 4, 4, 1, false, 1, true>(a, s);
-      if (a.K >= 12288) return launch_plain_t<GS, 2, 2, 8, 2, false, 1, true>(a, s);
-      return launch_plain_t<GS, 2, 2, 16, 1, false, 2, true>(a, s);
+    switch (plain_form(a.M, a.N, a.K, GS)) {
+      case kXs1x2: return launch_plain_t<GS, 1, 2, 8, 1, false, 1, true>(a, s);
+      case kXs1x4: return launch_plain_t<GS, 1, 4, 8, 1, false, 1, true>(a, s);
+      case kXs1x5: return launch_plain_t<GS, 1, 5, 8, 1, false, 1, true>(a, s);
+      case kXs2x2: return launch_plain_t<GS, 2, 2, 16, 1, false, 2, true>(a, s);
+      case kXs2x3: return launch_plain_t<GS, 2, 3, 16, 1, false, 2, true>(a, s);
+      case kXs2x4: return launch_plain_t<GS, 2, 4, 16, 1, false, 2, true>(a, s);
+      case kXs2x5: return launch_plain_t<GS, 2, 5, 8, 1, false, 2, true>(a, s);
+      case kXs4x4: return launch_plain_t<GS, 4, 4, 16, 1, false, 4, true>(a, s);
+      default: break;
     }
-    if (wide) return launch_plain_t<GS, 4, 4, 8, 1, false, 4, true>(a, s);
-    return launch_plain_t<GS, 4, 2, 16, 2, false, 4, true>(a, s);
-  } else {
-    if (a.M <= 32) {
-      if (wide) return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
-      return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
-    }
-    // 33 and more rows: 64-row tiles (grid.y covers any M)
-    if (wide) return launch_plain_t<GS, 4, 4, 4, 1, false>(a, s);
-    return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
   }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+int plain_form(int M, int N, int K, int group) {
+  const bool wide = (N + 15) / 16 >= 1024;
+  const size_t xlds_rows = static_cast<size_t>(M < 16 ? M : 16) * (static_cast<size_t>(K) + 8) * 2 +
+                           static_cast<size_t>(K / group) * 64;
+  if (M <= 16) {
+    if (wide) {
+      if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
+      return M <= 4 ? kWide2 : kWide4;
+    }
+    if (M <= 2 && K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit) return kDeepStaged;
+    return M <= 8 ? kSmall8 : kWide2;
+  }
+  if (group == 128) return best_xs_form(M, N, K, nullptr);
+  if (M <= 32) return wide ? kOp2x4 : kOp2x2;
+  return wide ? kOp4x4 : kOp4x2;
+}
+
+void plain_form_shape(int form, int* rows, int* cols, int* waves) {
+  const PlainFormInfo& i = kPlainFormInfo[form >= 0 && form < kPlainForms ? form : 0];
+  *rows = 16 * i.mb;
+  *cols = 16 * i.nb;
+  *waves = i.waves;
+}
+
+// The best XS form's modelled time; at other group sizes the forms load their
+// activation fragments in operand order, measured 1.3x slower than XS at 64
+// rows on the decode layer set.
+double plain_estimate_us(int M, int N, int K, int group) {
+  double est = 0.0;
+  best_xs_form(M, N, K, &est);
+  return group == 128 ? est : 1.3 * est;
+}
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
   switch (a.group) {

@@ -915,16 +915,30 @@ hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan
                 : launch_streamk_x<false, true>(sk, h.group, h.grid, h.lds_bytes, stream);
 }
 
-// w4a16_gemm's M-dispatch. Measured on the decode layer set as four plain
-// calls: the small-M kernel (w4a16_plain.hip) takes 47 us at M = 1, 75 at 16,
-// 152 at 64, 240 at 128, 313 at 192, 403 at 256, 502 at 320 and 583 at 384;
-// the one-workgroup-per-tile MFMA engine 467 to 483 us up to M = 128 and 555 to
-// 559 us from 160 to 384.
+// w4a16_gemm's M-dispatch: up to 16 rows the small-M forms of plain_kernel;
+// from 17 to 320 rows whichever of the two families the time models put
+// first (the tile engine needs enough 256-column tiles to fill the compute
+// units: on the decode layer set gate_up from 17 rows, qkv from 160, o and
+// down from 224); above 320 rows the tile engine.
 int choose_path(int M, int N, int K, int group) {
-  (void)N;
-  (void)K;
-  (void)group;
-  return M <= 320 ? W4A16_PATH_SKINNY : W4A16_PATH_LARGE;
+  if (M <= 16 || !large_supported(group)) return W4A16_PATH_SKINNY;
+  if (M > 320) return W4A16_PATH_LARGE;
+  return tile_estimate_us(M, N, K, group, nullptr) < plain_estimate_us(M, N, K, group)
+             ? W4A16_PATH_LARGE
+             : W4A16_PATH_SKINNY;
+}
+
+int describe_form(int M, int N, int K, int group, int path, int* rows, int* cols, int* waves) {
+  if (path == W4A16_PATH_AUTO) path = choose_path(M, N, K, group);
+  const long long qbytes = static_cast<long long>((N + 15) / 16) * 16 * K / 2;
+  if (path == W4A16_PATH_LARGE && large_supported(group) && qbytes <= 0xFFFFFFF0LL) {
+    tile_estimate_us(M, N, K, group, rows);
+    *cols = 256;
+    *waves = 8;
+    return W4A16_PATH_LARGE;
+  }
+  plain_form_shape(plain_form(M, N, K, group), rows, cols, waves);
+  return W4A16_PATH_SKINNY;
 }
 
 }  // namespace w4a16_internal
