@@ -2,9 +2,10 @@
 
 w4a16_gemm picks a form per shape from time models of its kernels (the
 library's own choice; w4a16_select_form reports it): up to 16 rows the small-M
-forms of the plain kernel; from 17 rows either a plain-kernel form (16, 32 or
-64 rows by 32 to 80 columns per workgroup; at group 128 the activation
-fragments pass through a wave-private LDS area) or the whole-K tile engine
+forms of the plain kernel (from 9 rows at group 128 the forms below); from 17
+rows either a plain-kernel form (16, 32 or 64 rows by 32 to 80 columns per
+workgroup; at group 128 the activation fragments pass through a wave-private
+LDS area) or the whole-K tile engine
 (32, 64 or 128 rows by 256 columns; at 32 and 64 rows loads run three
 k-tiles ahead). Each case below is a shape for which the automatic choice is
 one given form (asserted first, on the host), ragged in M and N, with several
@@ -27,6 +28,9 @@ AUTO, SKINNY, LARGE = 0, 1, 2
 
 # ((M, N, K, group), expected (path, rows, cols, waves))
 FORM_CASES = [
+    ((9, 2000, 4096, 128), (1, 16, 32, 8)),
+    ((13, 17000, 1024, 128), (1, 16, 80, 8)),
+    ((16, 9000, 8192, 128), (1, 16, 64, 8)),
     ((17, 100, 4096, 128), (1, 16, 32, 8)),
     ((17, 5000, 8192, 128), (1, 16, 64, 8)),
     ((17, 9000, 8192, 128), (1, 16, 80, 8)),

@@ -155,7 +155,8 @@ def test_select_path():
 # 17408x5120) at the row counts of its sweep, the time models' choices.
 FORMS = {
     (1, 7168, 5120, 128): (1, 16, 32, 8), (1, 34816, 5120, 128): (1, 16, 32, 4),
-    (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 64, 4),
+    (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 80, 8),
+    (8, 34816, 5120, 128): (1, 16, 64, 4), (12, 5120, 17408, 128): (1, 16, 32, 8),
     (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (2, 32, 256, 8),
     (32, 5120, 17408, 128): (1, 16, 64, 8), (64, 7168, 5120, 128): (1, 32, 64, 16),
     (64, 5120, 6144, 128): (1, 32, 48, 16), (64, 34816, 5120, 128): (2, 64, 256, 8),

@@ -371,7 +371,7 @@ constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
 constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
                                   kXs2x3, kXs2x4, kXs2x5, kXs4x4};
 
-// Modelled time of an XS form (microseconds): at 17 to 320 rows each
+// Modelled time of an XS form (microseconds): at 9 to 320 rows each
 // workgroup streams its MB x 16 activation rows (from L2) and NB weight
 // columns over all of K at about 45 GB/s per compute unit, after a fixed
 // start of 4 us (8 waves) or 1.5 us (16 waves: more loads in flight from the
@@ -379,7 +379,9 @@ constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
 // Fitted to the decode layer set and its tensor-parallel shard (qkv 5120x896,
 // o 768x5120, gate_up 5120x4352, down 2176x5120) at M = 17 to 320, where the
 // form it puts first is within 1 % of the fastest of every form measured,
-// summed over the shapes.
+// summed over the shapes; at 9 to 16 rows (the rows past M repeat row M - 1
+// and are read from the caches) it puts first the fastest XS form of each
+// decode projection.
 double xs_estimate_us(PlainForm f, int M, int N, int K) {
   const PlainFormInfo& i = kPlainFormInfo[f];
   const long long ncb = (static_cast<long long>(N) + 15) / 16;
@@ -441,6 +443,10 @@ int plain_form(int M, int N, int K, int group) {
   const bool wide = (N + 15) / 16 >= 1024;
   const size_t xlds_rows = static_cast<size_t>(M < 16 ? M : 16) * (static_cast<size_t>(K) + 8) * 2 +
                            static_cast<size_t>(K / group) * 64;
+  // From 9 rows at group 128 the XS forms win on the decode layer set and its
+  // tensor-parallel shard (M = 16: 76.6 -> 61.8 us per layer set as four
+  // calls); at 8 rows and fewer the forms below (measured at M = 4, 6 and 8).
+  if (group == 128 && M >= 9) return best_xs_form(M, N, K, nullptr);
   if (M <= 16) {
     if (wide) {
       if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
@@ -449,7 +455,6 @@ int plain_form(int M, int N, int K, int group) {
     if (M <= 2 && K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit) return kDeepStaged;
     return M <= 8 ? kSmall8 : kWide2;
   }
-  if (group == 128) return best_xs_form(M, N, K, nullptr);
   if (M <= 32) return wide ? kOp2x4 : kOp2x2;
   return wide ? kOp4x4 : kOp4x2;
 }
