@@ -151,7 +151,11 @@ size_t w4a16_workspace_bytes(int M, long long total_columns);
  * 128) a persistent grid of MFMA workgroups splits the (tile, k-tile) work
  * evenly, combining the tiles cut between workgroups through the workspace.
  * Both sum parts in a fixed order, so results are deterministic. Group 256 at
- * M > 16 runs the kernels of w4a16_gemm and does not use the workspace.
+ * M > 16 runs the kernels of w4a16_gemm and does not use the workspace; so
+ * does any problem above 16 rows for which the library's time models put
+ * w4a16_gemm's kernels ahead of the stream-K schedule (most shapes below a
+ * few hundred rows; the exceptions are few, deep 256-column tiles), and the
+ * result is then that of w4a16_gemm, bit for bit.
  * Extra errors: W4A16_ERR_INVALID_ARG for a null or too small workspace
  * (checked only when a streaming kernel runs), W4A16_ERR_MISALIGNED for a
  * workspace that is not 256-byte aligned.
@@ -198,7 +202,8 @@ typedef struct w4a16_problem {
  * 1..W4A16_MAX_PROBLEMS. The workspace is sized by
  * w4a16_workspace_bytes(M, sum of N). Each problem is validated as in
  * w4a16_gemm; with group 256 at M > 16 the problems run one after another on
- * `stream` without the workspace.
+ * `stream` without the workspace. A call of one problem runs as w4a16_gemm_ws
+ * (which may take w4a16_gemm's kernels above 16 rows).
  */
 #define W4A16_MAX_PROBLEMS 8
 int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int group,

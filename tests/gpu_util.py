@@ -69,6 +69,22 @@ def workspace(M: int, total_columns: int):
     return torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device="cuda")
 
 
+def run_streamk(prob: "Problem", ws=None) -> np.ndarray:
+    """One w4a16_gemm_grouped launch holding the problem twice, with two outputs:
+    the stream-K schedule runs whatever the shape (w4a16_gemm_ws may run
+    w4a16_gemm's kernels for a single problem above 16 rows). Both outputs are
+    returned; the copies are cut differently, so their bits may differ."""
+    import w4a16_weight_only_gemm_amd as w4
+    torch = torch_mod()
+    if ws is None:
+        ws = workspace(prob.M, 2 * prob.N)
+    ys = [torch.empty((prob.M, prob.N), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    w4.w4a16_gemm_grouped([(prob.x, prob.qw, prob.sp, y, prob.N, prob.K) for y in ys], prob.M,
+                          prob.group, ws)
+    torch.cuda.synchronize()
+    return [y.view(torch.int16).cpu().numpy().view(np.uint16) for y in ys]
+
+
 def run_ws(prob: "Problem", ws=None) -> np.ndarray:
     """One call of w4a16_gemm_ws (streaming kernel for M <= 16)."""
     import w4a16_weight_only_gemm_amd as w4

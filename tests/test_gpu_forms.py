@@ -119,3 +119,35 @@ def test_forced_form_parity(case):
     if form is not None:
         assert got == form
     _check(100 + cid, M, N, K, g, path)
+
+
+# single problems on the workspace entry point: (M, N, K, group), whether the
+# time models route them to w4a16_gemm's kernels
+WS_SINGLE = [((64, 5120, 6144, 128), True), ((17, 272, 384, 128), True),
+             ((64, 40, 65536, 128), False), ((500, 40, 16384, 128), False)]
+
+
+@pytest.mark.parametrize("case", list(enumerate(WS_SINGLE)),
+                         ids=lambda c: "x".join(map(str, c[1][0])))
+def test_workspace_call_of_one_problem(case):
+    """w4a16_gemm_ws with one problem above 16 rows: where the models put
+    w4a16_gemm's kernels ahead it returns w4a16_gemm's result bit for bit and
+    leaves the workspace untouched; either way the result is within the
+    tolerance of the oracle (48 sampled columns)."""
+    import torch
+
+    from gpu_util import run_ws, workspace
+    cid, ((M, N, K, g), whole) = case
+    log(f"workspace call of one problem M={M} N={N} K={K} g={g}")
+    q = synth.gen_q(synth.tensor_id(synth.KIND_Q, 760 + cid, 0), N, K)
+    s = synth.gen_scales(synth.tensor_id(synth.KIND_SCALES, 760 + cid, 0), N, K // g)
+    x = synth.gen_x(synth.tensor_id(synth.KIND_X, 760 + cid, 0, M), M, K)
+    prob = Problem(x, q, s, g)
+    ws = workspace(M, N)
+    y = run_ws(prob, ws)
+    assert int(torch.count_nonzero(ws)) == 0
+    if whole:
+        assert np.array_equal(y, prob.run(AUTO))
+    cols = np.sort(np.random.default_rng(cid).choice(N, min(N, 48), replace=False))
+    ref = oracle.gemm(x, q[cols], s[cols], g, threads=synth.default_threads())
+    assert tolerance_ratio(y[:, cols], ref) <= 1.0

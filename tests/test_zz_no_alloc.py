@@ -56,12 +56,13 @@ def _check(case, M, N, K, g):
     assert tolerance_ratio(y[:, cols], ref) <= 1.0
 
 
-# (first call, second smaller call): both stream-K forms of the workspace path
+# (first call, second smaller call): both stream-K forms of the workspace path,
+# and the single problems above 16 rows that run w4a16_gemm's kernels instead
 PAIRS = [
     ((16, 7168, 5120, 128), (3, 1000, 1024, 128)),     # M <= 16 streaming kernel
     ((1, 34816, 5120, 128), (1, 520, 512, 64)),        # M = 1, activations staged in LDS
-    ((64, 5120, 6144, 128), (20, 520, 512, 64)),       # M > 16 MFMA stream-K
-    ((1024, 2048, 2048, 128), (100, 300, 1280, 128)),  # 128-row tiles, then 128-row tiles again
+    ((1024, 48, 32768, 128), (64, 40, 65536, 128)),    # M > 16 MFMA stream-K (deep, narrow), twice
+    ((64, 5120, 6144, 128), (20, 520, 512, 64)),       # M > 16, w4a16_gemm's kernels: no scratch used
     ((300, 72, 512, 256), (17, 40, 256, 256)),         # group 256 above 16 rows: no scratch used
 ]
 

@@ -190,6 +190,13 @@ int w4a16_gemm_grouped(const w4a16_problem* problems, int count, int M, int grou
       return W4A16_ERR_MISALIGNED;
     columns += p.N;
   }
+  // One problem above 16 rows: w4a16_gemm's kernels when the time models put
+  // them ahead (they need no workspace, which is then left untouched).
+  if (count == 1 && w4a16_internal::single_prefers_whole_k(M, problems[0].N, problems[0].K, group)) {
+    const w4a16_problem& p = problems[0];
+    return w4a16_gemm_ex(p.x, p.qweight, p.scales, p.y, M, p.N, p.K, group, W4A16_PATH_AUTO,
+                         stream);
+  }
   w4a16_internal::StreamKProblem probs[W4A16_MAX_PROBLEMS] = {};
   for (int i = 0; i < count; ++i) {
     probs[i].x = static_cast<const uint16_t*>(problems[i].x);

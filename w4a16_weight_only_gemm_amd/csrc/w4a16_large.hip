@@ -49,6 +49,7 @@
 // beyond N are clamped on load; neither is stored.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 
@@ -632,6 +633,20 @@ hipError_t launch_tile_g(const GemmArgs& a, int rows, hipStream_t stream) {
   }
 }
 
+// Stream-K cost figures (one MI355X, decode layer-set projections launched
+// alone and grouped): one k-tile of 128 per workgroup costs about 0.6, 0.75 and
+// 2.2 us at 32, 64 and 128 rows, and the workgroup that finishes a cut tile
+// reads each part (8 waves x 16, 32 or 64 floats per lane: 32, 64 or 128 KB)
+// at about 55 GB/s.
+double streamk_ktile_us(int rows) { return rows <= 32 ? 0.6 : (rows <= 64 ? 0.75 : 2.2); }
+double streamk_part_us(int rows) { return 2048.0 * (rows / 16) * 8 / 55000.0; }
+
+long long streamk_max_ways(int rows, int max_kt) {
+  const double s = std::sqrt(static_cast<double>(max_kt) * streamk_ktile_us(rows) / streamk_part_us(rows));
+  const long long w = static_cast<long long>(std::ceil(s));
+  return w < 2 ? 2 : w;
+}
+
 // Units and tiles of the problems for tiles of `rows` rows (group GS): fills
 // the problems' offsets and returns the unit count; *tiles_out is the tile
 // count, *nwg_out the workgroups of the persistent grid.
@@ -639,6 +654,7 @@ long long plan_large_probs(LargeProblem* probs, int count, int M, int group, int
                            long long* tiles_out, int* nwg_out) {
   const int T = kLgKT / group;  // groups per k-tile
   long long units = 0, tiles = 0;
+  int max_kt = 1;
   for (int i = 0; i < count; ++i) {
     LargeProblem& p = probs[i];
     p.G = p.K / group;
@@ -650,9 +666,17 @@ long long plan_large_probs(LargeProblem* probs, int count, int M, int group, int
     p.t_begin = static_cast<int>(tiles);
     units += static_cast<long long>(p.MT) * p.NT * p.KT;
     tiles += static_cast<long long>(p.MT) * p.NT;
+    if (p.KT > max_kt) max_kt = p.KT;
   }
   long long nwg = static_cast<long long>(device_cus());
   if (nwg > kLargeMaxWorkgroups) nwg = kLargeMaxWorkgroups;
+  // A tile cut among S workgroups is summed by one of them, which reads the S
+  // parts; beyond about sqrt(k-tiles x cost per k-tile / time per part) ways
+  // that read costs more than the split saves. A launch of few, deep tiles
+  // (one 64-column problem with K = 65536 has one tile of 512 k-tiles) would
+  // otherwise cut each tile among every workgroup.
+  const long long cap = tiles * streamk_max_ways(rows, max_kt);
+  if (nwg > cap) nwg = cap;
   if (nwg > units) nwg = units;  // every workgroup owns at least one unit
   *tiles_out = tiles;
   *nwg_out = static_cast<int>(nwg);
@@ -762,6 +786,37 @@ size_t large_streamk_counter_bytes(int M, long long total_columns) {
 size_t large_streamk_part_bytes(int M) {
   const int regs = large_streamk_rows(M) / 16 * kLgNB * 4;
   return static_cast<size_t>(kLargeMaxWorkgroups) * 2 * kLgWaves * regs * 64 * sizeof(float);
+}
+
+// One problem above 16 rows: whether the kernels of w4a16_gemm (whole K per
+// workgroup, no workspace) are expected to beat the stream-K schedule. The
+// stream-K time: a workgroup's k-tiles at their cost, the finisher's reads of
+// the parts of a cut tile, and about 15 us of launch, first loads and hand-off;
+// it must win by 10 % to be chosen. On the decode layer set's projections
+// alone it wins only for down (17408 x 5120) from M = 256 (1024 rows: 217
+// against 241 us); at M = 64 every projection is about twice as fast whole
+// (qkv 15.5 against 33.8 us).
+bool single_prefers_whole_k(int M, int N, int K, int group) {
+  if (M <= 16 || !large_supported(group)) return false;
+  const int rows = large_streamk_rows(M);
+  LargeProblem p = {};
+  p.N = N;
+  p.K = K;
+  long long tiles = 0;
+  int nwg = 0;
+  const long long units = plan_large_probs(&p, 1, M, group, rows, &tiles, &nwg);
+  if (nwg < 1) return true;
+  const double u = static_cast<double>(units) / nwg;
+  const double kt = static_cast<double>(p.KT);
+  double ways = u < kt ? std::ceil(kt / u) + 1.0 : 2.0;
+  if (ways > nwg) ways = nwg;
+  const double sk = u * streamk_ktile_us(rows) + ways * streamk_part_us(rows) + 15.0;
+  double whole = tile_estimate_us(M, N, K, group, nullptr);
+  if (M <= 320) {
+    const double plain = plain_estimate_us(M, N, K, group);
+    if (plain < whole) whole = plain;
+  }
+  return !(sk < 0.9 * whole);
 }
 
 bool large_streamk_fits(const StreamKProblem* probs, int count, int M, int group) {

@@ -35,6 +35,9 @@ double tile_estimate_us(int M, int N, int K, int group, int* rows_out);
 int plain_form(int M, int N, int K, int group);
 void plain_form_shape(int form, int* rows, int* cols, int* waves);
 double plain_estimate_us(int M, int N, int K, int group);
+// A single problem above 16 rows that the workspace entry points run with the
+// kernels of w4a16_gemm instead of the stream-K schedule.
+bool single_prefers_whole_k(int M, int N, int K, int group);
 
 // ---- stream-K (persistent, several problems per launch, M <= 16) ----
 constexpr int kMaxProblems = 8;
