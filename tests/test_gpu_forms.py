@@ -31,6 +31,8 @@ FORM_CASES = [
     ((9, 2000, 4096, 128), (1, 16, 32, 8)),
     ((13, 17000, 1024, 128), (1, 16, 80, 8)),
     ((16, 9000, 8192, 128), (1, 16, 64, 8)),
+    ((11, 300, 128, 128), (1, 32, 32, 16)),     # 32-row forms below 17 rows: a padding row block
+    ((15, 9000, 256, 128), (1, 32, 48, 16)),
     ((17, 100, 4096, 128), (1, 16, 32, 8)),
     ((17, 5000, 8192, 128), (1, 16, 64, 8)),
     ((17, 9000, 8192, 128), (1, 16, 80, 8)),
