@@ -87,6 +87,15 @@ DRIVER = textwrap.dedent(r'''
         for cols in (0, 1, 52224, 248320):
             assert san.w4a16_workspace_bytes(M, cols) == ref.w4a16_workspace_bytes(M, cols)
         assert san.w4a16_select_path(M, 512, 256, 64) == ref.w4a16_select_path(M, 512, 256, 64)
+    # the form models (host arithmetic over the shape): same choice in both builds
+    outs = [(ctypes.c_int * 3)() for _ in range(2)]
+    for M in (1, 2, 9, 16, 17, 64, 129, 320, 321, 4096):
+        for (N, K, g) in ((1, 128, 32), (100, 2048, 64), (5120, 17408, 128), (34816, 5120, 128),
+                          (248320, 5120, 128), (7000, 4096, 256)):
+            for path in (0, 1, 2):
+                rs = [lib.w4a16_select_form(M, N, K, g, path, ctypes.byref(o, 0), ctypes.byref(o, 4),
+                                            ctypes.byref(o, 8)) for lib, o in zip((san, ref), outs)]
+                assert rs[0] == rs[1] and list(outs[0]) == list(outs[1]), (M, N, K, g, path)
     for st in range(-1, 8):
         assert san.w4a16_status_string(st) == ref.w4a16_status_string(st)
     # argument checks of every GEMM entry point: each returns before any launch
