@@ -19,7 +19,7 @@ struct GemmArgs {
 // all pointers 16-byte aligned.
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream);
-// Group sizes the tiled large-M kernel handles (others fall back to split-K).
+// Group sizes the MFMA tile engine handles (others run the plain kernel).
 bool large_supported(int group);
 
 // ---- w4a16_gemm's choice of kernel form (host arithmetic only) ----
