@@ -335,8 +335,9 @@ enum PlainForm : int {
   // over every (column blocks, waves, groups in flight, staging) form that
   // fits: wide N (2176 column blocks) prefers 4-wave workgroups with 2 to 4
   // column blocks; deep K at one or two rows 16 waves and staged rows; the
-  // rest 8 waves below 9 rows, 4 waves above. Group 256 (twice the registers
-  // per group) keeps fewer groups in flight.
+  // rest 8 waves below 9 rows, 4 waves above (at groups 32, 64 and 256; group
+  // 128 takes the XS forms from 9 rows). Group 256 (twice the registers per
+  // group) keeps fewer groups in flight.
   kWideStaged,   // 1 x 2 blocks, 4 waves, rows in LDS
   kWide2,        // 1 x 2, 4 waves
   kWide4,        // 1 x 4, 4 waves
