@@ -864,6 +864,59 @@ def run_head(steps: int, warmup: int, rows=HEAD_ROWS):
             "rows": out}
 
 
+PATH_ROWS = (17, 32, 48, 64, 96, 128, 160, 192, 256, 320, 512, 1024)
+
+
+def run_paths(layers: int, rows=PATH_ROWS, reps: int = 50):
+    """The M-dispatch of w4a16_gemm checked against its two alternatives: for
+    every projection of the decode layer set and of its tensor-parallel shard,
+    at each M, the median time of one call forced onto the small-M kernel
+    (W4A16_PATH_SKINNY: the plain_kernel form its model ranks first), forced
+    onto the tile engine (W4A16_PATH_LARGE: the tile height its model ranks
+    first), and left to choose (W4A16_PATH_AUTO), with the workgroup tile
+    w4a16_select_form reports. Above 320 rows the automatic choice is always
+    the tile engine. One JSON object."""
+    import ctypes
+
+    import torch
+
+    import synth
+    import w4a16_weight_only_gemm_amd as w4
+    lib = w4._lib
+    cur = torch.cuda.current_stream()
+    out = []
+    # enough layer sets cycled that no call finds its weights in the 256 MB
+    # last-level cache: 8 of the layer set (1.4 GB), 16 of the shard (346 MB)
+    for label, projs, base, nl in (("layer set", synth.LAYER_PROJECTIONS, 0, layers),
+                                   ("tp8 shard", synth.TP8_SHARD_PROJECTIONS, synth.SHARD_PROJ_BASE,
+                                    2 * layers)):
+        store = LayerStore(nl, projs, base)
+        for M in rows:
+            wl = Workload(store, M)
+            for pi, p in enumerate(projs):
+                rec = {"set": label, "proj": p.name, "M": M, "N": p.N, "K": p.K,
+                       "form": w4.w4a16_select_form(M, p.N, p.K, GROUP)}
+                for name, path in (("skinny", w4.W4A16_PATH_SKINNY), ("large", w4.W4A16_PATH_LARGE),
+                                   ("auto", w4.W4A16_PATH_AUTO)):
+                    def call(s, path=path):
+                        a = wl.plain[s % wl.L][pi]
+                        rc = lib.w4a16_gemm_ex(*a, path, ctypes.c_void_p(cur.cuda_stream))
+                        if rc != 0:
+                            raise RuntimeError(f"w4a16_gemm_ex failed with status {rc}")
+                    clock_warmup(lambda: call(0), 0.05)
+                    rec[name + "_us"] = window_stats(call, reps, 10, cur)["median_ms"] * 1e3
+                best = min(rec["skinny_us"], rec["large_us"])
+                rec["auto_over_best"] = rec["auto_us"] / best
+                out.append(rec)
+                print(f"# {label} {p.name} M={M}: skinny {rec['skinny_us']:.1f} large "
+                      f"{rec['large_us']:.1f} auto {rec['auto_us']:.1f} us, form {rec['form']}",
+                      file=sys.stderr, flush=True)
+            del wl
+        del store
+        torch.cuda.empty_cache()
+    return {"workload": "w4a16_gemm_ex per projection, forced paths and the automatic choice",
+            "rows": out}
+
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
@@ -899,6 +952,9 @@ def main(argv=None):
                          "model fitted to it (one JSON object), instead of the headline line")
     ap.add_argument("--sweep-layers", type=int, default=64)
     ap.add_argument("--sweep-passes", type=int, default=10)
+    ap.add_argument("--paths", action="store_true",
+                    help="w4a16_gemm's automatic path against both forced paths per projection "
+                         "at M = 17..1024 (one JSON object), instead of the headline line")
     ap.add_argument("--head", action="store_true",
                     help="output-head workload (N = 248,320, K = 5120) at M = 1..16 (one JSON "
                          "object), instead of the headline line")
@@ -923,6 +979,9 @@ def main(argv=None):
         return 0
     if args.head:
         print(json.dumps(run_head(args.steps, min(args.warmup, 1000))))
+        return 0
+    if args.paths:
+        print(json.dumps(run_paths(min(args.layers, 8))))
         return 0
 
     sampler = None if args.no_smi else ClockSampler().start()

@@ -41,7 +41,7 @@ FORM_CASES = [
     ((37, 7001, 256, 128), (1, 32, 64, 16)),
     ((17, 17000, 1024, 128), (1, 32, 80, 8)),
     ((37, 9000, 256, 128), (1, 64, 64, 16)),
-    ((333, 520, 256, 128), (2, 32, 256, 8)),
+    ((17, 17000, 256, 128), (2, 32, 256, 8)),
     ((37, 35001, 256, 128), (2, 64, 256, 8)),
     ((517, 12001, 256, 128), (2, 128, 256, 8)),
     ((17, 100, 512, 64), (1, 32, 32, 4)),

@@ -89,7 +89,7 @@ def test_large_row_sums_are_per_row_and_group():
 
 def test_large_deterministic_and_auto_choice():
     import w4a16_weight_only_gemm_amd as w4
-    M, N, K, g = 512, 512, 1024, 128
+    M, N, K, g = 512, 4096, 1024, 128   # 16 column tiles: the tile engine's shape
     assert w4.w4a16_select_path(M, N, K, g) == LARGE
     x, q, s = _inputs(90, M, N, K, g)
     prob = Problem(x, q, s, g)

@@ -51,7 +51,8 @@ def _rows_bits(x, rows):
 
 def test_w4a16_large_path_activations_over_4gb():
     """w4a16_gemm_ex on the one-workgroup-per-tile path with 4.3 GB of
-    activations (K = 32768): two row chunks, the first of 65,408 rows."""
+    activations (K = 32768): two row chunks, the first of 65,408 rows; then
+    w4a16_gemm and w4a16_gemm_ws (plain_kernel) on the same input."""
     import torch
 
     import w4a16_weight_only_gemm_amd as w4
@@ -68,14 +69,22 @@ def test_w4a16_large_path_activations_over_4gb():
     ref = oracle.gemm(_rows_bits(x, rows), q, s, g)
     yb = y[rows].view(torch.int16).cpu().numpy().view(np.uint16)
     assert tolerance_ratio(yb, ref) <= 1.0
-    # the workspace entry point falls back to the same per-problem kernels here
+    # w4a16_gemm runs plain_kernel here (three column blocks: the tile engine
+    # would leave most compute units idle), and the workspace entry point
+    # routes this one problem to w4a16_gemm's kernels
+    assert w4.w4a16_select_form(M, N, K, g)[0] == w4.W4A16_PATH_SKINNY
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm(x, dev_u32(qw), dev_u16(sp), y2, M, N, K, g)
+    torch.cuda.synchronize()
+    yb2 = y2[rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert tolerance_ratio(yb2, ref) <= 1.0
     nb = w4.w4a16_workspace_bytes(M, N)
     ws = torch.zeros((nb + 3) // 4, dtype=torch.int32, device="cuda")
-    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    w4.w4a16_gemm_ws(x, dev_u32(qw), dev_u16(sp), y2, M, N, K, g, ws)
+    y3 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    w4.w4a16_gemm_ws(x, dev_u32(qw), dev_u16(sp), y3, M, N, K, g, ws)
     torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    del x, y, y2, ws
+    assert torch.equal(y2.view(torch.int16), y3.view(torch.int16))
+    del x, y, y2, y3, ws
 
 
 def test_w4a8_activations_over_4gb():

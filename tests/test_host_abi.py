@@ -144,7 +144,9 @@ def test_select_path():
     assert w4.w4a16_select_path(192, 5120, 6144, 128) == S
     assert w4.w4a16_select_path(320, 5120, 6144, 128) == L
     assert w4.w4a16_select_path(1024, 5120, 6144, 128) == L
-    assert w4.w4a16_select_path(1024, 16, 256, 128) == L            # above 320 rows: always
+    assert w4.w4a16_select_path(1024, 16, 256, 128) == S            # one column block
+    assert w4.w4a16_select_path(512, 896, 5120, 128) == S           # narrow: 4 column tiles
+    assert w4.w4a16_select_path(65535 * 16 + 1, 896, 5120, 128) == L  # past plain_kernel's grid
     assert w4.w4a16_select_path(64, 34816, 5120, 256) == S          # no tile engine at group 256
     assert w4.w4a16_select_path(1, 512, 256, 48) == -1
     assert w4.w4a16_select_path(-1, 512, 256, 64) == -1

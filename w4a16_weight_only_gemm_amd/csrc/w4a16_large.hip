@@ -812,7 +812,7 @@ bool single_prefers_whole_k(int M, int N, int K, int group) {
   if (ways > nwg) ways = nwg;
   const double sk = u * streamk_ktile_us(rows) + ways * streamk_part_us(rows) + 15.0;
   double whole = tile_estimate_us(M, N, K, group, nullptr);
-  if (M <= 320) {
+  if (M <= kPlainMaxRows) {
     const double plain = plain_estimate_us(M, N, K, group);
     if (plain < whole) whole = plain;
   }

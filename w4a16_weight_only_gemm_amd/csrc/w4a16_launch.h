@@ -26,6 +26,9 @@ bool large_supported(int group);
 // Compute units the time models below assume (one MI355X); the choice is a
 // pure function of the shape, so it is the same on every device and call.
 constexpr int kModelCUs = 256;
+// Rows plain_kernel takes: its grid's second dimension counts row tiles of at
+// least 16 rows and holds at most 65535.
+constexpr int kPlainMaxRows = 65535 * 16;
 // Modelled time (microseconds) of the best whole-K tile form (tile_kernel) for
 // the shape, and its tile height (32, 64 or 128 rows) in *rows_out.
 double tile_estimate_us(int M, int N, int K, int group, int* rows_out);

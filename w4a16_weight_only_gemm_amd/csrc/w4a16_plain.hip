@@ -308,6 +308,8 @@ __global__ __launch_bounds__(64 * WAVES) void plain_kernel(const uint16_t* __res
 template <int GS, int MB, int NB, int WAVES, int P, bool XLDS, int WM = 1, bool XS = false>
 hipError_t launch_plain_t(const GemmArgs& a, hipStream_t stream) {
   const int NCB = (a.N + 15) / 16;
+  if ((static_cast<long long>(a.M) + 16 * MB - 1) / (16 * MB) > 65535)
+    return hipErrorInvalidValue;  // grid.y holds at most 65535 row tiles
   dim3 grid((NCB + NB - 1) / NB, (a.M + 16 * MB - 1) / (16 * MB));
   const int Mr = a.M < 16 * MB ? a.M : 16 * MB;
   size_t lds = static_cast<size_t>(WAVES / WM) * MB * NB * 256 * sizeof(float);
@@ -372,7 +374,7 @@ constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
 constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
                                   kXs2x3, kXs2x4, kXs2x5, kXs4x4};
 
-// Modelled time of an XS form (microseconds): at 9 to 320 rows each
+// Modelled time of an XS form (microseconds): from 9 rows each
 // workgroup streams its MB x 16 activation rows (from L2) and NB weight
 // columns over all of K at about 45 GB/s per compute unit, after a fixed
 // start of 4 us (8 waves) or 1.5 us (16 waves: more loads in flight from the
@@ -380,7 +382,9 @@ constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
 // Fitted to the decode layer set and its tensor-parallel shard (qkv 5120x896,
 // o 768x5120, gate_up 5120x4352, down 2176x5120) at M = 17 to 320, where the
 // form it puts first is within 1 % of the fastest of every form measured,
-// summed over the shapes; at 9 to 16 rows (the rows past M repeat row M - 1
+// summed over the shapes (above 320 rows it runs 5-11 % under the measured
+// time of the shard's qkv, 12.4 and 19.7 against 13.0 and 22.1 us at 512 and
+// 1024 rows, still far from the tile engine's 30 us); at 9 to 16 rows (the rows past M repeat row M - 1
 // and are read from the caches) it puts first the fastest XS form of each
 // decode projection.
 double xs_estimate_us(PlainForm f, int M, int N, int K) {

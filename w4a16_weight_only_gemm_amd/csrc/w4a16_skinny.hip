@@ -916,13 +916,15 @@ hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan
 }
 
 // w4a16_gemm's M-dispatch: up to 16 rows the small-M forms of plain_kernel;
-// from 17 to 320 rows whichever of the two families the time models put
-// first (the tile engine needs enough 256-column tiles to fill the compute
-// units: on the decode layer set gate_up from 17 rows, qkv from 160, o and
-// down from 224); above 320 rows the tile engine.
+// above, whichever of the two families the time models put first (the tile
+// engine needs enough 256-column tiles to fill the compute units: on the
+// decode layer set gate_up from 17 rows, qkv from 160, o and down from 224;
+// a narrow projection such as the tensor-parallel shard's qkv 5120x896 stays
+// on plain_kernel at 1024 rows, 22 against 30 us). Beyond 65535 row tiles of
+// 16 (the grid's second dimension) only the tile engine runs.
 int choose_path(int M, int N, int K, int group) {
   if (M <= 16 || !large_supported(group)) return W4A16_PATH_SKINNY;
-  if (M > 320) return W4A16_PATH_LARGE;
+  if (M > kPlainMaxRows) return W4A16_PATH_LARGE;
   return tile_estimate_us(M, N, K, group, nullptr) < plain_estimate_us(M, N, K, group)
              ? W4A16_PATH_LARGE
              : W4A16_PATH_SKINNY;
