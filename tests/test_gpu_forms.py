@@ -2,7 +2,8 @@
 
 w4a16_gemm picks a form per shape from time models of its kernels (the
 library's own choice; w4a16_select_form reports it): up to 16 rows the small-M
-forms of the plain kernel (from 9 rows at group 128 the forms below); from 17
+forms of the plain kernel (16 to 64 columns per workgroup of 4, 8 or 16 waves,
+rows in LDS at one or two rows; from 9 rows at group 128 the forms below); from 17
 rows either a plain-kernel form (16, 32 or 64 rows by 32 to 80 columns per
 workgroup; at group 128 the activation fragments pass through a wave-private
 LDS area) or the whole-K tile engine
@@ -28,6 +29,12 @@ AUTO, SKINNY, LARGE = 0, 1, 2
 
 # ((M, N, K, group), expected (path, rows, cols, waves))
 FORM_CASES = [
+    ((1, 3000, 4096, 128), (1, 16, 16, 16)),    # one row in LDS, one column block per workgroup
+    ((5, 900, 2048, 128), (1, 16, 16, 16)),     # few column blocks: one per 16-wave workgroup
+    ((3, 1000, 1024, 32), (1, 16, 16, 16)),
+    ((1, 3000, 2048, 64), (1, 16, 16, 16)),
+    ((2, 500, 2048, 256), (1, 16, 16, 16)),
+    ((7, 17000, 512, 128), (1, 16, 32, 4)),
     ((9, 2000, 4096, 128), (1, 16, 32, 8)),
     ((13, 17000, 1024, 128), (1, 16, 80, 8)),
     ((16, 9000, 8192, 128), (1, 16, 64, 8)),

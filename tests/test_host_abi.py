@@ -156,9 +156,11 @@ def test_select_path():
 # decode layer set (qkv 5120x7168, o 6144x5120, gate_up 5120x34816, down
 # 17408x5120) at the row counts of its sweep, the time models' choices.
 FORMS = {
-    (1, 7168, 5120, 128): (1, 16, 32, 8), (1, 34816, 5120, 128): (1, 16, 32, 4),
+    (1, 7168, 5120, 128): (1, 16, 16, 16), (1, 34816, 5120, 128): (1, 16, 32, 4),
     (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 80, 8),
-    (8, 34816, 5120, 128): (1, 16, 64, 4), (12, 5120, 17408, 128): (1, 16, 32, 8),
+    (8, 34816, 5120, 128): (1, 16, 32, 4), (12, 5120, 17408, 128): (1, 16, 32, 8),
+    (2, 7168, 5120, 128): (1, 16, 32, 8), (4, 896, 5120, 128): (1, 16, 16, 16),
+    (8, 34816, 5120, 64): (1, 16, 64, 4), (1, 896, 17408, 128): (1, 16, 32, 16),
     (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (2, 32, 256, 8),
     (32, 5120, 17408, 128): (1, 16, 64, 8), (64, 7168, 5120, 128): (1, 32, 64, 16),
     (64, 5120, 6144, 128): (1, 32, 48, 16), (64, 34816, 5120, 128): (2, 64, 256, 8),
@@ -189,13 +191,13 @@ def test_select_form():
 
 def test_select_form_bounds():
     """Every chosen form exists and tiles the output: rows 16..128, columns
-    32..256 in 16-column blocks, 4..16 waves, over a grid of shapes."""
+    16..256 in 16-column blocks, 4..16 waves, over a grid of shapes."""
     for M in (1, 2, 3, 5, 9, 16, 17, 31, 33, 64, 65, 100, 200, 320, 321, 700, 5000):
         for N in (1, 16, 100, 1000, 5000, 34816, 248320):
             for K, g in ((128, 32), (256, 64), (5120, 128), (17408, 128), (4096, 256)):
                 p, r, c, w = w4.w4a16_select_form(M, N, K, g)
                 assert p in (1, 2) and r in (16, 32, 64, 128) and c % 16 == 0
-                assert 32 <= c <= 256 and w in (4, 8, 16)
+                assert 16 <= c <= 256 and w in (4, 8, 16)
 
 
 def test_workspace_sizes():

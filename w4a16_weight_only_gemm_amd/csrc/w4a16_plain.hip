@@ -339,12 +339,17 @@ enum PlainForm : int {
   // column blocks; deep K at one or two rows 16 waves and staged rows; the
   // rest 8 waves below 9 rows, 4 waves above (at groups 32, 64 and 256; group
   // 128 takes the XS forms from 9 rows). Group 256 (twice the registers per
-  // group) keeps fewer groups in flight.
+  // group) keeps fewer groups in flight. Few column blocks (the tensor-parallel
+  // shard's qkv 5120x896: 56) take one block per 16-wave workgroup, and so does
+  // one row whose K fits LDS (qkv and o of the layer set: 6.75 -> 6.29 and
+  // 6.88 -> 6.47 us).
   kWideStaged,   // 1 x 2 blocks, 4 waves, rows in LDS
   kWide2,        // 1 x 2, 4 waves
   kWide4,        // 1 x 4, 4 waves
   kDeepStaged,   // 1 x 2, 16 waves, rows in LDS
   kSmall8,       // 1 x 2, 8 waves
+  kOne16Staged,  // 1 x 1, 16 waves, rows in LDS
+  kOne16,        // 1 x 1, 16 waves
   // more rows at group 128, activation fragments through a wave-private LDS
   // area (XS); MB x NB blocks, waves (along rows x along K)
   kXs1x2,        // 1 x 2, 8 waves (1 x 8)
@@ -367,7 +372,7 @@ struct PlainFormInfo {
   int mb, nb, waves;
 };
 constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
-    {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8},
+    {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8}, {1, 1, 16}, {1, 1, 16},
     {1, 2, 8}, {1, 4, 8}, {1, 5, 8}, {2, 2, 16}, {2, 3, 16}, {2, 4, 16}, {2, 5, 8}, {4, 4, 16},
     {2, 2, 4}, {2, 4, 4}, {4, 2, 4}, {4, 4, 4}};
 
@@ -414,12 +419,19 @@ template <int GS>
 hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
   constexpr int P2 = GS >= 256 ? 1 : 2;
   constexpr int P4 = GS >= 256 ? 2 : 4;
+  // one group of 128 (or more) in flight: at group 128 the 4-wave two-block
+  // form at 3 to 8 rows (gate_up M = 4: 23.2 -> 22.1 us) and the one-block
+  // 16-wave forms
+  constexpr int P1 = GS >= 128 ? 1 : 128 / GS;
+  constexpr int PW = GS == 128 ? 1 : P2;
   switch (plain_form(a.M, a.N, a.K, GS)) {
     case kWideStaged: return launch_plain_t<GS, 1, 2, 4, P4, true>(a, s);
-    case kWide2: return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
+    case kWide2: return launch_plain_t<GS, 1, 2, 4, PW, false>(a, s);
     case kWide4: return launch_plain_t<GS, 1, 4, 4, P2, false>(a, s);
     case kDeepStaged: return launch_plain_t<GS, 1, 2, 16, P2, true>(a, s);
     case kSmall8: return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
+    case kOne16Staged: return launch_plain_t<GS, 1, 1, 16, P1, true>(a, s);
+    case kOne16: return launch_plain_t<GS, 1, 1, 16, P1, false>(a, s);
     case kOp2x2: return launch_plain_t<GS, 2, 2, 4, P2, false>(a, s);
     case kOp2x4: return launch_plain_t<GS, 2, 4, 4, P2, false>(a, s);
     case kOp4x2: return launch_plain_t<GS, 4, 2, 4, 1, false>(a, s);
@@ -455,9 +467,11 @@ int plain_form(int M, int N, int K, int group) {
   if (M <= 16) {
     if (wide) {
       if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
-      return M <= 4 ? kWide2 : kWide4;
+      return M <= 4 || (group == 128 && M <= 8) ? kWide2 : kWide4;
     }
     if (M <= 2 && K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit) return kDeepStaged;
+    if (M <= 8 && (N + 15) / 16 < 128) return kOne16;
+    if (M == 1 && xlds_rows + 16 * 1024 <= kPlainLdsLimit) return kOne16Staged;
     return M <= 8 ? kSmall8 : kWide2;
   }
   if (M <= 32) return wide ? kOp2x4 : kOp2x2;
