@@ -34,12 +34,16 @@ FORM_CASES = [
     ((3, 1000, 1024, 32), (1, 16, 16, 16)),
     ((1, 3000, 2048, 64), (1, 16, 16, 16)),
     ((2, 500, 2048, 256), (1, 16, 16, 16)),
-    ((7, 17000, 512, 128), (1, 16, 32, 4)),
+    ((3, 17000, 512, 128), (1, 16, 48, 4)),     # wide N: 4-wave workgroups, fragments through LDS
+    ((7, 17000, 512, 128), (1, 16, 80, 4)),
+    ((5, 5000, 768, 128), (1, 16, 32, 8)),      # short K
+    ((2, 17000, 512, 64), (1, 16, 32, 4)),      # wide N at group 64: rows in LDS, then operand order
+    ((7, 17000, 512, 64), (1, 16, 64, 4)),
     ((9, 2000, 4096, 128), (1, 16, 32, 8)),
-    ((13, 17000, 1024, 128), (1, 16, 80, 8)),
+    ((13, 17000, 1024, 128), (1, 16, 80, 4)),
     ((16, 9000, 8192, 128), (1, 16, 64, 8)),
     ((11, 300, 128, 128), (1, 32, 32, 16)),     # 32-row forms below 17 rows: a padding row block
-    ((15, 9000, 256, 128), (1, 32, 48, 16)),
+    ((15, 9000, 1152, 128), (1, 32, 48, 16)),
     ((17, 100, 4096, 128), (1, 16, 32, 8)),
     ((17, 5000, 8192, 128), (1, 16, 64, 8)),
     ((17, 9000, 8192, 128), (1, 16, 80, 8)),

@@ -156,9 +156,9 @@ def test_select_path():
 # decode layer set (qkv 5120x7168, o 6144x5120, gate_up 5120x34816, down
 # 17408x5120) at the row counts of its sweep, the time models' choices.
 FORMS = {
-    (1, 7168, 5120, 128): (1, 16, 16, 16), (1, 34816, 5120, 128): (1, 16, 32, 4),
-    (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 80, 8),
-    (8, 34816, 5120, 128): (1, 16, 32, 4), (12, 5120, 17408, 128): (1, 16, 32, 8),
+    (1, 7168, 5120, 128): (1, 16, 16, 16), (1, 34816, 5120, 128): (1, 16, 48, 4),
+    (1, 5120, 17408, 128): (1, 16, 32, 16), (16, 34816, 5120, 128): (1, 16, 80, 4),
+    (8, 34816, 5120, 128): (1, 16, 80, 4), (1, 5120, 768, 128): (1, 16, 32, 8), (12, 5120, 17408, 128): (1, 16, 32, 8),
     (2, 7168, 5120, 128): (1, 16, 32, 8), (4, 896, 5120, 128): (1, 16, 16, 16),
     (8, 34816, 5120, 64): (1, 16, 64, 4), (1, 896, 17408, 128): (1, 16, 32, 16),
     (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (2, 32, 256, 8),

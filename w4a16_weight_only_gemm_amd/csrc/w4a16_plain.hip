@@ -360,6 +360,11 @@ enum PlainForm : int {
   kXs2x4,        // 2 x 4, 16 waves (2 x 8)
   kXs2x5,        // 2 x 5, 8 waves (2 x 4)
   kXs4x4,        // 4 x 4, 16 waves (4 x 4)
+  // up to 16 rows at group 128 with wide N (2176 column blocks): 4-wave
+  // workgroups, 3 column blocks up to 4 rows and 5 above (gate_up 5120x34816:
+  // 20.5 -> 17.9 us at M = 1, 26.0 -> 19.3 at 8, 24.5 -> 21.6 at 16)
+  kXs1x3w4,      // 1 x 3, 4 waves
+  kXs1x5w4,      // 1 x 5, 4 waves
   // more rows at groups 32, 64 and 256, fragments loaded in operand order
   kOp2x2,        // 2 x 2, 4 waves
   kOp2x4,        // 2 x 4, 4 waves
@@ -374,6 +379,7 @@ struct PlainFormInfo {
 constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
     {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8}, {1, 1, 16}, {1, 1, 16},
     {1, 2, 8}, {1, 4, 8}, {1, 5, 8}, {2, 2, 16}, {2, 3, 16}, {2, 4, 16}, {2, 5, 8}, {4, 4, 16},
+    {1, 3, 4}, {1, 5, 4},
     {2, 2, 4}, {2, 4, 4}, {4, 2, 4}, {4, 4, 4}};
 
 constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
@@ -419,14 +425,11 @@ template <int GS>
 hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
   constexpr int P2 = GS >= 256 ? 1 : 2;
   constexpr int P4 = GS >= 256 ? 2 : 4;
-  // one group of 128 (or more) in flight: at group 128 the 4-wave two-block
-  // form at 3 to 8 rows (gate_up M = 4: 23.2 -> 22.1 us) and the one-block
-  // 16-wave forms
+  // the one-block 16-wave forms keep 128 k (one group of 128 or more) in flight
   constexpr int P1 = GS >= 128 ? 1 : 128 / GS;
-  constexpr int PW = GS == 128 ? 1 : P2;
   switch (plain_form(a.M, a.N, a.K, GS)) {
     case kWideStaged: return launch_plain_t<GS, 1, 2, 4, P4, true>(a, s);
-    case kWide2: return launch_plain_t<GS, 1, 2, 4, PW, false>(a, s);
+    case kWide2: return launch_plain_t<GS, 1, 2, 4, P2, false>(a, s);
     case kWide4: return launch_plain_t<GS, 1, 4, 4, P2, false>(a, s);
     case kDeepStaged: return launch_plain_t<GS, 1, 2, 16, P2, true>(a, s);
     case kSmall8: return launch_plain_t<GS, 1, 2, 8, P2, false>(a, s);
@@ -448,6 +451,8 @@ hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
       case kXs2x4: return launch_plain_t<GS, 2, 4, 16, 1, false, 2, true>(a, s);
       case kXs2x5: return launch_plain_t<GS, 2, 5, 8, 1, false, 2, true>(a, s);
       case kXs4x4: return launch_plain_t<GS, 4, 4, 16, 1, false, 4, true>(a, s);
+      case kXs1x3w4: return launch_plain_t<GS, 1, 3, 4, 1, false, 1, true>(a, s);
+      case kXs1x5w4: return launch_plain_t<GS, 1, 5, 4, 1, false, 1, true>(a, s);
       default: break;
     }
   }
@@ -463,11 +468,18 @@ int plain_form(int M, int N, int K, int group) {
   // From 9 rows at group 128 the XS forms win on the decode layer set and its
   // tensor-parallel shard (M = 16: 76.6 -> 61.8 us per layer set as four
   // calls); at 8 rows and fewer the forms below (measured at M = 4, 6 and 8).
+  // At group 128 and up to 16 rows, wide N takes the 4-wave XS forms, and a
+  // short K (at most 8 groups: the shard's o 768x5120, 4.2-4.4 -> 3.6-3.8 us)
+  // the 8-wave two-block XS form, at every row count.
+  if (group == 128 && M <= 16) {
+    if (wide) return M <= 4 ? kXs1x3w4 : kXs1x5w4;
+    if (K <= 1024 && (N + 15) / 16 >= 128) return kXs1x2;
+  }
   if (group == 128 && M >= 9) return best_xs_form(M, N, K, nullptr);
   if (M <= 16) {
     if (wide) {
       if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
-      return M <= 4 || (group == 128 && M <= 8) ? kWide2 : kWide4;
+      return M <= 4 ? kWide2 : kWide4;
     }
     if (M <= 2 && K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit) return kDeepStaged;
     if (M <= 8 && (N + 15) / 16 < 128) return kOne16;
