@@ -50,7 +50,8 @@ FORM_CASES = [
     ((17, 100, 256, 128), (1, 32, 32, 16)),
     ((17, 9000, 256, 128), (1, 32, 48, 16)),
     ((37, 7001, 256, 128), (1, 32, 64, 16)),
-    ((17, 17000, 1024, 128), (1, 32, 80, 8)),
+    ((17, 17000, 1024, 128), (1, 32, 80, 4)),
+    ((33, 9000, 2048, 128), (1, 32, 80, 8)),
     ((37, 9000, 256, 128), (1, 64, 64, 16)),
     ((17, 17000, 256, 128), (2, 32, 256, 8)),
     ((37, 35001, 256, 128), (2, 64, 256, 8)),

@@ -138,7 +138,8 @@ def test_select_path():
     assert w4.w4a16_select_path(1, 7168, 5120, 128) == S
     assert w4.w4a16_select_path(16, 5120, 17408, 128) == S
     assert w4.w4a16_select_path(16, 34816, 5120, 128) == S          # up to 16 rows: always
-    assert w4.w4a16_select_path(17, 34816, 5120, 128) == L          # 136 column tiles fill the CUs
+    assert w4.w4a16_select_path(17, 34816, 5120, 128) == S          # 4-wave 32-row XS form
+    assert w4.w4a16_select_path(33, 34816, 5120, 128) == L          # 136 column tiles fill the CUs
     assert w4.w4a16_select_path(64, 34816, 5120, 128) == L
     assert w4.w4a16_select_path(64, 5120, 17408, 128) == S          # 20 column tiles do not
     assert w4.w4a16_select_path(192, 5120, 6144, 128) == S
@@ -161,7 +162,7 @@ FORMS = {
     (8, 34816, 5120, 128): (1, 16, 80, 4), (1, 5120, 768, 128): (1, 16, 32, 8), (12, 5120, 17408, 128): (1, 16, 32, 8),
     (2, 7168, 5120, 128): (1, 16, 32, 8), (4, 896, 5120, 128): (1, 16, 16, 16),
     (8, 34816, 5120, 64): (1, 16, 64, 4), (1, 896, 17408, 128): (1, 16, 32, 16),
-    (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (2, 32, 256, 8),
+    (32, 7168, 5120, 128): (1, 32, 32, 16), (32, 34816, 5120, 128): (1, 32, 80, 4),
     (32, 5120, 17408, 128): (1, 16, 64, 8), (64, 7168, 5120, 128): (1, 32, 64, 16),
     (64, 5120, 6144, 128): (1, 32, 48, 16), (64, 34816, 5120, 128): (2, 64, 256, 8),
     (64, 5120, 17408, 128): (1, 16, 80, 8), (128, 7168, 5120, 128): (1, 64, 64, 16),

@@ -365,6 +365,9 @@ enum PlainForm : int {
   // 20.5 -> 17.9 us at M = 1, 26.0 -> 19.3 at 8, 24.5 -> 21.6 at 16)
   kXs1x3w4,      // 1 x 3, 4 waves
   kXs1x5w4,      // 1 x 5, 4 waves
+  // and at 17 to 32 rows, where the time model puts it ahead of the tile
+  // engine (gate_up: 31.8 -> 25.8 us at M = 17, 32.7 -> 28.9 at 32)
+  kXs2x5w4,      // 2 x 5, 4 waves (1 x 4)
   // more rows at groups 32, 64 and 256, fragments loaded in operand order
   kOp2x2,        // 2 x 2, 4 waves
   kOp2x4,        // 2 x 4, 4 waves
@@ -379,7 +382,7 @@ struct PlainFormInfo {
 constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
     {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8}, {1, 1, 16}, {1, 1, 16},
     {1, 2, 8}, {1, 4, 8}, {1, 5, 8}, {2, 2, 16}, {2, 3, 16}, {2, 4, 16}, {2, 5, 8}, {4, 4, 16},
-    {1, 3, 4}, {1, 5, 4},
+    {1, 3, 4}, {1, 5, 4}, {2, 5, 4},
     {2, 2, 4}, {2, 4, 4}, {4, 2, 4}, {4, 4, 4}};
 
 constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
@@ -388,26 +391,29 @@ constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
 // Modelled time of an XS form (microseconds): from 9 rows each
 // workgroup streams its MB x 16 activation rows (from L2) and NB weight
 // columns over all of K at about 45 GB/s per compute unit, after a fixed
-// start of 4 us (8 waves) or 1.5 us (16 waves: more loads in flight from the
-// first group); a compute unit that holds n workgroups takes n times as long.
-// Fitted to the decode layer set and its tensor-parallel shard (qkv 5120x896,
-// o 768x5120, gate_up 5120x4352, down 2176x5120) at M = 17 to 320, where the
-// form it puts first is within 1 % of the fastest of every form measured,
-// summed over the shapes (above 320 rows it runs 5-11 % under the measured
-// time of the shard's qkv, 12.4 and 19.7 against 13.0 and 22.1 us at 512 and
-// 1024 rows, still far from the tile engine's 30 us); at 9 to 16 rows (the rows past M repeat row M - 1
-// and are read from the caches) it puts first the fastest XS form of each
-// decode projection.
+// start of 4 us (8 waves), 1.5 us (16 waves: more loads in flight from the
+// first group) or 2 us (4 waves); a compute unit that holds n workgroups takes
+// n times as long. Fitted to the decode layer set and its tensor-parallel
+// shard (qkv 5120x896, o 768x5120, gate_up 5120x4352, down 2176x5120) at M =
+// 17 to 320, where the form it puts first is within 1 % of the fastest of
+// every form measured, summed over the shapes (above 320 rows it runs 5-11 %
+// under the measured time of the shard's qkv, 12.4 and 19.7 against 13.0 and
+// 22.1 us at 512 and 1024 rows, still far from the tile engine's 30 us); at 9
+// to 16 rows (the rows past M repeat row M - 1 and are read from the caches)
+// it puts first the fastest XS form of each decode projection.
 double xs_estimate_us(PlainForm f, int M, int N, int K) {
   const PlainFormInfo& i = kPlainFormInfo[f];
   const long long ncb = (static_cast<long long>(N) + 15) / 16;
   const long long wgs = (ncb + i.nb - 1) / i.nb * ((static_cast<long long>(M) + 16 * i.mb - 1) / (16 * i.mb));
   const long long rounds = (wgs + kModelCUs - 1) / kModelCUs;
   const double bytes = static_cast<double>(K) * (32.0 * i.mb + 8.0 * i.nb);
-  return static_cast<double>(rounds) * (bytes / 45000.0 + (i.waves == 16 ? 1.5 : 4.0));
+  const double t0 = i.waves == 16 ? 1.5 : i.waves == 4 ? 2.0 : 4.0;
+  return static_cast<double>(rounds) * (bytes / 45000.0 + t0);
 }
 
-PlainForm best_xs_form(int M, int N, int K, double* est_out) {
+// The XS form of least modelled time; with wide4 and wide N (1024 column
+// blocks or more) the 4-wave 32-row form is a candidate too.
+PlainForm best_xs_form(int M, int N, int K, bool wide4, double* est_out) {
   PlainForm best = kXsForms[0];
   double best_est = xs_estimate_us(best, M, N, K);
   for (PlainForm f : kXsForms) {
@@ -415,6 +421,13 @@ PlainForm best_xs_form(int M, int N, int K, double* est_out) {
     if (e < best_est) {
       best_est = e;
       best = f;
+    }
+  }
+  if (wide4 && (N + 15) / 16 >= 1024) {
+    const double e = xs_estimate_us(kXs2x5w4, M, N, K);
+    if (e < best_est) {
+      best_est = e;
+      best = kXs2x5w4;
     }
   }
   if (est_out) *est_out = best_est;
@@ -453,6 +466,7 @@ hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
       case kXs4x4: return launch_plain_t<GS, 4, 4, 16, 1, false, 4, true>(a, s);
       case kXs1x3w4: return launch_plain_t<GS, 1, 3, 4, 1, false, 1, true>(a, s);
       case kXs1x5w4: return launch_plain_t<GS, 1, 5, 4, 1, false, 1, true>(a, s);
+      case kXs2x5w4: return launch_plain_t<GS, 2, 5, 4, 1, false, 1, true>(a, s);
       default: break;
     }
   }
@@ -475,7 +489,7 @@ int plain_form(int M, int N, int K, int group) {
     if (wide) return M <= 4 ? kXs1x3w4 : kXs1x5w4;
     if (K <= 1024 && (N + 15) / 16 >= 128) return kXs1x2;
   }
-  if (group == 128 && M >= 9) return best_xs_form(M, N, K, nullptr);
+  if (group == 128 && M >= 9) return best_xs_form(M, N, K, true, nullptr);
   if (M <= 16) {
     if (wide) {
       if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
@@ -502,7 +516,7 @@ void plain_form_shape(int form, int* rows, int* cols, int* waves) {
 // rows on the decode layer set.
 double plain_estimate_us(int M, int N, int K, int group) {
   double est = 0.0;
-  best_xs_form(M, N, K, &est);
+  best_xs_form(M, N, K, group == 128, &est);
   return group == 128 ? est : 1.3 * est;
 }
 
