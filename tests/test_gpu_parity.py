@@ -224,9 +224,10 @@ def test_instantiation_matrix(path, case):
 # dequantization adds and removes 24 * (row sum) in fp32 around them, an error
 # that grows with |x|, not |y|. Columns 0..15 are zero over all of K (y = 0
 # exactly, where the bound is tightest), columns 16..31 zero in every other
-# group, the rest random.
+# group, the rest random. The two cases of 16,400 columns run w4a16_gemm's
+# 4-wave forms for wide N.
 WIDE = [(1, 64, 17408, 128), (3, 48, 5120, 128), (16, 64, 6144, 64), (20, 48, 2048, 32),
-        (70, 80, 17408, 128), (200, 64, 4096, 128)]
+        (70, 80, 17408, 128), (200, 64, 4096, 128), (4, 16400, 1024, 128), (20, 16400, 1024, 128)]
 
 
 def _wide_inputs(case, M, N, K, g):
