@@ -112,6 +112,9 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
  * All four pointers must be 16-byte aligned device addresses of the current
  * device. Supported shapes: M >= 0, N >= 1, K >= 1, group in {32, 64, 128, 256},
  * K % group == 0; N needs no rounding (ragged column tiles are masked).
+ * Above 1,048,560 rows (65,535 row tiles of 16) only the tile engine runs,
+ * which needs group 32, 64 or 128 and packed weights below 4 GB; other shapes
+ * of that many rows return W4A16_ERR_UNSUPPORTED before any launch.
  * M == 0 returns W4A16_OK and launches nothing.
  * Returns W4A16_OK, W4A16_ERR_INVALID_ARG, W4A16_ERR_UNSUPPORTED,
  * W4A16_ERR_MISALIGNED or W4A16_ERR_LAUNCH.
@@ -121,7 +124,9 @@ int w4a16_gemm(const void* x, const void* qweight, const void* scales, void* y, 
 
 /* As w4a16_gemm, with the kernel path forced (W4A16_PATH_*; the M-dispatch
  * choice is the library's own, the pages give none); every path gives a result
- * within the same tolerance of the exact product. */
+ * within the same tolerance of the exact product. W4A16_PATH_LARGE runs the
+ * plain kernel where the tile engine cannot (group 256, packed weights of 4 GB
+ * or more), and W4A16_PATH_SKINNY the tile engine above 1,048,560 rows. */
 int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* y, int M,
                   int N, int K, int group, int path, struct ihipStream_t* stream);
 
@@ -329,7 +334,7 @@ int w4a8_gemm_grouped(const w4a8_problem* problems, int count, int M, int group,
                       struct ihipStream_t* stream);
 
 /* The path W4A16_PATH_AUTO picks for this shape (an M-dispatch heuristic on
- * host integers), or -1 for an unsupported shape. */
+ * host integers), or -1 for a shape w4a16_gemm does not take. */
 int w4a16_select_path(int M, int N, int K, int group);
 
 /* The kernel form w4a16_gemm_ex runs for this shape on `path` (the library's

@@ -126,6 +126,10 @@ def test_gemm_argument_checks_without_launch():
     assert st(A, A, A, A, 1, 512, 250, 64) == w4.W4A16_ERR_UNSUPPORTED       # K % group
     assert st(A, A, A, A, 1, 0, 256, 64) == w4.W4A16_ERR_UNSUPPORTED
     assert st(A, A, A, A, 1, 512, 0, 64) == w4.W4A16_ERR_UNSUPPORTED
+    # past plain_kernel's 65535 row tiles only the tile engine runs: not at group 256
+    big = 65535 * 16 + 1
+    assert st(A, A, A, A, big, 512, 256, 256) == w4.W4A16_ERR_UNSUPPORTED
+    assert st(A, A, A, A, big, 512, 256, 256, path=w4.W4A16_PATH_SKINNY) == w4.W4A16_ERR_UNSUPPORTED
     assert st(A + 2, A, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
     assert st(A, A + 8, A, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
     assert st(A, A, A + 4, A, 1, 512, 256, 64) == w4.W4A16_ERR_MISALIGNED
@@ -148,6 +152,8 @@ def test_select_path():
     assert w4.w4a16_select_path(1024, 16, 256, 128) == S            # one column block
     assert w4.w4a16_select_path(512, 896, 5120, 128) == S           # narrow: 4 column tiles
     assert w4.w4a16_select_path(65535 * 16 + 1, 896, 5120, 128) == L  # past plain_kernel's grid
+    assert w4.w4a16_select_path(65535 * 16 + 1, 896, 5120, 256) == -1  # and no tile engine
+    assert w4.w4a16_select_path(65535 * 16, 896, 5120, 256) == S
     assert w4.w4a16_select_path(64, 34816, 5120, 256) == S          # no tile engine at group 256
     assert w4.w4a16_select_path(1, 512, 256, 48) == -1
     assert w4.w4a16_select_path(-1, 512, 256, 64) == -1
@@ -182,6 +188,11 @@ def test_select_form():
     assert w4.w4a16_select_form(1, 7168, 5120, 128, w4.W4A16_PATH_LARGE) == (2, 32, 256, 8)
     assert w4.w4a16_select_form(1024, 5120, 6144, 128, w4.W4A16_PATH_SKINNY)[0] == 1
     assert w4.w4a16_select_form(1024, 5120, 6144, 256, w4.W4A16_PATH_LARGE)[0] == 1
+    # past plain_kernel's grid: the tile engine on every path, or no kernel at group 256
+    big = 65535 * 16 + 1
+    assert w4.w4a16_select_form(big, 896, 5120, 128, w4.W4A16_PATH_SKINNY)[0] == 2
+    assert w4.w4a16_select_form(big, 896, 5120, 256) is None
+    assert w4.w4a16_select_form(big - 1, 896, 5120, 256)[0] == 1
     assert w4.w4a16_select_form(1, 512, 256, 48) is None
     assert w4.w4a16_select_form(1, 512, 256, 64, path=7) is None
     assert w4.w4a16_select_form(-1, 512, 256, 64) is None

@@ -124,6 +124,7 @@ int w4a16_pack(const int8_t* q, const uint16_t* scales_in, uint32_t* qweight_out
 
 int w4a16_select_path(int M, int N, int K, int group) {
   if (M < 0 || N < 1 || K < 1 || !group_supported(group) || K % group != 0) return -1;
+  if (M > w4a16_internal::kPlainMaxRows && !w4a16_internal::large_runs(N, K, group)) return -1;
   return w4a16_internal::choose_path(M, N, K, group);
 }
 
@@ -145,6 +146,11 @@ int w4a16_gemm_ex(const void* x, const void* qweight, const void* scales, void* 
   if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y))
     return W4A16_ERR_MISALIGNED;
   if (path == W4A16_PATH_AUTO) path = w4a16_internal::choose_path(M, N, K, group);
+  if (M > w4a16_internal::kPlainMaxRows) {
+    // plain_kernel's grid holds at most that many rows: the tile engine, or nothing
+    if (!w4a16_internal::large_runs(N, K, group)) return W4A16_ERR_UNSUPPORTED;
+    path = W4A16_PATH_LARGE;
+  }
   w4a16_internal::GemmArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.qweight = static_cast<const uint32_t*>(qweight);

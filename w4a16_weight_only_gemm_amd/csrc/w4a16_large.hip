@@ -714,6 +714,11 @@ hipError_t launch_large_sk_g(LargeSKArgs& sk, int group, hipStream_t stream) {
 
 bool large_supported(int group) { return group == 32 || group == 64 || group == 128; }
 
+bool large_runs(int N, int K, int group) {
+  const long long qbytes = static_cast<long long>((N + 15) / 16) * 16 * K / 2;
+  return large_supported(group) && qbytes <= 0xFFFFFFF0LL;
+}
+
 // Whole-K tile forms, per k-tile of 128 (microseconds, one MI355X, decode
 // layer set and its tensor-parallel shard at M = 17 to 512): one workgroup of
 // 32, 64 or 128 rows per compute unit takes 0.75, 1.08 or 1.9; a second round
@@ -744,8 +749,7 @@ double tile_estimate_us(int M, int N, int K, int group, int* rows_out) {
 
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream) {
   // packed weights and scales are addressed with 32-bit buffer offsets
-  const long long qbytes = static_cast<long long>((a.N + 15) / 16) * 16 * a.K / 2;
-  if (qbytes > 0xFFFFFFF0LL || !large_supported(a.group)) return launch_skinny(a, stream);
+  if (!large_runs(a.N, a.K, a.group)) return launch_skinny(a, stream);
   int rows = 128;
   tile_estimate_us(a.M, a.N, a.K, a.group, &rows);
   switch (a.group) {

@@ -21,6 +21,10 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_large(const GemmArgs& a, hipStream_t stream);
 // Group sizes the MFMA tile engine handles (others run the plain kernel).
 bool large_supported(int group);
+// Whether the tile engine runs the shape: a group it handles and packed
+// weights below 4 GB (32-bit buffer offsets); launch_large falls back to
+// plain_kernel otherwise.
+bool large_runs(int N, int K, int group);
 
 // ---- w4a16_gemm's choice of kernel form (host arithmetic only) ----
 // Compute units the time models below assume (one MI355X); the choice is a

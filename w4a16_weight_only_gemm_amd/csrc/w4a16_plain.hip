@@ -336,7 +336,7 @@ enum PlainForm : int {
   // 5120x7168, o 6144x5120, gate_up 5120x34816, down 17408x5120, group 128)
   // over every (column blocks, waves, groups in flight, staging) form that
   // fits: wide N (2176 column blocks) prefers 4-wave workgroups with 2 to 4
-  // column blocks; deep K at one or two rows 16 waves and staged rows; the
+  // column blocks (at group 128 the 4-wave XS forms below); deep K at one or two rows 16 waves and staged rows; the
   // rest 8 waves below 9 rows, 4 waves above (at groups 32, 64 and 256; group
   // 128 takes the XS forms from 9 rows). Group 256 (twice the registers per
   // group) keeps fewer groups in flight. Few column blocks (the tensor-parallel

@@ -918,27 +918,27 @@ hipError_t launch_streamk_planned(const PlanHeader& h, const unsigned char* plan
 // w4a16_gemm's M-dispatch: up to 16 rows the small-M forms of plain_kernel;
 // above, whichever of the two families the time models put first (the tile
 // engine needs enough 256-column tiles to fill the compute units: on the
-// decode layer set gate_up from 17 rows, qkv from 160, o and down from 224;
+// decode layer set gate_up from 33 rows, qkv from 160, o and down from 224;
 // a narrow projection such as the tensor-parallel shard's qkv 5120x896 stays
 // on plain_kernel at 1024 rows, 22 against 30 us). Beyond 65535 row tiles of
 // 16 (the grid's second dimension) only the tile engine runs.
 int choose_path(int M, int N, int K, int group) {
-  if (M <= 16 || !large_supported(group)) return W4A16_PATH_SKINNY;
   if (M > kPlainMaxRows) return W4A16_PATH_LARGE;
+  if (M <= 16 || !large_supported(group)) return W4A16_PATH_SKINNY;
   return tile_estimate_us(M, N, K, group, nullptr) < plain_estimate_us(M, N, K, group)
              ? W4A16_PATH_LARGE
              : W4A16_PATH_SKINNY;
 }
 
 int describe_form(int M, int N, int K, int group, int path, int* rows, int* cols, int* waves) {
-  if (path == W4A16_PATH_AUTO) path = choose_path(M, N, K, group);
-  const long long qbytes = static_cast<long long>((N + 15) / 16) * 16 * K / 2;
-  if (path == W4A16_PATH_LARGE && large_supported(group) && qbytes <= 0xFFFFFFF0LL) {
+  if (path == W4A16_PATH_AUTO || M > kPlainMaxRows) path = choose_path(M, N, K, group);
+  if (path == W4A16_PATH_LARGE && large_runs(N, K, group)) {
     tile_estimate_us(M, N, K, group, rows);
     *cols = 256;
     *waves = 8;
     return W4A16_PATH_LARGE;
   }
+  if (M > kPlainMaxRows) return -1;  // no kernel takes that many rows of this shape
   plain_form_shape(plain_form(M, N, K, group), rows, cols, waves);
   return W4A16_PATH_SKINNY;
 }
