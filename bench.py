@@ -661,12 +661,14 @@ def stack_steps(store: LayerStore, rows, sampler=None, passes: int = 10, xsets: 
 
 
 def cpu_baseline(seconds_target: float = 15.0, single_seconds: float = 5.0,
-                 other_rows=(16, 64), other_seconds: float = 5.0):
+                 other_rows=(16, 64, 1024), other_seconds: float = 5.0):
     """The oracle, as it stands, on the host cores, in the metric's unit:
     decode layer sets (M = 1), projection after projection, layer after layer,
     for about `seconds_target` seconds on all host threads, then about
     `single_seconds` on one thread; then the layer sets at each M of
-    `other_rows` for about `other_seconds` each on all threads."""
+    `other_rows` for about `other_seconds` each on all threads (at M = 1024
+    one projection GEMM alone takes a few seconds: the sample is the first
+    projections of layer set 0)."""
     import synth
     import oracle
 
