@@ -39,7 +39,9 @@ FORM_CASES = [
     ((5, 5000, 768, 128), (1, 16, 32, 8)),      # short K
     ((2, 17000, 512, 64), (1, 16, 32, 4)),      # wide N at group 64: rows in LDS, then operand order
     ((7, 17000, 512, 64), (1, 16, 64, 4)),
+    ((7, 3000, 2048, 128), (1, 16, 32, 8)),     # two groups in flight at 7-12 rows
     ((9, 2000, 4096, 128), (1, 16, 32, 8)),
+    ((11, 2000, 4096, 128), (1, 16, 32, 8)),
     ((13, 17000, 1024, 128), (1, 16, 80, 4)),
     ((16, 9000, 8192, 128), (1, 16, 64, 8)),
     ((11, 300, 128, 128), (1, 32, 32, 16)),     # 32-row forms below 17 rows: a padding row block

@@ -368,6 +368,9 @@ enum PlainForm : int {
   // and at 17 to 32 rows, where the time model puts it ahead of the tile
   // engine (gate_up: 31.8 -> 25.8 us at M = 17, 32.7 -> 28.9 at 32)
   kXs2x5w4,      // 2 x 5, 4 waves (1 x 4)
+  // at 7 to 12 rows with K above 1024, two groups in flight (down 17408x5120:
+  // 17.2 -> 16.5 us at M = 8, 19.1 -> 16.9 at 9; 16 rows: the same)
+  kXs1x2p2,      // 1 x 2, 8 waves, P = 2
   // more rows at groups 32, 64 and 256, fragments loaded in operand order
   kOp2x2,        // 2 x 2, 4 waves
   kOp2x4,        // 2 x 4, 4 waves
@@ -382,7 +385,7 @@ struct PlainFormInfo {
 constexpr PlainFormInfo kPlainFormInfo[kPlainForms] = {
     {1, 2, 4}, {1, 2, 4}, {1, 4, 4}, {1, 2, 16}, {1, 2, 8}, {1, 1, 16}, {1, 1, 16},
     {1, 2, 8}, {1, 4, 8}, {1, 5, 8}, {2, 2, 16}, {2, 3, 16}, {2, 4, 16}, {2, 5, 8}, {4, 4, 16},
-    {1, 3, 4}, {1, 5, 4}, {2, 5, 4},
+    {1, 3, 4}, {1, 5, 4}, {2, 5, 4}, {1, 2, 8},
     {2, 2, 4}, {2, 4, 4}, {4, 2, 4}, {4, 4, 4}};
 
 constexpr PlainForm kXsForms[] = {kXs1x2, kXs1x4, kXs1x5, kXs2x2,
@@ -467,6 +470,7 @@ hipError_t launch_plain_g(const GemmArgs& a, hipStream_t s) {
       case kXs1x3w4: return launch_plain_t<GS, 1, 3, 4, 1, false, 1, true>(a, s);
       case kXs1x5w4: return launch_plain_t<GS, 1, 5, 4, 1, false, 1, true>(a, s);
       case kXs2x5w4: return launch_plain_t<GS, 2, 5, 4, 1, false, 1, true>(a, s);
+      case kXs1x2p2: return launch_plain_t<GS, 1, 2, 8, 2, false, 1, true>(a, s);
       default: break;
     }
   }
@@ -489,7 +493,10 @@ int plain_form(int M, int N, int K, int group) {
     if (wide) return M <= 4 ? kXs1x3w4 : kXs1x5w4;
     if (K <= 1024 && (N + 15) / 16 >= 128) return kXs1x2;
   }
-  if (group == 128 && M >= 9) return best_xs_form(M, N, K, true, nullptr);
+  if (group == 128 && M >= 9) {
+    const PlainForm f = best_xs_form(M, N, K, true, nullptr);
+    return f == kXs1x2 && M <= 12 && K > 1024 ? kXs1x2p2 : f;
+  }
   if (M <= 16) {
     if (wide) {
       if (M <= 2 && xlds_rows + 4 * 2 * 1024 <= kPlainLdsLimit) return kWideStaged;
@@ -498,6 +505,7 @@ int plain_form(int M, int N, int K, int group) {
     if (M <= 2 && K >= 12288 && xlds_rows + 16 * 2 * 1024 <= kPlainLdsLimit) return kDeepStaged;
     if (M <= 8 && (N + 15) / 16 < 128) return kOne16;
     if (M == 1 && xlds_rows + 16 * 1024 <= kPlainLdsLimit) return kOne16Staged;
+    if (group == 128 && M >= 7 && K > 1024) return kXs1x2p2;
     return M <= 8 ? kSmall8 : kWide2;
   }
   if (M <= 32) return wide ? kOp2x4 : kOp2x2;
